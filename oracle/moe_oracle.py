@@ -1,0 +1,352 @@
+"""CPU oracle for the forward pass of one sparse Mixture-of-Experts layer.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import or call this module; the HIP
+library never does, and nothing here is a fallback for it.
+
+Plain NumPy/SciPy, float64 throughout (the pages fix no precision), written from
+the pages' definitions so that a reader can check each step by eye.  Sources are
+cited by page title and section:
+
+  [MoE&SMS]  "Mixture-of-Experts & Sparse Model Scaling" (chipfoundryservices
+             glossary): "Mathematical Formulation"; "Advanced Theory &
+             Extensions"; appendix labs 1-3.
+  [MoEM]     "Mixture-of-experts Models" (sempe.dev chapter): Level 2 "Router
+             scores become a sparse dispatch decision", "Top-k selection has
+             ties...", "Capacity limits make dispatch observable", "Overflow
+             handling defines an output contract"; Level 3 imbalance example.
+  [SMoE-arch] "Scaling Capacity via Sparse Mixture of Experts (MoE)
+             Architectures" (quizzr): the router and layer snippets.
+  [LLM-09]   "Large Language Models part 09: Sparse Mixture-of-Experts (MoE),
+             Router, Switch" (shakilmahmud.com): section 2 (noisy top-k gating),
+             section 3 (expert capacity), section 4 (auxiliary load balancing).
+  [3D-lab]   "3D mixture-of-experts routing lab" (toy.new): Router and Capacity
+             panels.
+
+Readings taken where the pages are silent or disagree (each also listed in the
+design notes):
+  R1  Gates are the softmax over the k selected logits ([LLM-09] s.2), which is
+      the same real number as the renormalised full-softmax probabilities of
+      [MoE&SMS] lab 1 and [MoEM] Level 2.
+  R2  Top-k order: logit descending, ties to the lower expert index, decided on
+      the float32 logits; slot 0 is the best expert.
+  R3  Capacity C = floor(factor * T * k / E) ([3D-lab] Capacity panel),
+      evaluated in IEEE double left to right; dropless means C = T.
+  R4  Drop priority is arrival order over the flat token-major assignment
+      index t*k + s ([MoE&SMS] lab 3 generalised to k slots).  A dropped
+      assignment contributes zero and the surviving gates are not renormalised.
+  R5  f_i counts routed (pre-capacity) assignments / (T*k); P_i is the token
+      mean of the FULL softmax of the logits ([MoE&SMS] lab 2); alpha = 1.
+  R6  Noise: H = x W_g^T (+ b_g) + eps * softplus(x W_noise^T), eps supplied.
+  R7  Shared experts take every token with weight 1, outside routing,
+      capacity and the statistics ([MoE&SMS] "Advanced Theory & Extensions").
+  R8  GELU is the exact erf form; SwiGLU is silu(x W1^T) * (x W3^T) then W2.
+
+Layouts (row-major, every weight in out x in form, as an nn.Linear stores it):
+  x [T,d]; w_g, w_noise [E,d]; b_g [E]; eps [T,E]; w1, w3 [E,h,d]; w2 [E,d,h];
+  b1 [E,h]; b2 [E,d]; ws1, ws3 [S,h,d]; ws2 [S,d,h].
+bfloat16 tensors arrive as uint16 bit patterns and are widened exactly.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf, expit
+
+__all__ = [
+    "to_f64", "softplus", "router_logits", "select_top_k", "selected_gates",
+    "full_softmax", "capacity", "dispatch_in_arrival_order", "dispatch",
+    "activation", "expert_ffn", "combine", "balance_stats", "moe_forward",
+    "overflow_record",
+]
+
+
+def to_f64(a) -> np.ndarray:
+    """Exact widening: bfloat16 bit patterns (uint16) or float32 -> float64."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def softplus(z: np.ndarray) -> np.ndarray:
+    """log(1 + e^z), in the overflow-free form max(z,0) + log1p(e^-|z|)."""
+    return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+
+
+def router_logits(x, w_g, b_g=None, w_noise=None, eps=None) -> np.ndarray:
+    """Router logits H [T,E], returned as float32.
+
+    [MoE&SMS] "Mathematical Formulation": one logit per expert from a linear map
+    of the token; [LLM-09] s.2: H_i = (x W_g)_i + eps * softplus((x W_noise)_i)
+    with eps ~ N(0,1) supplied by the caller (R6).  An optional per-expert bias
+    is added to the linear term ([SMoE-arch] router uses a biased linear layer).
+    Computed in float64 and rounded once to float32: these float32 logits are
+    what routing decides on (R2).
+    """
+    x64 = to_f64(x)
+    H = x64 @ to_f64(w_g).T
+    if b_g is not None:
+        H = H + to_f64(b_g)[None, :]
+    if w_noise is not None:
+        if eps is None:
+            raise ValueError("noisy gating needs eps")
+        H = H + to_f64(eps) * softplus(x64 @ to_f64(w_noise).T)
+    H32 = H.astype(np.float32)
+    if not np.all(np.isfinite(H32)):
+        raise FloatingPointError("non-finite router logits")
+    return H32
+
+
+def select_top_k(H32: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest logits per token, best first (R2).
+
+    [MoE&SMS] "Mathematical Formulation" (TopK over the scores) and lab 1
+    (descending order); [MoEM] Level 2 asks for a deterministic tie rule.
+    A stable sort of the negated float32 logits orders by value descending
+    and, among equal values (including -0.0 == +0.0), by lower index first.
+    """
+    H32 = np.asarray(H32, dtype=np.float32)
+    E = H32.shape[1]
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    return np.argsort(-H32, axis=1, kind="stable")[:, :k].astype(np.int32)
+
+
+def selected_gates(H32: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Gates [T,k]: softmax over the selected logits only (R1, [LLM-09] s.2).
+
+    Shifted by the best selected logit (slot 0), as a softmax is computed
+    stably; the k gates of a token sum to 1.
+    """
+    sel = np.take_along_axis(np.asarray(H32, np.float64), idx.astype(np.int64), axis=1)
+    w = np.exp(sel - sel[:, :1])
+    return w / w.sum(axis=1, keepdims=True)
+
+
+def full_softmax(H32: np.ndarray) -> np.ndarray:
+    """p_i = exp(g_i) / sum_j exp(g_j) over all E experts ([MoE&SMS]
+    "Mathematical Formulation"), max-shifted as in its lab 1."""
+    H = np.asarray(H32, np.float64)
+    w = np.exp(H - H.max(axis=1, keepdims=True))
+    return w / w.sum(axis=1, keepdims=True)
+
+
+def capacity(capacity_factor: float, T: int, k: int, E: int) -> int:
+    """Per-expert quota C = floor(factor * tokens * k / experts) ([3D-lab]
+    Capacity panel; at k = 1 it is [LLM-09] s.3's factor * T / E).  A factor
+    <= 0 means dropless: C = T, the most assignments one expert can receive
+    because a token's k experts are distinct (R3)."""
+    if capacity_factor <= 0:
+        return int(T)
+    return int(math.floor(capacity_factor * T * k / E))
+
+
+def dispatch_in_arrival_order(idx: np.ndarray, E: int, C: int) -> dict:
+    """Capacity check as a sequential walk over arrivals (R4).
+
+    [MoE&SMS] lab 3: each arriving assignment is accepted while its expert's
+    load is below capacity, otherwise dropped; generalised to k slots by
+    walking the flat index t*k + s in increasing order.  Returns per-expert
+    demand ``counts``, accepted ``kept``, and per assignment the position
+    ``slot_rank`` it took in its expert's buffer, or -1 if dropped.
+    """
+    T, k = idx.shape
+    load = [0] * E
+    counts = [0] * E
+    slot_rank = np.full((T, k), -1, dtype=np.int64)
+    for t in range(T):
+        for s in range(k):
+            e = int(idx[t, s])
+            counts[e] += 1
+            if load[e] < C:
+                slot_rank[t, s] = load[e]
+                load[e] += 1
+    return {"counts": np.array(counts, np.int64), "kept": np.array(load, np.int64),
+            "slot_rank": slot_rank}
+
+
+def dispatch(idx: np.ndarray, E: int, C: int) -> dict:
+    """Dispatch tables for the expert-contiguous layout, vectorised.
+
+    The rank of assignment (t,s) within its expert is the number of earlier
+    flat assignments (t'*k+s' < t*k+s) to the same expert, which a stable sort
+    of the flat expert ids yields; it is kept iff rank < C (same decisions as
+    ``dispatch_in_arrival_order``).  [SMoE-arch] groups tokens by their expert;
+    the buffers here hold, per expert, its kept assignments in arrival order:
+      counts[e]   routed assignments (demand) of expert e
+      kept[e]     min(counts[e], C)
+      offsets     [E+1] exclusive prefix sum of kept
+      dest[t,s]   row of the assignment in the expert-contiguous buffer, or -1
+      row_token   [sum(kept)] the token held in each buffer row
+    [MoEM] Level 2 capacity example: overflow = counts - kept.
+    """
+    T, k = idx.shape
+    flat = idx.reshape(-1).astype(np.int64)
+    counts = np.bincount(flat, minlength=E).astype(np.int64)
+    order = np.argsort(flat, kind="stable")
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    rank = np.empty_like(flat)
+    rank[order] = np.arange(flat.size) - np.repeat(starts, counts)
+    kept = np.minimum(counts, C)
+    offsets = np.concatenate([[0], np.cumsum(kept)]).astype(np.int64)
+    keep = rank < C
+    dest = np.where(keep, offsets[flat] + rank, -1)
+    row_token = np.empty(int(offsets[-1]), dtype=np.int64)
+    tok = np.arange(flat.size) // k
+    row_token[dest[keep]] = tok[keep]
+    return {"counts": counts, "kept": kept, "offsets": offsets,
+            "dest": dest.reshape(T, k), "row_token": row_token,
+            "rank": rank.reshape(T, k), "capacity": int(C)}
+
+
+def activation(act: str, a: np.ndarray, b: np.ndarray | None = None) -> np.ndarray:
+    """Expert non-linearities (R8): exact GELU 0.5 a (1 + erf(a / sqrt 2));
+    ReLU max(a, 0); SwiGLU silu(a) * b with silu(a) = a * sigmoid(a)."""
+    if act == "gelu":
+        return 0.5 * a * (1.0 + erf(a / math.sqrt(2.0)))
+    if act == "relu":
+        return np.maximum(a, 0.0)
+    if act == "swiglu":
+        if b is None:
+            raise ValueError("swiglu needs the up projection")
+        return a * expit(a) * b
+    raise ValueError(act)
+
+
+def expert_ffn(x_rows, w1, w2, act, w3=None, b1=None, b2=None) -> np.ndarray:
+    """One expert FFN on a set of token rows, float64.
+
+    [MoE&SMS] "Core Concepts": an expert has the architecture of the dense FFN
+    it replaces with its own weights; lab 4 counts one hidden layer with
+    biases.  y = act(x W1^T (+ b1) [, x W3^T]) W2^T (+ b2); the hidden layer is
+    kept unrounded.
+    """
+    x = to_f64(x_rows)
+    a = x @ to_f64(w1).T
+    if b1 is not None:
+        a = a + to_f64(b1)[None, :]
+    u = x @ to_f64(w3).T if w3 is not None else None
+    hid = activation(act, a, u)
+    y = hid @ to_f64(w2).T
+    if b2 is not None:
+        y = y + to_f64(b2)[None, :]
+    return y
+
+
+def combine(T, d, idx, gates, dest, expert_rows_out, tokens, shared_out=None) -> np.ndarray:
+    """y_t = shared_t + sum over the token's slots s of [kept] g_ts * E_e(x_t).
+
+    [MoE&SMS] "Mathematical Formulation": the weighted sum runs over the
+    selected experts only; [LLM-09] s.1 writes it as sum_i G(x)_i E_i(x).
+    A dropped slot adds nothing and the other gates are not rescaled (R4,
+    [MoEM] "Overflow handling defines an output contract").  Shared experts
+    add with weight 1 (R7).  ``expert_rows_out`` maps a buffer row to that
+    assignment's expert output.
+    """
+    y = np.zeros((len(tokens), d), np.float64)
+    if shared_out is not None:
+        y += shared_out
+    k = idx.shape[1]
+    for j, t in enumerate(tokens):
+        for s in range(k):
+            r = int(dest[t, s])
+            if r >= 0:
+                y[j] += gates[t, s] * expert_rows_out[r]
+    return y
+
+
+def balance_stats(counts, kept, P, T: int, k: int, E: int) -> dict:
+    """Switch load-balance statistics (R5).
+
+    [MoE&SMS] "Mathematical Formulation": L_aux = N * sum_i f_i P_i, f_i the
+    hard fraction of assignments routed to expert i, P_i the mean router
+    probability; [LLM-09] s.4 gives the same with alpha (taken as 1).
+    Diagnostics from [MoEM]: overflow per expert, drop rate (lab 3 of
+    [MoE&SMS]: 1 - fraction processed), load coefficient of variation and the
+    absolute deviation from equal load (Level 3 example).
+    """
+    counts = np.asarray(counts, np.float64)
+    kept = np.asarray(kept, np.float64)
+    f = counts / (T * k)
+    l_aux = E * float(np.sum(f * P))
+    mean = counts.mean()
+    return {
+        "f": f, "P": P, "l_aux": l_aux,
+        "drop_rate": 1.0 - kept.sum() / (T * k),
+        "overflow": counts - kept,
+        "load_cv": float(counts.std() / mean) if mean > 0 else 0.0,
+        "deviation": float(np.abs(counts - T * k / E).sum()),
+    }
+
+
+def moe_forward(x, w_g, w1, w2, *, k: int, act: str, capacity_factor: float,
+                w3=None, b_g=None, w_noise=None, eps=None, b1=None, b2=None,
+                ws1=None, ws3=None, ws2=None, logits=None, tokens=None) -> dict:
+    """The whole layer forward, step by step.
+
+    1. router logits H (or the supplied float32 ``logits``);
+    2. top-k experts and their gates, full softmax for P;
+    3. counts, capacity and drops in arrival order, expert-contiguous tables;
+    4. every expert on its kept rows (restricted to ``tokens`` if given);
+    5. gate-weighted combine back to token order, plus shared experts, and
+       the load-balance statistics.
+    ``tokens`` (default all) selects which output rows to compute; steps 1-3
+    and the statistics always cover the whole batch, since capacity couples
+    tokens through their arrival order ([MoEM] "Routing is conditional on a
+    token and its batch context").
+    """
+    T, d = np.asarray(x).shape
+    E = np.asarray(w_g).shape[0]
+    if logits is None:
+        H = router_logits(x, w_g, b_g, w_noise, eps)
+    else:
+        H = np.asarray(logits, np.float32)
+    idx = select_top_k(H, k)
+    g = selected_gates(H, idx)
+    P = full_softmax(H).mean(axis=0)
+    C = capacity(capacity_factor, T, k, E)
+    disp = dispatch(idx, E, C)
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    want = np.zeros(T, bool)
+    want[tokens] = True
+
+    rows_out = {}
+    offsets, row_token = disp["offsets"], disp["row_token"]
+    for e in range(E):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        rows = rows[want[row_token[rows]]]
+        if rows.size == 0:
+            continue
+        ye = expert_ffn(np.asarray(x)[row_token[rows]], w1[e], w2[e], act,
+                        None if w3 is None else w3[e],
+                        None if b1 is None else b1[e], None if b2 is None else b2[e])
+        for r, v in zip(rows, ye):
+            rows_out[int(r)] = v
+
+    shared = None
+    if ws1 is not None:
+        shared = np.zeros((len(tokens), d), np.float64)
+        for s in range(ws1.shape[0]):
+            shared += expert_ffn(np.asarray(x)[tokens], ws1[s], ws2[s], act,
+                                 None if ws3 is None else ws3[s])
+    y = combine(T, d, idx, g, disp["dest"], rows_out, tokens, shared)
+    stats = balance_stats(disp["counts"], disp["kept"], P, T, k, E)
+    return {"logits": H, "idx": idx, "gates": g, "prob_mean": P, "capacity": C,
+            **disp, **stats, "y": y, "tokens": tokens, "shared": shared}
+
+
+def overflow_record(idx: np.ndarray, dest: np.ndarray) -> list:
+    """Per affected token: selected experts, successful assignments, fallback
+    type and final path ([MoEM] "Overflow handling defines an output
+    contract").  The fallback here is always "drop"."""
+    rec = []
+    for t in range(idx.shape[0]):
+        lost = [int(e) for e, r in zip(idx[t], dest[t]) if r < 0]
+        if lost:
+            rec.append({"token": t, "selected": [int(e) for e in idx[t]],
+                        "processed": [int(e) for e, r in zip(idx[t], dest[t]) if r >= 0],
+                        "fallback": "drop", "dropped": lost})
+    return rec
+

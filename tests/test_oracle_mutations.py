@@ -1,0 +1,179 @@
+"""Plants plausible mistakes in the CPU oracle and checks the pins catch each.
+
+Every mutation replaces one oracle function (in the oracle module and in the
+package namespace the pin tests use) with a subtly wrong variant: a dropped
+term, a wrong sign or index, a transposed reading, a different rounding.  The
+pin suite must fail for every one of them.  Runs on the CPU only.
+"""
+import math
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle
+import oracle.moe_oracle as M
+import tests.test_oracle_pins as pins
+
+ORIG = {n: getattr(M, n) for n in M.__all__}
+
+
+def _router_no_bias(x, w_g, b_g=None, w_noise=None, eps=None):
+    return ORIG["router_logits"](x, w_g, None, w_noise, eps)
+
+
+def _router_linear_noise(x, w_g, b_g=None, w_noise=None, eps=None):
+    H = M.to_f64(x) @ M.to_f64(w_g).T
+    if b_g is not None:
+        H = H + M.to_f64(b_g)
+    if w_noise is not None:
+        H = H + M.to_f64(eps) * (M.to_f64(x) @ M.to_f64(w_noise).T)
+    return H.astype(np.float32)
+
+
+def _router_noise_sign(x, w_g, b_g=None, w_noise=None, eps=None):
+    return ORIG["router_logits"](x, w_g, b_g, w_noise, None if eps is None else -eps)
+
+
+def _topk_ties_high(H32, k):
+    H32 = np.asarray(H32, np.float32)
+    E = H32.shape[1]
+    return (E - 1 - np.argsort(-H32[:, ::-1], axis=1, kind="stable")[:, :k]).astype(np.int32)
+
+
+def _topk_ascending(H32, k):
+    return np.argsort(np.asarray(H32, np.float32), axis=1, kind="stable")[:, :k].astype(np.int32)
+
+
+def _gates_unnormalised(H32, idx):
+    return np.take_along_axis(M.full_softmax(H32), idx.astype(np.int64), axis=1)
+
+
+def _capacity_round(cf, T, k, E):
+    return int(T) if cf <= 0 else int(round(cf * T * k / E))
+
+
+def _capacity_no_k(cf, T, k, E):
+    return int(T) if cf <= 0 else int(math.floor(cf * T / E))
+
+
+def _dispatch_slot_major(idx, E, C):
+    T, k = idx.shape
+    d = ORIG["dispatch"](idx.T.copy(), E, C)  # arrival order s*T + t
+    d["dest"] = d["dest"].T.copy()
+    d["rank"] = d["rank"].T.copy()
+    return d
+
+
+def _dispatch_off_by_one(idx, E, C):
+    return ORIG["dispatch"](idx, E, C + 1)
+
+
+def _combine_renormalised(T, d, idx, gates, dest, rows_out, tokens, shared_out=None):
+    kept = dest >= 0
+    g = gates * kept
+    s = g.sum(1, keepdims=True)
+    g = np.divide(g, s, out=np.zeros_like(g), where=s > 0)
+    return ORIG["combine"](T, d, idx, g, dest, rows_out, tokens, shared_out)
+
+
+def _ffn_no_b2(x_rows, w1, w2, act, w3=None, b1=None, b2=None):
+    return ORIG["expert_ffn"](x_rows, w1, w2, act, w3, b1, None)
+
+
+def _act_swapped_or_tanh(act, a, b=None):
+    if act == "swiglu":
+        return b * expit(b) * a
+    if act == "gelu":
+        return 0.5 * a * (1 + np.tanh(math.sqrt(2 / math.pi) * (a + 0.044715 * a ** 3)))
+    return ORIG["activation"](act, a, b)
+
+
+def _stats_f_swapped(counts, kept, P, T, k, E):
+    return ORIG["balance_stats"](np.asarray(counts)[::-1], kept, P, T, k, E)
+
+
+def _stats_f_over_T(counts, kept, P, T, k, E):
+    return ORIG["balance_stats"](np.asarray(counts) * k, kept, P, T, k, E)
+
+
+def _forward_sparse_P(*a, **kw):
+    out = ORIG["moe_forward"](*a, **kw)
+    T = out["idx"].shape[0]
+    sparse = np.zeros((T, out["prob_mean"].size))
+    np.put_along_axis(sparse, out["idx"].astype(np.int64), out["gates"], 1)
+    out["prob_mean"] = sparse.mean(0)
+    return out
+
+
+MUTATIONS = {
+    "router drops the bias": ("router_logits", _router_no_bias),
+    "noise without softplus": ("router_logits", _router_linear_noise),
+    "noise sign flipped": ("router_logits", _router_noise_sign),
+    "ties go to the higher index": ("select_top_k", _topk_ties_high),
+    "top-k picks the smallest": ("select_top_k", _topk_ascending),
+    "gates not renormalised": ("selected_gates", _gates_unnormalised),
+    "capacity rounded, not floored": ("capacity", _capacity_round),
+    "capacity without k": ("capacity", _capacity_no_k),
+    "slot-major drop priority": ("dispatch", _dispatch_slot_major),
+    "capacity off by one": ("dispatch", _dispatch_off_by_one),
+    "surviving gates rescaled": ("combine", _combine_renormalised),
+    "second bias dropped": ("expert_ffn", _ffn_no_b2),
+    "swiglu halves swapped / tanh gelu": ("activation", _act_swapped_or_tanh),
+    "f indices reversed": ("balance_stats", _stats_f_swapped),
+    "f divided by T, not T*k": ("balance_stats", _stats_f_over_T),
+    "P from the sparse gates": ("moe_forward", _forward_sparse_P),
+}
+
+PIN_TESTS = [
+    pins.test_top2_worked_example,
+    pins.test_capacity_worked_example,
+    pins.test_load_deviation_example,
+    pins.test_topk_brute_force_with_ties_and_signed_zero,
+    pins.test_gate_closed_forms,
+    pins.test_router_identity_rows_give_weight_columns,
+    pins.test_router_noise_reduces_and_matches_softplus,
+    pins.test_capacity_formula_values,
+    lambda: pins.test_dispatch_brute_force(3, 3, 2),
+    lambda: [pins.test_dense_equivalence_E1_k1(a) for a in ("gelu", "relu", "swiglu")],
+    pins.test_identical_experts_and_drops,
+    pins.test_laux_closed_forms,
+    pins.test_activations_match_library_forms,
+]
+
+
+def _sequential_reference_ok():
+    """The sequential arrival walk is the definition; a mutated vectorised
+    dispatch must disagree with it somewhere on the tiny-batch grid."""
+    for idx in pins._all_idx_patterns(3, 3, 2):
+        for cf in (0.5, 1.0, 1.5):
+            C = ORIG["capacity"](cf, 3, 2, 3)
+            seq = ORIG["dispatch_in_arrival_order"](idx, 3, C)
+            vec = M.dispatch(idx, 3, C)
+            if not np.array_equal(seq["kept"], vec["kept"]):
+                return False
+            if not np.array_equal(seq["slot_rank"] >= 0, vec["dest"] >= 0):
+                return False
+    return True
+
+
+@pytest.mark.parametrize("name", list(MUTATIONS))
+def test_pins_catch_mutation(name, monkeypatch):
+    fn_name, bad = MUTATIONS[name]
+    monkeypatch.setattr(M, fn_name, bad)
+    monkeypatch.setattr(oracle, fn_name, bad)
+    caught = []
+    for t in PIN_TESTS:
+        try:
+            t()
+        except Exception:  # an assertion or an error: the pin fired
+            caught.append(t)
+    if fn_name == "dispatch" and not _sequential_reference_ok():
+        caught.append("sequential walk")
+    assert caught, f"no pin caught the planted mistake: {name}"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    for t in PIN_TESTS:
+        t()
+    assert _sequential_reference_ok()
