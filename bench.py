@@ -1,0 +1,242 @@
+"""Throughput of one sparse-MoE layer forward on one MI355X.
+
+A step is one pass of the whole layer (router + top-k, dispatch, the two
+grouped expert GEMMs, shared experts, combine + statistics) over one batch of
+seeded synthetic input already resident in HBM, through the C ABI's stage
+entry points on torch's current stream.  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Workloads: mixtral_prefill (default; the MFMA-bound Mixtral-shaped prefill,
+T=8192, d=4096, 8 experts top-2, SwiGLU h=14336), mixtral_decode, switch_top1,
+finegrained_shared, toy_fp32.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+DOMINANT = {"ffn_tiled": "ffn_tiled_kernel", "ffn_skinny": "ffn_skinny_kernel",
+            "ffn_f32": "ffn_f32_kernel"}
+
+
+def algorithmic_work(cfg, counts, C):
+    """Algorithmic FLOPs and bytes of the layer and of its first expert GEMM.
+
+    Only work the method must do counts: kept assignments (dropped ones and
+    padding excluded), weights of experts that received rows, each operand and
+    result once.  m = weight matrices per expert (3 SwiGLU, 2 otherwise)."""
+    b = 2 if cfg.dtype == "bf16" else 4
+    T, d, E, k, h, S = cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, cfg.n_shared
+    kept = np.minimum(np.asarray(counts, np.int64), C)
+    rows = int(kept.sum())
+    active = int((kept > 0).sum())
+    m_up = 2 if cfg.act == "swiglu" else 1
+    m = m_up + 1
+    up_flops = 2.0 * d * h * m_up * (rows + S * T)
+    down_flops = 2.0 * d * h * (rows + S * T)
+    router_flops = 2.0 * T * d * E * (2 if cfg.router_noise else 1)
+    up_bytes = (m_up * h * d * b) * (active + S) + T * d * b + (rows + S * T) * h * b
+    layer_bytes = (m * h * d * b) * (active + S) + E * d * b * (2 if cfg.router_noise else 1) \
+        + 2 * T * d * b + (T * E * 4 if cfg.router_noise else 0)
+    return {"layer_flops": up_flops + down_flops + router_flops, "layer_bytes": float(layer_bytes),
+            "up_flops": up_flops, "up_bytes": float(up_bytes), "kept_rows": rows,
+            "active_experts": active}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_mixture_experts_26_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload, kernel):
+    """HBM traffic per launch from committed rocprofv3 counter summaries, or
+    None when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, budget_s):
+    """The CPU oracle, untuned, on a bounded sample of the same workload: all
+    routing for the whole batch plus the outputs of the first n tokens."""
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    n = {"mixtral_prefill": 128, "mixtral_decode": 32, "switch_top1": 4096,
+         "finegrained_shared": 256, "toy_fp32": 64}.get(cfg.name, 64)
+    n = min(n, cfg.T)
+    tokens = np.arange(n)
+    t0 = time.perf_counter()
+    O.moe_forward(inp.x, inp.w_g, inp.w1, inp.w2, k=cfg.k, act=cfg.act,
+                  capacity_factor=cfg.capacity_factor, w3=inp.w3, b_g=inp.b_g,
+                  w_noise=inp.w_noise, eps=inp.eps, b1=inp.b1, b2=inp.b2, ws1=inp.ws1,
+                  ws3=inp.ws3, ws2=inp.ws2, tokens=tokens)
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} of {cfg.T} tokens' outputs (routing, capacity and statistics over "
+                      f"all {cfg.T}); float64 NumPy; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    from sparse_mixture_experts_26_amd.layer import MoeLayer
+    from workloads import FULL, make_inputs, to_torch
+
+    cfg = FULL[args.workload]
+    t0 = time.time()
+    inp = make_inputs(cfg, args.seed)
+    dev = {k: to_torch(v, "cuda") for k, v in inp.tensors().items()}
+    torch.cuda.synchronize()
+    print(f"[bench] {cfg.name}: inputs ready in {time.time() - t0:.1f} s", file=sys.stderr,
+          flush=True)
+    layer = MoeLayer(cfg, dev)
+    x, eps = dev["x"], dev.get("eps")
+
+    if args.calib_copy_mb:
+        src = torch.empty(args.calib_copy_mb << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        layer.staged(x, eps)
+    torch.cuda.synchronize()
+
+    stages = ["route", "dispatch", "up", "down"] + (["shared"] if cfg.n_shared else []) + ["combine"]
+    ev = {s: [] for s in stages}
+    marks = []
+
+    def mark(name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        marks.append((name, e))
+
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        mark("begin")
+        layer.staged(x, eps, between=mark)
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    prev = None
+    for name, e in marks:
+        if prev is not None and name != "begin":
+            ev[name].append(prev.elapsed_time(e))
+        prev = e
+    stage_ms = {s: float(np.mean(v)) for s, v in ev.items() if v}
+    step_ms = []
+    begins = [e for n, e in marks if n == "begin"] + [stop]
+    for a, b in zip(begins[:-1], begins[1:]):
+        step_ms.append(a.elapsed_time(b))
+
+    # the single-call path, timed separately for reference
+    for _ in range(2):
+        layer.forward(x, eps)
+    torch.cuda.synchronize()
+    s2 = torch.cuda.Event(enable_timing=True)
+    e2 = torch.cuda.Event(enable_timing=True)
+    s2.record()
+    for _ in range(args.steps):
+        layer.forward(x, eps)
+    e2.record()
+    torch.cuda.synchronize()
+    fwd_ms = s2.elapsed_time(e2) / args.steps
+
+    out = layer.out
+    counts = out["counts"].cpu().numpy()
+    stats = out["stats"].cpu().numpy()
+    work = algorithmic_work(cfg, counts, layer.capacity)
+    kernel = "ffn_f32" if cfg.dtype == "f32" else (
+        "ffn_skinny" if layer.group_bound <= 32 and (cfg.n_shared == 0 or cfg.T <= 32) else "ffn_tiled")
+    up_ms = stage_ms["up"]
+    mfma_bound = kernel == "ffn_tiled"
+    if mfma_bound:
+        achieved = work["up_flops"] / (up_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = work["up_bytes"] / (up_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = read_traffic(cfg.name, kernel)
+    roof["kernel"] = DOMINANT[kernel]
+    roof["kernel_ms"] = round(up_ms, 4)
+
+    E = cfg.E
+    tokens_per_s = cfg.T / (ms_per_step * 1e-3)
+    rec = {
+        "metric": "MoE-layer tokens/sec at 1 GPU",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
+                   "h": cfg.h, "act": cfg.act, "n_shared": cfg.n_shared,
+                   "capacity": int(layer.capacity), "dropless": cfg.dropless,
+                   "parallelism": "single GPU"},
+        "layer_tflops": round(work["layer_flops"] / (ms_per_step * 1e-3) / 1e12, 2),
+        "layer_gbs": round(work["layer_bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
+        "p50_ms": round(float(np.percentile(step_ms, 50)), 4),
+        "p95_ms": round(float(np.percentile(step_ms, 95)), 4),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "layer_forward_ms": round(fwd_ms, 4),
+        "routing": {"kept_rows": work["kept_rows"], "active_experts": work["active_experts"],
+                    "drop_rate": round(float(stats[2 * E + 1]), 5),
+                    "l_aux": round(float(stats[2 * E]), 5),
+                    "load_cv": round(float(counts.std() / counts.mean()), 4)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, inp, 30.0)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,245 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts layer forward.
+ *
+ * One sparse MoE layer in five steps, each a HIP kernel on the caller's stream:
+ *   router logits -> top-k + gates -> counts/capacity/dispatch -> grouped expert
+ *   FFN -> gate-weighted combine (+ load-balance statistics).
+ *
+ * Sources (page title and section):
+ *   [MoE&SMS]  "Mixture-of-Experts & Sparse Model Scaling": Mathematical
+ *              Formulation (softmax, top-k weighted sum, L_aux); Advanced Theory &
+ *              Extensions (capacity and dropping, shared experts); labs 1-3.
+ *   [MoEM]     "Mixture-of-experts Models", Level 2 (top-k dispatch, tie rule,
+ *              capacity, overflow contract) and Level 3 (balance diagnostics).
+ *   [SMoE-arch] "Scaling Capacity via Sparse Mixture of Experts (MoE)
+ *              Architectures": router module and grouping tokens by expert.
+ *   [LLM-09]   "Large Language Models part 09: Sparse Mixture-of-Experts":
+ *              s.2 noisy top-k gating, s.3 capacity, s.4 auxiliary loss.
+ *   [3D-lab]   "3D mixture-of-experts routing lab": Router and Capacity panels.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns every
+ *     buffer, including the workspace; the library never allocates, never frees,
+ *     never synchronises the stream and never throws.
+ *   - All work is enqueued on `stream` (a hipStream_t; 0 = the null stream), in
+ *     order.  A return of MOE_OK means the launches were enqueued; faults inside
+ *     a kernel surface at the caller's next synchronisation.
+ *   - Validation (null pointers, shapes, workspace size, alignment) happens on
+ *     the host before any HIP call; on any error nothing is enqueued.
+ *   - Layouts are row-major; weights are stored out x in (nn.Linear form), so
+ *     every product is A * B^T with both operands contiguous along the
+ *     reduction axis:
+ *       x [T,d]; w_g, w_noise [E,d]; b_g [E]; eps [T,E];
+ *       w1, w3 [E,h,d]; w2 [E,d,h]; b1 [E,h]; b2 [E,d];
+ *       shared experts ws1, ws3 [S,h,d]; ws2 [S,d,h].
+ *   - Activations and weights have the config dtype (float32 or bfloat16 bit
+ *     patterns); biases, eps, logits, gates, expert outputs and statistics are
+ *     float32; every index and count is int32.
+ *   - All device pointers must be 16-byte aligned; d and h must be multiples
+ *     of 8; E <= 256; k <= 8 (MOE_ERR_UNSUPPORTED otherwise).
+ *   - Entry points are stateless and may be called from several host threads;
+ *     calls that share a workspace or outputs must be ordered by the caller.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad shape, k > E, ...        */
+  MOE_ERR_UNSUPPORTED = 2,        /* valid, but outside what the kernels cover  */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4                 /* a HIP launch or runtime call failed        */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/* Expert non-linearity: exact-erf GELU, ReLU, or SwiGLU silu(x w1^T) * (x w3^T). */
+typedef enum { MOE_ACT_GELU = 0, MOE_ACT_RELU = 1, MOE_ACT_SWIGLU = 2 } moe_act_t;
+
+typedef struct moe_config {
+  int64_t T;                /* tokens in the batch                               */
+  int64_t d;                /* model width                                       */
+  int64_t E;                /* routed experts                                    */
+  int64_t k;                /* experts per token, 1 <= k <= min(E, 8)            */
+  int64_t h;                /* expert hidden width                               */
+  int64_t n_shared;         /* always-on shared experts (same act and h), >= 0   */
+  double capacity_factor;   /* > 0: C = floor(factor*T*k/E); <= 0: dropless, C=T */
+  int32_t act;              /* moe_act_t                                         */
+  int32_t dtype;            /* moe_dtype_t of x, y and every weight matrix       */
+  int32_t ffn_bias;         /* nonzero: b1 [E,h], b2 [E,d] are given             */
+  int32_t router_bias;      /* nonzero: b_g [E] is given                         */
+  int32_t router_noise;     /* nonzero: w_noise [E,d] and eps [T,E] are given    */
+} moe_config_t;
+
+/* Device pointers to the layer's parameters (unused ones may be NULL). */
+typedef struct moe_weights {
+  const void* w_g;      const float* b_g;     const void* w_noise;
+  const void* w1;       const void* w3;       const void* w2;
+  const float* b1;      const float* b2;
+  const void* ws1;      const void* ws3;      const void* ws2;
+} moe_weights_t;
+
+/* Optional outputs of moe_layer_forward: each non-NULL member receives the
+ * same values the stage entry points would write; NULL members live in the
+ * workspace instead. */
+typedef struct moe_aux {
+  float*   logits;      /* [T,E]                                              */
+  int32_t* topk_idx;    /* [T,k]                                              */
+  float*   topk_gate;   /* [T,k]                                              */
+  float*   prob_sum;    /* [E]                                                */
+  int32_t* counts;      /* [E]                                                */
+  int32_t* offsets;     /* [E+1]                                              */
+  int32_t* dest;        /* [T,k]                                              */
+  int32_t* row_token;   /* [T*k]                                              */
+  float*   stats;       /* [2E+2]                                             */
+} moe_aux_t;
+
+/* (host) Human-readable name of a status code; never NULL. */
+const char* moe_status_string(int status);
+
+/* (host) Expert capacity C = floor(capacity_factor * T * k / E) evaluated in
+ * IEEE double left to right ([3D-lab] Capacity panel; at k = 1 this is [LLM-09]
+ * s.3's factor * T / E), or T when capacity_factor <= 0 (dropless: a token's k
+ * experts are distinct, so no expert can receive more than T assignments).
+ * No clamp: C may be 0, and then every routed assignment is dropped.
+ * Returns -1 for an invalid config. */
+int64_t moe_capacity(const moe_config_t* cfg);
+
+/* (host) Upper bound on the rows any routed expert buffer can hold in total:
+ * min(T*k, E*C).  Returns -1 for an invalid config. */
+int64_t moe_routed_rows_bound(const moe_config_t* cfg);
+
+/* (host) Workspace bytes that suffice for every entry point below and for
+ * moe_layer_forward with all moe_aux_t members NULL.  0 for an invalid config. */
+size_t moe_workspace_bytes(const moe_config_t* cfg);
+
+/*
+ * Router and gating ([MoE&SMS] Mathematical Formulation; [LLM-09] s.2;
+ * [3D-lab] Router).
+ *   logits[t,e] = x[t] . w_g[e] (+ b_g[e]) (+ eps[t,e] * softplus(x[t] . w_noise[e]))
+ *   topk_idx[t,s]: the k experts with the largest float32 logits, slot 0 best;
+ *     equal logits go to the lower expert index ([MoEM] asks for a fixed tie
+ *     rule); -0.0 and +0.0 compare equal.
+ *   topk_gate[t,s] = exp(l_s - l_0) / sum_j exp(l_j - l_0) over the k selected
+ *     logits, which equals the renormalised full-softmax probabilities.
+ *   prob_sum[e] = sum_t softmax(logits[t])_e (the P_i numerator of L_aux).
+ * x == NULL selects replay mode: `logits` is then an INPUT [T,E] (for example
+ * logits computed elsewhere) and w_g, b_g, w_noise, eps are ignored.
+ * Products accumulate in float32 (bf16 inputs on MFMA).  Deterministic.
+ * Workspace: at least moe_workspace_bytes(cfg).
+ */
+moe_status_t moe_route(const moe_config_t* cfg, const void* x, const void* w_g,
+                       const float* b_g, const void* w_noise, const float* eps,
+                       float* logits, int32_t* topk_idx, float* topk_gate,
+                       float* prob_sum, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Counts, capacity and dispatch tables ([MoE&SMS] lab 3 and Advanced Theory;
+ * [MoEM] "Capacity limits make dispatch observable"; [SMoE-arch] grouping).
+ * Assignments are taken in arrival order i = t*k + s.  With C = moe_capacity:
+ *   counts[e]     number of assignments routed to e (before capacity)
+ *   rank(t,s)     number of earlier assignments (smaller i) to the same expert
+ *   kept          rank < C; dropped assignments contribute nothing later
+ *   offsets[e]    exclusive prefix sum over experts of min(counts, C); [E+1]
+ *   dest[t,s]     offsets[e] + rank if kept, else -1
+ *   row_token[r]  token of buffer row r, for r < offsets[E]; rows of one
+ *                 expert are in arrival (token) order
+ *   x_perm[r,:]   = x[row_token[r],:]  (optional: x and x_perm may both be NULL)
+ * Integer results are exact and deterministic.  row_token rows at or beyond
+ * offsets[E] and x_perm rows beyond it are left untouched.
+ */
+moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx,
+                          const void* x, int32_t* counts, int32_t* offsets,
+                          int32_t* dest, int32_t* row_token, void* x_perm,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Grouped expert FFN over expert-contiguous rows ([MoE&SMS] Core Concepts:
+ * each expert is an FFN with its own weights; [SMoE-arch] each expert runs
+ * once on its grouped tokens).  For every group g < n_groups and every row r in
+ * [offsets[g], offsets[g+1]):
+ *   y_rows[r,:] (+)= act(a_r w1[g]^T (+ b1[g]) [, a_r w3[g]^T]) w2[g]^T (+ b2[g])
+ * where a_r = x_rows[r] if row_token == NULL, else x_rows[row_token[r]] (a
+ * gather straight from the token matrix, so no permuted copy is needed).
+ * The hidden layer is stored in the config dtype (bf16 for bf16 configs).
+ *   offsets      [n_groups+1] device int32, nondecreasing, offsets[0] = 0
+ *   rows_bound   (host) upper bound on offsets[n_groups]; sizes the launch
+ *   group_bound  (host) upper bound on any single group's row count; small
+ *                bounds (<= 32) select the weight-streaming kernels
+ *   accumulate   nonzero: add into y_rows instead of overwriting
+ * n_groups <= E, and w1/w3/w2/b1/b2 hold at least n_groups experts.
+ * Workspace: at least moe_workspace_bytes(cfg).
+ */
+moe_status_t moe_expert_ffn(const moe_config_t* cfg, int64_t n_groups,
+                            const void* x_rows, const int32_t* row_token,
+                            const int32_t* offsets, int64_t rows_bound,
+                            int64_t group_bound, const void* w1, const void* w3,
+                            const void* w2, const float* b1, const float* b2,
+                            float* y_rows, int accumulate, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/*
+ * The two halves of moe_expert_ffn, for callers that time or reuse them:
+ *   moe_expert_up:   hidden[r,:] = act(a_r w1[g]^T (+ b1[g]) [, a_r w3[g]^T])
+ *                    hidden has rows_bound rows of h elements, config dtype.
+ *   moe_expert_down: y_rows[r,:] (+)= hidden[r] w2[g]^T (+ b2[g])
+ * Arguments mean what they mean for moe_expert_ffn.  Both halves rebuild the
+ * same tile schedule from `offsets`, so they must be given the same offsets,
+ * rows_bound and group_bound.
+ */
+moe_status_t moe_expert_up(const moe_config_t* cfg, int64_t n_groups,
+                           const void* x_rows, const int32_t* row_token,
+                           const int32_t* offsets, int64_t rows_bound, int64_t group_bound,
+                           const void* w1, const void* w3, const float* b1,
+                           void* hidden, void* ws, size_t ws_bytes, hipStream_t stream);
+
+moe_status_t moe_expert_down(const moe_config_t* cfg, int64_t n_groups,
+                             const void* hidden, const int32_t* offsets,
+                             int64_t rows_bound, int64_t group_bound, const void* w2,
+                             const float* b2, float* y_rows, int accumulate,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Gate-weighted combine and statistics ([MoE&SMS] Mathematical Formulation:
+ * weighted sum over the selected experts and L_aux = N sum f_i P_i; [LLM-09]
+ * s.1 and s.4; [MoEM] "Overflow handling defines an output contract").
+ *   y[t,:] = sum_{s < n_shared} y_shared[s,t,:] + sum_{slot} [dest >= 0]
+ *            topk_gate[t,slot] * y_rows[dest[t,slot],:]
+ * accumulated in float32 in that order (shared experts first, then slot 0,
+ * 1, ...) and stored in the config dtype (bf16 with round-to-nearest-even).
+ * Dropped slots add nothing and the surviving gates are not rescaled.
+ *   y_shared  [n_shared, T, d] float32, or NULL when n_shared == 0
+ *   stats     optional [2E+2]: f[E] = counts/(T*k), P[E] = prob_sum/T,
+ *             L_aux = E * sum f P (alpha = 1), drop_rate = 1 - sum min(counts,C)/(T*k)
+ */
+moe_status_t moe_combine(const moe_config_t* cfg, const float* y_rows,
+                         const int32_t* dest, const float* topk_gate,
+                         const float* y_shared, const int32_t* counts,
+                         const float* prob_sum, void* y, float* stats,
+                         hipStream_t stream);
+
+/*
+ * The whole layer: moe_route -> moe_dispatch -> grouped FFN over the routed
+ * experts and the shared experts -> moe_combine, on one stream, with no host
+ * synchronisation.  `logits_in` != NULL replays supplied float32 logits [T,E]
+ * instead of computing them (w_g, b_g, w_noise and eps are then unused).
+ * `eps` is the [T,E] noise for noisy gating (required when router_noise).
+ * Intermediates live in `ws` unless `aux` names a buffer for them.
+ */
+moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w,
+                               const void* x, const float* eps, const float* logits_in,
+                               void* y, const moe_aux_t* aux, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,478 @@
+// C ABI of the sparse MoE layer forward: argument validation, workspace
+// planning and launch orchestration on the caller's stream.  No allocation,
+// no synchronisation; every failure is reported before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/moe.h"
+#include "launch.hpp"
+
+namespace moe {
+hipError_t launch_ffn_tiled(const FfnParams& p, hipStream_t stream);
+hipError_t launch_ffn_skinny(const FfnParams& p, hipStream_t stream);
+hipError_t launch_ffn_f32(const FfnParams& p, hipStream_t stream);
+
+// float32 -> plain kernel; <= 32 rows in every group (shared groups hold T
+// rows) -> weight-streaming kernel; otherwise the tiled MFMA kernel.
+hipError_t launch_ffn(const FfnParams& p, hipStream_t stream) {
+  if (!p.bf16) return launch_ffn_f32(p, stream);
+  const bool small = p.group_bound <= 32 && (p.S == 0 || p.T <= 32);
+  return small ? launch_ffn_skinny(p, stream) : launch_ffn_tiled(p, stream);
+}
+}  // namespace moe
+
+namespace {
+
+using namespace moe;
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;  // 32-bit element offsets in kernels
+
+struct Cfg {
+  int64_t T, d, E, k, h, S;
+  int act, bf16;
+  int64_t C;      // capacity, clamped to T (no expert can receive more)
+  int64_t R;      // routed rows bound min(T*k, E*C)
+  size_t esz;     // bytes per activation / weight element
+};
+
+int64_t capacity_of(const moe_config_t* c) {
+  if (c->capacity_factor <= 0.0) return c->T;
+  const double v = floor(c->capacity_factor * (double)c->T * (double)c->k / (double)c->E);
+  if (!(v >= 0.0)) return 0;
+  return v > 9.0e18 ? INT64_MAX : (int64_t)v;
+}
+
+moe_status_t check_cfg(const moe_config_t* c, Cfg* o) {
+  if (!c) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->T < 0 || c->d <= 0 || c->E <= 0 || c->h <= 0 || c->k < 1 || c->k > c->E ||
+      c->n_shared < 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (c->act < 0 || c->act > 2 || (c->dtype != MOE_F32 && c->dtype != MOE_BF16))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (isnan(c->capacity_factor)) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->E > 256 || c->k > 8 || c->d % 8 || c->h % 8) return MOE_ERR_UNSUPPORTED;
+  if (c->router_noise && c->E > 128) return MOE_ERR_UNSUPPORTED;
+  if (c->n_shared > 64) return MOE_ERR_UNSUPPORTED;
+  o->T = c->T; o->d = c->d; o->E = c->E; o->k = c->k; o->h = c->h; o->S = c->n_shared;
+  o->act = c->act;
+  o->bf16 = c->dtype == MOE_BF16;
+  o->esz = o->bf16 ? 2 : 4;
+  o->C = std::min<int64_t>(capacity_of(c), c->T);
+  o->R = std::min<int64_t>(c->T * c->k, c->E * o->C);
+  const int64_t rows = o->R + o->S * o->T;
+  if (o->T * o->k >= kMaxElems || o->T * o->d >= kMaxElems || o->T * o->E >= kMaxElems ||
+      rows * std::max(o->d, o->h) >= kMaxElems || o->d * o->h >= kMaxElems)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+bool aligned(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Sequential 256-byte-aligned sub-allocation of the caller's workspace; with a
+// null base it only measures.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    off = (off + 255) & ~(size_t)255;
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+struct RouteWs { float* prob_partial; };
+struct DispatchWs { int32_t* local_rank; int32_t* chunk_hist; };
+struct FfnWs { TileEntry* entries; int32_t* n_entries; };
+
+RouteWs carve_route(Carve& cv, const Cfg& c) {
+  return {static_cast<float*>(cv.take((size_t)route_blocks(c.T) * c.E * 4))};
+}
+DispatchWs carve_dispatch(Carve& cv, const Cfg& c) {
+  DispatchWs w;
+  w.local_rank = static_cast<int32_t*>(cv.take((size_t)c.T * c.k * 4));
+  w.chunk_hist = static_cast<int32_t*>(cv.take((size_t)dispatch_chunks(c.T * c.k) * c.E * 4));
+  return w;
+}
+FfnWs carve_ffn(Carve& cv, int64_t rows_bound, int64_t groups, int64_t S, int64_t T) {
+  FfnWs w;
+  w.entries = static_cast<TileEntry*>(
+      cv.take((size_t)ffn_max_entries(rows_bound, (int)groups, (int)S, (int)T) * sizeof(TileEntry)));
+  w.n_entries = static_cast<int32_t*>(cv.take(4));
+  return w;
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Workspace of the whole layer: intermediates plus every stage's scratch.
+struct LayerWs {
+  float* logits; int32_t* idx; float* gate; float* prob_sum;
+  int32_t* counts; int32_t* offsets; int32_t* dest; int32_t* row_token;
+  void* hidden; float* y_rows;
+  RouteWs rw; DispatchWs dw; FfnWs fw;
+};
+
+LayerWs carve_layer(Carve& cv, const Cfg& c, const moe_aux_t* aux) {
+  LayerWs w;
+  const size_t tk = (size_t)c.T * c.k;
+  auto pick = [&](void* given, size_t bytes) { return given ? given : cv.take(bytes); };
+  w.logits = static_cast<float*>(pick(aux ? aux->logits : nullptr, (size_t)c.T * c.E * 4));
+  w.idx = static_cast<int32_t*>(pick(aux ? aux->topk_idx : nullptr, tk * 4));
+  w.gate = static_cast<float*>(pick(aux ? aux->topk_gate : nullptr, tk * 4));
+  w.prob_sum = static_cast<float*>(pick(aux ? aux->prob_sum : nullptr, (size_t)c.E * 4));
+  w.counts = static_cast<int32_t*>(pick(aux ? aux->counts : nullptr, (size_t)c.E * 4));
+  w.offsets = static_cast<int32_t*>(pick(aux ? aux->offsets : nullptr, (size_t)(c.E + 1) * 4));
+  w.dest = static_cast<int32_t*>(pick(aux ? aux->dest : nullptr, tk * 4));
+  w.row_token = static_cast<int32_t*>(pick(aux ? aux->row_token : nullptr, tk * 4));
+  const int64_t rows = c.R + c.S * c.T;
+  w.hidden = cv.take((size_t)rows * c.h * c.esz);
+  w.y_rows = static_cast<float*>(cv.take((size_t)rows * c.d * 4));
+  w.rw = carve_route(cv, c);
+  w.dw = carve_dispatch(cv, c);
+  w.fw = carve_ffn(cv, c.R, c.E, c.S, c.T);
+  return w;
+}
+
+size_t layer_ws_bytes(const Cfg& c) {
+  Carve cv(nullptr);
+  carve_layer(cv, c, nullptr);
+  return cv.off + 256;
+}
+
+// Expert FFN workspace for a stage call: tile schedule (+ hidden rows).
+size_t ffn_ws_bytes(const Cfg& c, int64_t rows_bound, int64_t groups, bool with_hidden) {
+  Carve cv(nullptr);
+  carve_ffn(cv, rows_bound, groups, 0, c.T);
+  if (with_hidden) cv.take((size_t)rows_bound * c.h * c.esz);
+  return cv.off + 256;
+}
+
+FfnParams ffn_params(const Cfg& c, int64_t n_groups, const int32_t* offsets, int64_t rows_bound,
+                     int64_t group_bound, const FfnWs& fw) {
+  FfnParams p;
+  memset(&p, 0, sizeof(p));
+  p.offsets = offsets;
+  p.G = (int)n_groups;
+  p.S = 0;
+  p.T = (int)c.T;
+  p.rows_bound = rows_bound;
+  p.group_bound = group_bound;
+  p.bf16 = c.bf16;
+  p.entries = fw.entries;
+  p.n_entries = fw.n_entries;
+  return p;
+}
+
+moe_status_t check_ffn_args(const Cfg& c, int64_t n_groups, const int32_t* offsets,
+                            int64_t rows_bound, int64_t group_bound) {
+  if (n_groups < 0 || n_groups > 256 || rows_bound < 0 || group_bound < 0 || !offsets)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (group_bound > rows_bound && n_groups > 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (rows_bound * std::max(c.d, c.h) >= kMaxElems) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(offsets)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status_t run_up(const Cfg& c, FfnParams p, const void* x_rows, const int32_t* row_token,
+                    const void* w1, const void* w3, const float* b1, void* hidden,
+                    hipStream_t s) {
+  p.a_main = x_rows; p.a_shared = x_rows; p.gather = row_token; p.a_from_c = 0;
+  p.w_main = w1; p.u_main = w3; p.bias_main = b1;
+  p.out = hidden; p.out_bf16 = c.bf16; p.accumulate = 0;
+  p.N = (int)c.h; p.K = (int)c.d; p.act = c.act;
+  return hip_status(launch_ffn(p, s));
+}
+
+moe_status_t run_down(const Cfg& c, FfnParams p, const void* hidden, const void* w2,
+                      const float* b2, float* y_rows, int accumulate, hipStream_t s) {
+  p.a_main = hidden; p.a_shared = hidden; p.gather = nullptr; p.a_from_c = 1;
+  p.w_main = w2; p.u_main = nullptr; p.bias_main = b2;
+  p.out = y_rows; p.out_bf16 = 0; p.accumulate = accumulate;
+  p.N = (int)c.d; p.K = (int)c.h; p.act = -1;
+  return hip_status(launch_ffn(p, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int64_t moe_capacity(const moe_config_t* cfg) {
+  Cfg c;
+  if (check_cfg(cfg, &c) == MOE_ERR_INVALID_ARGUMENT) return -1;
+  return capacity_of(cfg);
+}
+
+int64_t moe_routed_rows_bound(const moe_config_t* cfg) {
+  Cfg c;
+  if (check_cfg(cfg, &c) != MOE_OK) return -1;
+  return c.R;
+}
+
+size_t moe_workspace_bytes(const moe_config_t* cfg) {
+  Cfg c;
+  if (check_cfg(cfg, &c) != MOE_OK) return 0;
+  size_t b = layer_ws_bytes(c);
+  b = std::max(b, ffn_ws_bytes(c, std::max(c.R, c.T), c.E, true));
+  return b;
+}
+
+moe_status_t moe_route(const moe_config_t* cfg, const void* x, const void* w_g,
+                       const float* b_g, const void* w_noise, const float* eps,
+                       float* logits, int32_t* topk_idx, float* topk_gate, float* prob_sum,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  Cfg c;
+  moe_status_t st = check_cfg(cfg, &c);
+  if (st != MOE_OK) return st;
+  if (!logits || !topk_idx || !topk_gate || !prob_sum || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (x) {
+    if (!w_g) return MOE_ERR_INVALID_ARGUMENT;
+    if (cfg->router_bias && !b_g) return MOE_ERR_INVALID_ARGUMENT;
+    if (cfg->router_noise && (!w_noise || !eps)) return MOE_ERR_INVALID_ARGUMENT;
+  }
+  const void* ptrs[] = {x, w_g, b_g, w_noise, eps, logits, topk_idx, topk_gate, prob_sum, ws};
+  for (const void* q : ptrs)
+    if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
+  Carve cv(nullptr);
+  carve_route(cv, c);
+  if (ws_bytes < cv.off + 256) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (c.T == 0) return MOE_OK;
+  Carve wv(ws);
+  RouteParams p;
+  p.x = x;
+  p.w_g = w_g;
+  p.b_g = x && cfg->router_bias ? b_g : nullptr;
+  p.w_noise = x && cfg->router_noise ? w_noise : nullptr;
+  p.eps = x && cfg->router_noise ? eps : nullptr;
+  p.logits = logits; p.idx = topk_idx; p.gate = topk_gate;
+  p.prob_partial = carve_route(wv, c).prob_partial;
+  p.prob_sum = prob_sum;
+  p.T = (int)c.T; p.d = (int)c.d; p.E = (int)c.E; p.k = (int)c.k; p.bf16 = c.bf16;
+  return hip_status(launch_route(p, stream));
+}
+
+moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx, const void* x,
+                          int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* row_token,
+                          void* x_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Cfg c;
+  moe_status_t st = check_cfg(cfg, &c);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !counts || !offsets || !dest || !row_token || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {topk_idx, x, counts, offsets, dest, row_token, x_perm, ws};
+  for (const void* q : ptrs)
+    if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
+  Carve cv(nullptr);
+  carve_dispatch(cv, c);
+  if (ws_bytes < cv.off + 256) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (c.T == 0) return MOE_OK;
+  Carve wv(ws);
+  DispatchWs dw = carve_dispatch(wv, c);
+  DispatchParams p;
+  p.idx = topk_idx; p.counts = counts; p.offsets = offsets; p.dest = dest;
+  p.row_token = row_token; p.local_rank = dw.local_rank; p.chunk_hist = dw.chunk_hist;
+  p.n = (int)(c.T * c.k); p.k = (int)c.k; p.E = (int)c.E; p.C = (int)c.C;
+  st = hip_status(launch_dispatch(p, stream));
+  if (st != MOE_OK || !x) return st;
+  return hip_status(launch_permute(x, row_token, offsets + c.E, x_perm,
+                                   (int64_t)c.d * (int64_t)c.esz, c.R, stream));
+}
+
+moe_status_t moe_expert_up(const moe_config_t* cfg, int64_t n_groups, const void* x_rows,
+                           const int32_t* row_token, const int32_t* offsets, int64_t rows_bound,
+                           int64_t group_bound, const void* w1, const void* w3, const float* b1,
+                           void* hidden, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Cfg c;
+  moe_status_t st = check_cfg(cfg, &c);
+  if (st != MOE_OK) return st;
+  st = check_ffn_args(c, n_groups, offsets, rows_bound, group_bound);
+  if (st != MOE_OK) return st;
+  if (!x_rows || !w1 || !hidden || !ws || (c.act == MOE_ACT_SWIGLU && !w3))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {x_rows, row_token, w1, w3, b1, hidden, ws};
+  for (const void* q : ptrs)
+    if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < ffn_ws_bytes(c, rows_bound, n_groups, false)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (n_groups == 0 || rows_bound == 0) return MOE_OK;
+  Carve wv(ws);
+  FfnWs fw = carve_ffn(wv, rows_bound, n_groups, 0, c.T);
+  return run_up(c, ffn_params(c, n_groups, offsets, rows_bound, group_bound, fw), x_rows,
+                row_token, w1, w3, b1, hidden, stream);
+}
+
+moe_status_t moe_expert_down(const moe_config_t* cfg, int64_t n_groups, const void* hidden,
+                             const int32_t* offsets, int64_t rows_bound, int64_t group_bound,
+                             const void* w2, const float* b2, float* y_rows, int accumulate,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  Cfg c;
+  moe_status_t st = check_cfg(cfg, &c);
+  if (st != MOE_OK) return st;
+  st = check_ffn_args(c, n_groups, offsets, rows_bound, group_bound);
+  if (st != MOE_OK) return st;
+  if (!hidden || !w2 || !y_rows || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {hidden, w2, b2, y_rows, ws};
+  for (const void* q : ptrs)
+    if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < ffn_ws_bytes(c, rows_bound, n_groups, false)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (n_groups == 0 || rows_bound == 0) return MOE_OK;
+  Carve wv(ws);
+  FfnWs fw = carve_ffn(wv, rows_bound, n_groups, 0, c.T);
+  return run_down(c, ffn_params(c, n_groups, offsets, rows_bound, group_bound, fw), hidden, w2,
+                  b2, y_rows, accumulate, stream);
+}
+
+moe_status_t moe_expert_ffn(const moe_config_t* cfg, int64_t n_groups, const void* x_rows,
+                            const int32_t* row_token, const int32_t* offsets, int64_t rows_bound,
+                            int64_t group_bound, const void* w1, const void* w3, const void* w2,
+                            const float* b1, const float* b2, float* y_rows, int accumulate,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  Cfg c;
+  moe_status_t st = check_cfg(cfg, &c);
+  if (st != MOE_OK) return st;
+  st = check_ffn_args(c, n_groups, offsets, rows_bound, group_bound);
+  if (st != MOE_OK) return st;
+  if (!x_rows || !w1 || !w2 || !y_rows || !ws || (c.act == MOE_ACT_SWIGLU && !w3))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {x_rows, row_token, w1, w3, w2, b1, b2, y_rows, ws};
+  for (const void* q : ptrs)
+    if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < ffn_ws_bytes(c, rows_bound, n_groups, true)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (n_groups == 0 || rows_bound == 0) return MOE_OK;
+  Carve wv(ws);
+  FfnWs fw = carve_ffn(wv, rows_bound, n_groups, 0, c.T);
+  void* hidden = wv.take((size_t)rows_bound * c.h * c.esz);
+  FfnParams p = ffn_params(c, n_groups, offsets, rows_bound, group_bound, fw);
+  st = run_up(c, p, x_rows, row_token, w1, w3, b1, hidden, stream);
+  if (st != MOE_OK) return st;
+  return run_down(c, p, hidden, w2, b2, y_rows, accumulate, stream);
+}
+
+moe_status_t moe_combine(const moe_config_t* cfg, const float* y_rows, const int32_t* dest,
+                         const float* topk_gate, const float* y_shared, const int32_t* counts,
+                         const float* prob_sum, void* y, float* stats, hipStream_t stream) {
+  Cfg c;
+  moe_status_t st = check_cfg(cfg, &c);
+  if (st != MOE_OK) return st;
+  if (!y_rows || !dest || !topk_gate || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.S > 0 && !y_shared) return MOE_ERR_INVALID_ARGUMENT;
+  if (stats && (!counts || !prob_sum)) return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {y_rows, dest, topk_gate, y_shared, counts, prob_sum, y, stats};
+  for (const void* q : ptrs)
+    if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
+  if (c.T == 0) return MOE_OK;
+  CombineParams p;
+  p.y_rows = y_rows; p.dest = dest; p.gate = topk_gate;
+  p.y_shared = c.S > 0 ? y_shared : nullptr;
+  p.y = y; p.T = (int)c.T; p.d = (int)c.d; p.k = (int)c.k; p.S = (int)c.S; p.out_bf16 = c.bf16;
+  st = hip_status(launch_combine(p, stream));
+  if (st != MOE_OK || !stats) return st;
+  StatsParams sp;
+  sp.counts = counts; sp.prob_sum = prob_sum; sp.stats = stats;
+  sp.T = (int)c.T; sp.k = (int)c.k; sp.E = (int)c.E; sp.C = (int)c.C;
+  return hip_status(launch_stats(sp, stream));
+}
+
+moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                               const float* eps, const float* logits_in, void* y,
+                               const moe_aux_t* aux, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  Cfg c;
+  moe_status_t st = check_cfg(cfg, &c);
+  if (st != MOE_OK) return st;
+  if (!w || !x || !y || !ws || !w->w1 || !w->w2) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.act == MOE_ACT_SWIGLU && !w->w3) return MOE_ERR_INVALID_ARGUMENT;
+  if (cfg->ffn_bias && (!w->b1 || !w->b2)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!logits_in) {
+    if (!w->w_g) return MOE_ERR_INVALID_ARGUMENT;
+    if (cfg->router_bias && !w->b_g) return MOE_ERR_INVALID_ARGUMENT;
+    if (cfg->router_noise && (!w->w_noise || !eps)) return MOE_ERR_INVALID_ARGUMENT;
+  }
+  if (c.S > 0 && (!w->ws1 || !w->ws2 || (c.act == MOE_ACT_SWIGLU && !w->ws3)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {x, eps, logits_in, y, ws, w->w_g, w->b_g, w->w_noise, w->w1, w->w3,
+                        w->w2, w->b1, w->b2, w->ws1, w->ws3, w->ws2};
+  for (const void* q : ptrs)
+    if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
+  if (aux) {
+    const void* ap[] = {aux->logits, aux->topk_idx, aux->topk_gate, aux->prob_sum, aux->counts,
+                        aux->offsets, aux->dest, aux->row_token, aux->stats};
+    for (const void* q : ap)
+      if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
+  }
+  {
+    Carve cv(nullptr);
+    carve_layer(cv, c, aux);
+    if (ws_bytes < cv.off + 256) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  }
+  if (c.T == 0) return MOE_OK;
+  Carve wv(ws);
+  LayerWs L = carve_layer(wv, c, aux);
+
+  // 1-2. router, top-k, gates, softmax sums
+  RouteParams rp;
+  rp.x = logits_in ? nullptr : x;
+  rp.w_g = w->w_g;
+  rp.b_g = cfg->router_bias ? w->b_g : nullptr;
+  rp.w_noise = cfg->router_noise ? w->w_noise : nullptr;
+  rp.eps = cfg->router_noise ? eps : nullptr;
+  rp.logits = logits_in ? const_cast<float*>(logits_in) : L.logits;
+  rp.idx = L.idx; rp.gate = L.gate; rp.prob_partial = L.rw.prob_partial; rp.prob_sum = L.prob_sum;
+  rp.T = (int)c.T; rp.d = (int)c.d; rp.E = (int)c.E; rp.k = (int)c.k; rp.bf16 = c.bf16;
+  if ((st = hip_status(launch_route(rp, stream))) != MOE_OK) return st;
+
+  // 3. counts, capacity, dispatch tables
+  DispatchParams dp;
+  dp.idx = L.idx; dp.counts = L.counts; dp.offsets = L.offsets; dp.dest = L.dest;
+  dp.row_token = L.row_token; dp.local_rank = L.dw.local_rank; dp.chunk_hist = L.dw.chunk_hist;
+  dp.n = (int)(c.T * c.k); dp.k = (int)c.k; dp.E = (int)c.E; dp.C = (int)c.C;
+  if ((st = hip_status(launch_dispatch(dp, stream))) != MOE_OK) return st;
+
+  // 4. grouped expert FFN: routed groups gathered through row_token, then the
+  //    shared experts over all tokens, in one launch per projection
+  FfnParams fp = ffn_params(c, c.E, L.offsets, c.R, c.C, L.fw);
+  fp.S = (int)c.S;
+  FfnParams up = fp;
+  up.a_main = x; up.a_shared = x; up.gather = L.row_token; up.a_from_c = 0;
+  up.w_main = w->w1; up.u_main = w->w3; up.w_shared = w->ws1; up.u_shared = w->ws3;
+  up.bias_main = cfg->ffn_bias ? w->b1 : nullptr; up.bias_shared = nullptr;
+  up.out = L.hidden; up.out_bf16 = c.bf16; up.accumulate = 0;
+  up.N = (int)c.h; up.K = (int)c.d; up.act = c.act;
+  if ((st = hip_status(launch_ffn(up, stream))) != MOE_OK) return st;
+  FfnParams dn = fp;
+  dn.a_main = L.hidden; dn.a_shared = L.hidden; dn.gather = nullptr; dn.a_from_c = 1;
+  dn.w_main = w->w2; dn.u_main = nullptr; dn.w_shared = w->ws2; dn.u_shared = nullptr;
+  dn.bias_main = cfg->ffn_bias ? w->b2 : nullptr; dn.bias_shared = nullptr;
+  dn.out = L.y_rows; dn.out_bf16 = 0; dn.accumulate = 0;
+  dn.N = (int)c.d; dn.K = (int)c.h; dn.act = -1;
+  if ((st = hip_status(launch_ffn(dn, stream))) != MOE_OK) return st;
+
+  // 5. combine (+ statistics)
+  CombineParams cp;
+  cp.y_rows = L.y_rows; cp.dest = L.dest; cp.gate = L.gate;
+  cp.y_shared = c.S > 0 ? L.y_rows + (size_t)c.R * c.d : nullptr;
+  cp.y = y; cp.T = (int)c.T; cp.d = (int)c.d; cp.k = (int)c.k; cp.S = (int)c.S;
+  cp.out_bf16 = c.bf16;
+  if ((st = hip_status(launch_combine(cp, stream))) != MOE_OK) return st;
+  if (aux && aux->stats) {
+    StatsParams sp;
+    sp.counts = L.counts; sp.prob_sum = L.prob_sum; sp.stats = aux->stats;
+    sp.T = (int)c.T; sp.k = (int)c.k; sp.E = (int)c.E; sp.C = (int)c.C;
+    if ((st = hip_status(launch_stats(sp, stream))) != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+}  // extern "C"

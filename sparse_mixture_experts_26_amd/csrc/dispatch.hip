@@ -1,0 +1,156 @@
+// Per-expert counts, capacity and expert-contiguous dispatch tables.
+//
+// "Mixture-of-Experts & Sparse Model Scaling", lab 3 and Advanced Theory: each
+// expert accepts assignments in arrival order until it holds C of them, the
+// rest are dropped; "Mixture-of-experts Models", Level 2: loads and overflow
+// per expert; "Scaling Capacity via Sparse MoE Architectures": tokens are
+// grouped by their expert.  Arrival order is the flat index i = t*k + s.
+//
+// The sequential walk becomes a stable counting sort in three launches:
+//   1. rank:   per 1024-assignment chunk, each 64-lane slice finds the lanes
+//              holding the same expert with 9 ballots, so its stable rank within
+//              the slice is a popcount; slice histograms in LDS are prefix-summed
+//              in slice order to give the rank within the chunk and the chunk's
+//              per-expert histogram.
+//   2. scan:   one block turns the chunk histograms into per-chunk bases (chunk
+//              order), counts, kept = min(counts, C) and the offsets.
+//   3. assign: rank = base + local rank; kept iff rank < C; dest and row_token.
+// Every step is ordered, so the integer outputs are exact and deterministic.
+#include "launch.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kSlices = kDispatchChunk / 64;  // 16 slices of 64 per chunk
+constexpr int kInvalid = 511;                 // expert id that matches no expert
+
+__global__ __launch_bounds__(256) void dispatch_rank_kernel(DispatchParams p) {
+  __shared__ int hist[kSlices][256];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kSlices * 256; i += 256) (&hist[0][0])[i] = 0;
+  __syncthreads();
+  const int64_t chunk0 = (int64_t)blockIdx.x * kDispatchChunk;
+  int my_e[4], my_r[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int s = w + 4 * r;
+    const int64_t i = chunk0 + s * 64 + lane;
+    int e = kInvalid;
+    if (i < p.n) {
+      e = p.idx[i];
+      if (e < 0 || e >= p.E) e = kInvalid;
+    }
+    uint64_t peers = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 9; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      peers &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+    if (e != kInvalid && rank == 0) hist[s][e] = __popcll(peers);
+    my_e[r] = e;
+    my_r[r] = rank;
+  }
+  __syncthreads();
+  if (threadIdx.x < p.E) {
+    const int e = threadIdx.x;
+    int run = 0;
+    for (int s = 0; s < kSlices; ++s) {
+      const int c = hist[s][e];
+      hist[s][e] = run;
+      run += c;
+    }
+    p.chunk_hist[(int64_t)blockIdx.x * p.E + e] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int s = w + 4 * r;
+    const int64_t i = chunk0 + s * 64 + lane;
+    if (i < p.n) p.local_rank[i] = my_e[r] == kInvalid ? -1 : hist[s][my_e[r]] + my_r[r];
+  }
+}
+
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(DispatchParams p, int nchunks) {
+  __shared__ int skept[256];
+  const int e = threadIdx.x;
+  int kept = 0;
+  if (e < p.E) {
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      int* cell = p.chunk_hist + (int64_t)c * p.E + e;
+      const int v = *cell;
+      *cell = run;  // becomes the chunk's base rank for expert e
+      run += v;
+    }
+    p.counts[e] = run;
+    kept = run < p.C ? run : p.C;
+  }
+  skept[e] = kept;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over 256 experts.
+  for (int o = 1; o < 256; o <<= 1) {
+    const int v = e >= o ? skept[e - o] : 0;
+    __syncthreads();
+    skept[e] += v;
+    __syncthreads();
+  }
+  if (e < p.E) p.offsets[e] = skept[e] - kept;
+  if (e == p.E - 1) p.offsets[p.E] = skept[e];
+}
+
+__global__ __launch_bounds__(256) void dispatch_assign_kernel(DispatchParams p) {
+  const int64_t chunk0 = (int64_t)blockIdx.x * kDispatchChunk;
+  for (int j = threadIdx.x; j < kDispatchChunk; j += 256) {
+    const int64_t i = chunk0 + j;
+    if (i >= p.n) break;
+    const int lr = p.local_rank[i];
+    int d = -1;
+    if (lr >= 0) {
+      const int e = p.idx[i];
+      const int rank = p.chunk_hist[(int64_t)blockIdx.x * p.E + e] + lr;
+      if (rank < p.C) {
+        d = p.offsets[e] + rank;
+        p.row_token[d] = (int)(i / p.k);
+      }
+    }
+    p.dest[i] = d;
+  }
+}
+
+// One wave per destination row; 16-byte copies.
+__global__ __launch_bounds__(256) void permute_kernel(const uint4* x, const int32_t* row_token,
+                                                      const int32_t* total, uint4* xp,
+                                                      int64_t row_vecs) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= *total) return;
+  const int64_t t = row_token[r];
+  const uint4* src = x + t * row_vecs;
+  uint4* dst = xp + r * row_vecs;
+  for (int64_t c = lane; c < row_vecs; c += 64) dst[c] = src[c];
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const DispatchParams& p, hipStream_t stream) {
+  const int chunks = dispatch_chunks(p.n);
+  hipLaunchKernelGGL(dispatch_rank_kernel, dim3(chunks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, stream, p, chunks);
+  hipLaunchKernelGGL(dispatch_assign_kernel, dim3(chunks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const void* x, const int32_t* row_token, const int32_t* total,
+                          void* x_perm, int64_t row_bytes, int64_t rows_bound,
+                          hipStream_t stream) {
+  const int64_t blocks = (rows_bound + 3) / 4;
+  if (blocks > 0)
+    hipLaunchKernelGGL(permute_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint4*)x, row_token, total, (uint4*)x_perm, row_bytes / 16);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,109 @@
+"""Device-side driver of one MoE layer over the C ABI (marshalling only).
+
+``MoeLayer`` owns the workspace and output buffers for a fixed shape and calls
+either ``moe_layer_forward`` or the five stage entry points in order; every
+step runs in the HIP kernels of libmoe.so.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+WEIGHT_NAMES = ("w_g", "b_g", "w_noise", "w1", "w3", "w2", "b1", "b2", "ws1", "ws3", "ws2")
+
+
+def config_of(spec) -> L.MoeConfig:
+    """MoeConfig from any object with the layer-shape attributes (T, d, E, k, h,
+    act, dtype, capacity_factor, n_shared, ffn_bias, router_bias, router_noise)."""
+    return L.make_config(spec.T, spec.d, spec.E, spec.k, spec.h, act=spec.act, dtype=spec.dtype,
+                         capacity_factor=spec.capacity_factor, n_shared=spec.n_shared,
+                         ffn_bias=spec.ffn_bias, router_bias=spec.router_bias != "none",
+                         router_noise=spec.router_noise)
+
+
+class MoeLayer:
+    def __init__(self, spec, weights: dict, device="cuda"):
+        self.spec = spec
+        self.cfg = config_of(spec)
+        self.device = torch.device(device)
+        self.w = {n: weights.get(n) for n in WEIGHT_NAMES}
+        c = self.cfg
+        T, E, k, d, h, S = c.T, c.E, c.k, c.d, c.h, c.n_shared
+        self.capacity = L.moe_capacity(c)
+        self.rows_bound = L.moe_routed_rows_bound(c)
+        self.group_bound = min(T, self.capacity)
+        dev = self.device
+        self.ws = torch.empty(max(L.moe_workspace_bytes(c), 256), dtype=torch.uint8, device=dev)
+        out_dtype = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.out = {
+            "y": torch.empty((T, d), dtype=out_dtype, device=dev),
+            "logits": torch.empty((T, E), **f32),
+            "topk_idx": torch.empty((T, k), **i32),
+            "topk_gate": torch.empty((T, k), **f32),
+            "prob_sum": torch.empty((E,), **f32),
+            "counts": torch.empty((E,), **i32),
+            "offsets": torch.empty((E + 1,), **i32),
+            "dest": torch.empty((T, k), **i32),
+            "row_token": torch.empty((max(T * k, 1),), **i32),
+            "stats": torch.empty((2 * E + 2,), **f32),
+        }
+        rows = self.rows_bound + S * T
+        self.hidden = torch.empty((max(rows, 1), h), dtype=out_dtype, device=dev)
+        self.y_rows = torch.empty((max(rows, 1), d), **f32)
+
+    def forward(self, x, eps=None, logits_in=None, stream=None):
+        """moe_layer_forward with every auxiliary output captured."""
+        aux = {n: self.out[n] for n in ("logits", "topk_idx", "topk_gate", "prob_sum", "counts",
+                                        "offsets", "dest", "row_token", "stats")}
+        if logits_in is not None:
+            aux.pop("logits")
+        L.moe_layer_forward(self.cfg, self.w, x, eps, logits_in, self.out["y"], aux, self.ws,
+                            stream)
+        return self.out
+
+    def staged(self, x, eps=None, logits_in=None, stream=None, between=None):
+        """The same layer through the five stage entry points; ``between(name)``
+        is called after each stage is enqueued (for event timing)."""
+        c, o, w = self.cfg, self.out, self.w
+        T, d, S = c.T, c.d, c.n_shared
+        tick = between or (lambda name: None)
+        if logits_in is not None:
+            o["logits"].copy_(logits_in)
+            L.moe_route(c, None, None, None, None, None, o["logits"], o["topk_idx"],
+                        o["topk_gate"], o["prob_sum"], self.ws, stream)
+        else:
+            L.moe_route(c, x, w["w_g"], w["b_g"], w["w_noise"], eps, o["logits"], o["topk_idx"],
+                        o["topk_gate"], o["prob_sum"], self.ws, stream)
+        tick("route")
+        L.moe_dispatch(c, o["topk_idx"], None, o["counts"], o["offsets"], o["dest"],
+                       o["row_token"], None, self.ws, stream)
+        tick("dispatch")
+        R = self.rows_bound
+        L.moe_expert_up(c, c.E, x, o["row_token"], o["offsets"], R, self.group_bound, w["w1"],
+                        w["w3"], w["b1"], self.hidden, self.ws, stream)
+        tick("up")
+        L.moe_expert_down(c, c.E, self.hidden, o["offsets"], R, self.group_bound, w["w2"],
+                          w["b2"], self.y_rows, 0, self.ws, stream)
+        tick("down")
+        y_shared = None
+        if S:
+            y_shared = self.y_rows[R:R + S * T]
+            for s in range(S):
+                off = self._shared_offsets()
+                L.moe_expert_up(c, 1, x, None, off, T, T, w["ws1"][s], w["ws3"][s], None,
+                                self.hidden[R:], self.ws, stream)
+                L.moe_expert_down(c, 1, self.hidden[R:], off, T, T, w["ws2"][s], None,
+                                  y_shared[s * T:(s + 1) * T], 0, self.ws, stream)
+            tick("shared")
+        L.moe_combine(c, self.y_rows, o["dest"], o["topk_gate"], y_shared, o["counts"],
+                      o["prob_sum"], o["y"], o["stats"], stream)
+        tick("combine")
+        return o
+
+    def _shared_offsets(self):
+        if not hasattr(self, "_soff"):
+            self._soff = torch.tensor([0, self.cfg.T], dtype=torch.int32, device=self.device)
+        return self._soff
