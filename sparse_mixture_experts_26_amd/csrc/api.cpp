@@ -27,7 +27,9 @@ namespace {
 
 using namespace moe;
 
-constexpr int64_t kMaxElems = (int64_t)1 << 31;  // 32-bit element offsets in kernels
+// Kernels address operands with 31-bit byte offsets (buffer loads): every
+// operand must stay below 2^30 two-byte elements.
+constexpr int64_t kMaxElems = (int64_t)1 << 30;
 
 struct Cfg {
   int64_t T, d, E, k, h, S;

@@ -7,22 +7,28 @@
 //
 // Tile schedule: a one-block kernel turns the device-side group offsets into a
 // list of (group, first row, rows, first output row) entries of at most 256
-// rows, so no host synchronisation is needed; the GEMM grid is sized for the
-// worst case and surplus blocks exit at once.  Blocks are mapped to tiles so
-// that each of the 8 XCDs (which receive workgroups round-robin) walks a
-// contiguous range of tiles, and within it groups of 4 row-tiles sweep the
-// output columns together, so the A and B slabs of concurrent tiles are shared
-// through that XCD's L2.
+// rows, so no host synchronisation is needed.  The GEMM is persistent: one
+// block per CU walks the tiles; the hardware hands block P to XCD P % 8, and
+// XCD x owns an equal, contiguous range of the real tiles, in which groups of
+// 8 row tiles sweep the output columns together so the operand slabs of
+// concurrent tiles are shared through that XCD's L2.
 //
-// Block tile: 256 rows x 256 weight rows x 64 deep, 4 waves in a 2x2 grid, each
-// wave 128x128 as 4x4 tiles of v_mfma_f32_32x32x16_bf16 with float32 accumulators.
-// For the gated (SwiGLU) form the 256 weight rows are 128 rows of w1 and the
-// same 128 rows of w3, and every wave holds matching gate and up accumulators,
-// so silu(gate) * up is formed in registers.  Operands are staged through a
-// double-buffered LDS tile whose 16-byte chunks are XOR-swizzled per row, so
-// both the row-wise stores and the MFMA operand reads are bank-conflict-free.
-// Routed rows may be gathered from the token matrix through row_token, which
-// removes the separate permuted copy from the layer.
+// Block tile: 256 rows x 256 weight rows, 8 waves (2 per SIMD, so one wave's
+// stalls are covered by the other's MFMAs) in a 2x4 grid, each wave 128x64 as
+// 4x2 tiles of v_mfma_f32_32x32x16_bf16 with float32 accumulators.  For the
+// gated (SwiGLU) form the 256 weight rows are 128 rows of w1 and the same 128
+// rows of w3, and every wave holds matching gate and up tiles, so
+// silu(gate) * up is formed in registers.  Operands travel global -> LDS with
+// direct-to-LDS buffer loads (no register staging) through a ring of five
+// 32-deep stages (the whole 160 KiB of LDS), four in flight while one is
+// consumed; each wave waits only for its own loads of the next stage, then a
+// plain s_barrier publishes it.  The 16-byte chunks of every 64-byte LDS row
+// are XOR-swizzled by row so the MFMA operand reads are bank-conflict-free.
+// Routed rows are gathered from the token matrix through row_token, which
+// removes the separate permuted copy from the layer.  The epilogue stages each
+// wave's results through LDS and stores 16-byte row chunks.
+#include <algorithm>
+
 #include "launch.hpp"
 
 namespace moe {
@@ -31,24 +37,32 @@ namespace {
 
 constexpr int BM = 256;      // output rows per tile
 constexpr int BR = 256;      // weight rows per tile
-constexpr int BK = 64;       // reduction depth per stage
-constexpr int kThreads = 256;
-constexpr int kGroupM = 4;   // row-tiles that sweep the columns together
-constexpr int kTileBytes = BM * BK * 2;  // one operand tile, 32 KiB
+constexpr int BK = 32;       // reduction depth per stage
+constexpr int kThreads = 512;  // 8 waves: 2 per SIMD
+constexpr int kGroupM = 8;   // row-tiles that sweep the columns together
+constexpr int kTileBytes = BM * BK * 2;  // one operand tile, 16 KiB
+constexpr int kStageBytes = 2 * kTileBytes;  // A tile then B tile
 
 // Kept out of line so the fully unrolled epilogue stays small enough to keep
 // every accumulator in registers.
 __device__ __noinline__ float gelu_outlined(float a) { return gelu_f32(a); }
 
-__device__ __forceinline__ int lds_off(int row, int kc) {
-  return row * 128 + ((kc ^ ((row + (row >> 3)) & 7)) << 4);
+// Slot of 16-byte chunk kc (0..3) of a 64-byte LDS row: XOR with bits 1-3 of
+// the row, so 8 consecutive rows (one 128-byte bank sweep) and 16 consecutive
+// rows (two sweeps) both hit distinct banks for a fixed chunk.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+__device__ __forceinline__ int lds_off(int row, int kc) { return row * 64 + ((kc ^ swz(row)) << 4); }
+
+#define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt with vmcnt = N (gfx9 encoding: vmcnt bits [3:0] and [15:14]) and
+// the expcnt / lgkmcnt fields at their maxima, i.e. not waited on.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Workgroup P runs on XCD P % 8; give every XCD a contiguous range of tiles.
-__device__ __forceinline__ int xcd_remap(int P, int nb) {
-  const int x = P & 7, q = P >> 3, per = nb >> 3, rem = nb & 7;
-  return x < rem ? x * (per + 1) + q : rem * (per + 1) + (x - rem) * per + q;
-}
 
 // Entries beyond max_entries (possible only if a caller's rows_bound is below
 // offsets[G]) are not written, so the schedule never overruns its workspace.
@@ -98,160 +112,252 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* offsets
 }
 
 // ACT: moe_act_t for the up projection (2 = gated SwiGLU), -1 for none.
+//
+// Persistent: one block per CU walks tiles.  XCD x (the hardware hands block
+// P to XCD P % 8) owns the contiguous tile range [x*per, (x+1)*per) with
+// per = ceil(tiles / 8), read from the device-side schedule, so every XCD gets
+// an equal share of real tiles and neighbouring tiles share an L2.
 template <int ACT>
-__global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int n_tiles_n,
-                                                                int max_entries) {
+__global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int n_tiles_n) {
   constexpr bool GATED = ACT == 2;
-  __shared__ __attribute__((aligned(16))) char lds[4 * kTileBytes];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
-
-  // ---- which tile ----
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int per_group = kGroupM * n_tiles_n;
-  const int grp = L / per_group, rem = L - grp * per_group;
-  const int gsize = min(kGroupM, max_entries - grp * kGroupM);
-  const int e_idx = grp * kGroupM + rem % gsize;
-  const int n_idx = rem / gsize;
-  if (e_idx >= *p.n_entries) return;
-  const TileEntry te = p.entries[e_idx];
-  const bool routed = te.group < p.G;
-  const int gw = routed ? te.group : te.group - p.G;
+  __shared__ __attribute__((aligned(16))) char S0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) char S1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) char S2[kStageBytes];
+  __shared__ __attribute__((aligned(16))) char S3[kStageBytes];
+  __shared__ __attribute__((aligned(16))) char S4[kStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform per wave; say so, or LDS-destination and buffer
+  // resource operands that depend on it become per-lane (waterfall) loops
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid >> 2, wn = wid & 3;  // 2 x 4 waves: 128 rows x 64 weight rows each
+  const int lr = lane & 31, lh = lane >> 5;
+  const int n_entries = *p.n_entries;
+  const int tiles = n_entries * n_tiles_n;
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3, nq = (gridDim.x + 7 - xcd) >> 3;
+  const int per = (tiles + 7) >> 3;
+  const int t_end = min(tiles, (xcd + 1) * per);
   const int K = p.K, N = p.N;
   const int64_t wstride = (int64_t)N * K;
-  const uint16_t* W = static_cast<const uint16_t*>(routed ? p.w_main : p.w_shared) + gw * wstride;
-  const uint16_t* U = nullptr;
-  if (GATED) U = static_cast<const uint16_t*>(routed ? p.u_main : p.u_shared) + gw * wstride;
-  const uint16_t* A = static_cast<const uint16_t*>(routed ? p.a_main : p.a_shared);
-  const int n_out0 = n_idx * (GATED ? BR / 2 : BR);
-
-  // ---- global -> register staging assignment: rows r_ld + 32 i, chunk kc_ld ----
-  // Element offsets stay 32-bit (the host rejects operands of 2^31 elements or
-  // more); the weight rows of stage i are b_row0 + 32 (i mod 4) for the gated
-  // form (w1 for i < 4, w3 after) and b_row0 + 32 i otherwise.
-  const int kc_ld = tid & 7, r_ld = tid >> 3;
-  uint32_t a_off[8];
-  unsigned a_ok = 0, b_ok = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = r_ld + 32 * i;
-    const bool ok = row < te.rows;
-    int arow = p.a_from_c ? te.c_row0 + row : te.a_row0 + row;
-    if (ok && routed && p.gather && !p.a_from_c) arow = p.gather[arow];
-    a_off[i] = (uint32_t)(ok ? arow : 0) * (uint32_t)K + kc_ld * 8;
-    a_ok |= (unsigned)ok << i;
-    const int n = n_out0 + r_ld + 32 * (GATED ? (i & 3) : i);
-    b_ok |= (unsigned)(n < N) << i;
-  }
-  const uint32_t b_off0 = (uint32_t)min(n_out0 + r_ld, N - 1) * (uint32_t)K + kc_ld * 8;
-  const uint32_t b_step = 32u * (uint32_t)K;
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x16{};
-
-  const int lr = lane & 31, lh = lane >> 5;
-  int brow[4];
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni)
-    brow[ni] = GATED ? (ni < 2 ? wn * 64 + ni * 32 : 128 + wn * 64 + (ni - 2) * 32)
-                     : wn * 128 + ni * 32;
-  int st_off[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) st_off[i] = lds_off(r_ld + 32 * i, kc_ld);
-
   const int nk = (K + BK - 1) / BK;
-  u32x4 ra[8], rb[8];
-  const u32x4 z4 = {0u, 0u, 0u, 0u};
-#define MOE_LOAD_STAGE(k0)                                                                 \
-  {                                                                                        \
-    const bool k_ok = (k0) + kc_ld * 8 < K;                                                \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                        \
-      ra[i] = (((a_ok >> i) & 1u) && k_ok)                                                 \
-                  ? *reinterpret_cast<const u32x4*>(A + a_off[i] + (k0))                   \
-                  : z4;                                                                    \
-      const uint16_t* Bb = (GATED && i >= 4) ? U : W;                                      \
-      const uint32_t bo = b_off0 + (uint32_t)(GATED ? (i & 3) : i) * b_step + (k0);        \
-      rb[i] = (((b_ok >> i) & 1u) && k_ok) ? *reinterpret_cast<const u32x4*>(Bb + bo) : z4; \
-    }                                                                                      \
-  }
-#define MOE_STORE_STAGE(buf)                                                               \
-  {                                                                                        \
-    char* As_ = lds + (buf) * 2 * kTileBytes;                                              \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                        \
-      *reinterpret_cast<u32x4*>(As_ + st_off[i]) = ra[i];                                  \
-      *reinterpret_cast<u32x4*>(As_ + kTileBytes + st_off[i]) = rb[i];                     \
-    }                                                                                      \
-  }
+  constexpr uint32_t kOOB = 0x80000000u;
 
-  MOE_LOAD_STAGE(0)
-  MOE_STORE_STAGE(0)
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) MOE_LOAD_STAGE((kt + 1) * BK)
-    const char* As = lds + (kt & 1) * 2 * kTileBytes;
-    const char* Bs = As + kTileBytes;
+  // LDS read offsets (fragment rows are 32-aligned, so the swizzle depends on lr)
+  int rd_a[2], rd_b[2][2];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int kc = kk * 2 + lh;
-      bf16x8 af[4], bv[4];
+  for (int kk = 0; kk < 2; ++kk) {
+    rd_a[kk] = lds_off(wm * 128 + lr, kk * 2 + lh);
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        af[mi] = *reinterpret_cast<const bf16x8*>(As + lds_off(wm * 128 + mi * 32 + lr, kc));
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-        bv[ni] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(brow[ni] + lr, kc));
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bv[ni], acc[mi][ni], 0, 0, 0);
+    for (int ni = 0; ni < 2; ++ni) {
+      const int br = GATED ? ni * 128 + wn * 32 : wn * 64 + ni * 32;
+      rd_b[kk][ni] = kTileBytes + lds_off(br + lr, kk * 2 + lh);
     }
-    if (more) MOE_STORE_STAGE((kt + 1) & 1)
-    __syncthreads();
   }
-#undef MOE_LOAD_STAGE
-#undef MOE_STORE_STAGE
 
-  // ---- epilogue: 32x32 result layout, lane holds column lane%32,
-  //      rows 8*(v/4) + 4*(lane/32) + v%4 for v = 0..15 ----
-  const float* bias = routed ? p.bias_main : p.bias_shared;
-  constexpr int NJ = GATED ? 2 : 4;  // output column blocks per wave
-  int col[NJ];
-  float bcol[NJ];
+  for (int t = xcd * per + q; t < t_end; t += nq) {
+    // groups of 8 row tiles sweep the columns together
+    const int per_group = kGroupM * n_tiles_n;
+    const int grp = t / per_group, rem = t - grp * per_group;
+    const int gsize = min(kGroupM, n_entries - grp * kGroupM);
+    const int e_idx = grp * kGroupM + rem % gsize;
+    const int n_idx = rem / gsize;
+    const TileEntry te = p.entries[e_idx];
+    const bool routed = te.group < p.G;
+    const int gw = routed ? te.group : te.group - p.G;
+    const uint16_t* W = static_cast<const uint16_t*>(routed ? p.w_main : p.w_shared) + gw * wstride;
+    const uint16_t* U = W;
+    if (GATED) U = static_cast<const uint16_t*>(routed ? p.u_main : p.u_shared) + gw * wstride;
+    const uint16_t* A = static_cast<const uint16_t*>(routed ? p.a_main : p.a_shared);
+    const int n_out0 = n_idx * (GATED ? BR / 2 : BR);
+
+    // ---- direct-to-LDS loads: a stage is 16 A and 16 B loads of 1 KiB (16 rows x
+    // 64 bytes); wave w issues A blocks 2w, 2w+1 and B blocks 2w, 2w+1.  Lane i
+    // fills row i/4, slot i%4 of its block, so it fetches the chunk the swizzle
+    // stores there.  Buffer resources return zeros past their end: rows past
+    // the tile, weight rows past N and chunks past K need no branches.
+    const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(A), (short)0, 0x7fffffff, 0x00020000);
+    const uint16_t* Bsrc = (GATED && wid >= 4) ? U : W;  // B rows 128.. are w3's
+    const __amdgpu_buffer_rsrc_t b_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(Bsrc), (short)0, (int)(wstride * 2), 0x00020000);
+    uint32_t a_off[2], b_off[2];
+    int l_kc[2];
 #pragma unroll
-  for (int nj = 0; nj < NJ; ++nj) {
-    col[nj] = n_out0 + (GATED ? wn * 64 : wn * 128) + nj * 32 + lr;
-    bcol[nj] = (bias && col[nj] < N) ? bias[(int64_t)gw * N + col[nj]] : 0.f;
+    for (int j = 0; j < 2; ++j) {
+      const int row = (wid * 2 + j) * 16 + (lane >> 2);  // tile row 0..255
+      const int kc = (lane & 3) ^ swz(row);
+      l_kc[j] = kc;
+      const bool ok = row < te.rows;
+      int arow = p.a_from_c ? te.c_row0 + row : te.a_row0 + row;
+      if (ok && routed && p.gather && !p.a_from_c) arow = p.gather[arow];
+      a_off[j] = ok ? ((uint32_t)arow * (uint32_t)K + kc * 8) * 2u : kOOB;
+      const int n = n_out0 + (GATED ? (row & 127) : row);
+      b_off[j] = n < N ? ((uint32_t)n * (uint32_t)K + kc * 8) * 2u : kOOB;
+    }
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x16{};
+
+    auto issue = [&](char* Sx, int kt) __attribute__((always_inline)) {
+      const int k0 = kt * BK;  // stages past the end (kt >= nk) read zeros
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t kadd = (k0 + l_kc[j] * 8 < K) ? (uint32_t)k0 * 2u : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, MOE_LDS(Sx + (wid * 2 + j) * 1024), 16,
+                                                 a_off[j] + kadd, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, MOE_LDS(Sx + kTileBytes + (wid * 2 + j) * 1024),
+                                                 16, b_off[j] + kadd, 0, 0, 0);
+      }
+    };
+    // Fragments of one 16-deep half of a stage: 4 A and 2 B operands.
+    struct Frags { bf16x8 a[4], b[2]; };
+    auto read = [&](Frags& f, const char* Sx, int kk) __attribute__((always_inline)) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        f.a[mi] = *reinterpret_cast<const bf16x8*>(Sx + rd_a[kk] + mi * 32 * 64);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) f.b[ni] = *reinterpret_cast<const bf16x8*>(Sx + rd_b[kk][ni]);
+    };
+    auto mfma = [&](const Frags& f) __attribute__((always_inline)) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[ni], acc[mi][ni], 0, 0, 0);
+    };
+    auto barrier = [&]() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
+
+    // Pipeline (stage = 32 deep in two 16-deep halves; ring of five LDS
+    // stages, the whole 160 KiB): at the top of step kt stage kt is published
+    // and the first half of its fragments is in registers.  The step waits for
+    // this wave's loads of stage kt+1 (the 8 loads of stages kt+2 and kt+3 may
+    // stay in flight); the barrier publishes stage kt+1 and frees the slot of
+    // stage kt-1, which is refilled with stage kt+4.  The second half of stage
+    // kt and the first half of stage kt+1 are read while the MFMAs run.  Every
+    // step issues its 4 loads, past the end too (they read zeros), so the wait
+    // counts are fixed.  Four stages in flight cover the load latency of the
+    // streamed operands.
+    //
+    // Instruction order inside a step, fixed with sched_group_barrier:
+    //   MFMAs 1-8  on f0: an LDS read into f1 after MFMA 1-6, loads after 2 and 6
+    //   MFMAs 9-16 on f1: an LDS read into f0 after MFMA 9-14, loads after 10 and 14
+#define MOE_PATTERN()                                                    \
+  {                                                                      \
+    _Pragma("unroll") for (int i = 0; i < 16; ++i) {                     \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 \
+      if ((i & 7) < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); \
+      if ((i & 3) == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); \
+    }                                                                    \
   }
-  uint16_t* __restrict__ out16 = static_cast<uint16_t*>(p.out);
-  float* __restrict__ out32 = static_cast<float*>(p.out);
+#define MOE_STEP(Scur, Snext, Sfill, kt) \
+  {                                      \
+    wait_vmcnt<8>();                     \
+    barrier();                           \
+    issue(Sfill, (kt) + 4);              \
+    read(f1, Scur, 1);                   \
+    mfma(f0);                            \
+    read(f0, Snext, 0);                  \
+    mfma(f1);                            \
+    MOE_PATTERN()                        \
+  }
+    Frags f0, f1;
+    barrier();  // the previous tile's last reads are done
+    issue(S0, 0);
+    issue(S1, 1);
+    issue(S2, 2);
+    issue(S3, 3);
+    wait_vmcnt<12>();
+    barrier();
+    read(f0, S0, 0);
+    int kt = 0;
+    for (; kt + 5 <= nk; kt += 5) {
+      MOE_STEP(S0, S1, S4, kt)
+      MOE_STEP(S1, S2, S0, kt + 1)
+      MOE_STEP(S2, S3, S1, kt + 2)
+      MOE_STEP(S3, S4, S2, kt + 3)
+      MOE_STEP(S4, S0, S3, kt + 4)
+    }
+    if (kt < nk) MOE_STEP(S0, S1, S4, kt)
+    if (kt + 1 < nk) MOE_STEP(S1, S2, S0, kt + 1)
+    if (kt + 2 < nk) MOE_STEP(S2, S3, S1, kt + 2)
+    if (kt + 3 < nk) MOE_STEP(S3, S4, S2, kt + 3)
+#undef MOE_STEP
+#undef MOE_PATTERN
+    // loads issued past the end (zeros) land before the LDS is reused or freed
+    wait_vmcnt<0>();
+
+    // ---- epilogue.  32x32 result layout: lane holds column lane%32, rows
+    // 8*(v/4) + 4*(lane/32) + v%4 for v = 0..15.  Each wave stages its block
+    // through a private LDS region (rows padded by 16 bytes so the two lane
+    // halves, 4 rows apart, hit different banks) and writes it back as 16-byte
+    // row chunks, instead of 2-byte scattered stores.  A wave's LDS operations
+    // complete in order, so only the barrier that frees the ring is needed.
+    barrier();
+    const float* bias = routed ? p.bias_main : p.bias_shared;
+    // Up projections (ACT >= 0) write the bf16 hidden layer; the down projection
+    // writes float32 (the host only selects this kernel for bf16 layers).
+    constexpr bool OUT_BF16 = ACT >= 0;
+    constexpr int NJ = GATED ? 1 : 2;            // 32-column blocks per wave
+    constexpr int COLS = NJ * 32;                // columns per wave
+    constexpr int esz = OUT_BF16 ? 2 : 4;
+    constexpr int row_bytes = COLS * esz + 16;
+    // Each wave owns half of one 32 KiB stage array (arrays need not be
+    // adjacent); rows per pass keep the block within those 16 KiB.
+    constexpr int rows_pass = (128 * row_bytes <= 16384) ? 128 : (64 * row_bytes <= 16384 ? 64 : 32);
+    static_assert(rows_pass * row_bytes <= 16384, "staging block exceeds the wave's region");
+    char* const stage_of_wave = wid < 2 ? S0 : wid < 4 ? S1 : wid < 6 ? S2 : S3;
+    char* const region = stage_of_wave + (wid & 1) * 16384;
+    const int col0 = n_out0 + (GATED ? wn * 32 : wn * 64);  // first column of the wave block
+    float bcol[NJ];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
+    for (int nj = 0; nj < NJ; ++nj) {
+      const int c = col0 + nj * 32 + lr;
+      bcol[nj] = (bias && c < N) ? bias[(int64_t)gw * N + c] : 0.f;
+    }
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = wm * 128 + mi * 32 + (v >> 2) * 8 + lh * 4 + (v & 3);
-      const bool row_ok = row < te.rows;
-      const int64_t orow = (int64_t)(te.c_row0 + row) * N;
+    for (int pass = 0; pass < 128 / rows_pass; ++pass) {
+      // 1. activation, then registers -> LDS
 #pragma unroll
-      for (int nj = 0; nj < NJ; ++nj) {
-        if (!row_ok || col[nj] >= N) continue;
-        float o;
-        if (GATED) {
-          o = silu_f32(acc[mi][nj][v] + bcol[nj]) * acc[mi][nj + 2][v];
-        } else {
-          o = acc[mi][nj][v] + bcol[nj];
-          if (ACT == 0) o = gelu_outlined(o);
-          if (ACT == 1) o = fmaxf(o, 0.f);
+      for (int mi = 0; mi < 4; ++mi) {
+        if ((mi * 32) / rows_pass != pass) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = (mi * 32 + (v >> 2) * 8 + lh * 4 + (v & 3)) % rows_pass;
+#pragma unroll
+          for (int nj = 0; nj < NJ; ++nj) {
+            float o;
+            if (GATED) {
+              o = silu_f32(acc[mi][0][v] + bcol[0]) * acc[mi][1][v];
+            } else {
+              o = acc[mi][nj][v] + bcol[nj];
+              if (ACT == 0) o = gelu_outlined(o);
+              if (ACT == 1) o = fmaxf(o, 0.f);
+            }
+            char* dst = region + r * row_bytes + (nj * 32 + lr) * esz;
+            if (OUT_BF16) *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16(o);
+            else *reinterpret_cast<float*>(dst) = o;
+          }
         }
-        if (p.out_bf16) {
-          out16[orow + col[nj]] = f32_to_bf16(o);
+      }
+      // 2. LDS -> global in 16-byte chunks (row-contiguous across lanes)
+      constexpr int chunks_row = COLS * esz / 16;
+      constexpr int chunks = rows_pass * chunks_row;
+      for (int c = lane; c < chunks; c += 64) {
+        const int r = c / chunks_row, ch = c - r * chunks_row;
+        const int row = wm * 128 + pass * rows_pass + r;
+        const int colc = col0 + ch * (16 / esz);
+        if (row >= te.rows || colc >= N) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(region + r * row_bytes + ch * 16);
+        const int64_t off = (int64_t)(te.c_row0 + row) * N + colc;
+        if (OUT_BF16) {
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + off) = v;
         } else {
-          float* dst = out32 + orow + col[nj];
-          *dst = p.accumulate ? *dst + o : o;
+          f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + off);
+          f32x4 val = __builtin_bit_cast(f32x4, v);
+          if (p.accumulate) val += *dst;
+          *dst = val;
         }
       }
     }
@@ -264,21 +370,35 @@ int64_t ffn_max_entries(int64_t rows_bound, int G, int S, int T) {
   return (rows_bound + BM - 1) / BM + G + (int64_t)S * ((T + BM - 1) / BM);
 }
 
+int device_cus() {
+  static int cus = 0;  // CUs of the current device, asked once
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
 hipError_t launch_ffn_tiled(const FfnParams& p, hipStream_t stream) {
   const int64_t max_entries = ffn_max_entries(p.rows_bound, p.G, p.S, p.T);
   const bool gated = p.act == 2;
   const int cols = gated ? BR / 2 : BR;
   const int n_tiles_n = (p.N + cols - 1) / cols;
-  const int64_t blocks = max_entries * n_tiles_n;
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, stream, p.offsets, p.G, p.S,
                      p.T, p.rows_bound, (int)max_entries, p.entries, p.n_entries);
-  if (blocks > 0) {
-    const dim3 grid((unsigned)blocks), block(kThreads);
+  // one resident block per CU (128 KiB of LDS each), never more blocks than tiles
+  const int64_t grid = std::min<int64_t>(device_cus(), max_entries * n_tiles_n);
+  if (grid > 0) {
+    const dim3 g((unsigned)grid), block(kThreads);
     switch (p.act) {
-      case 2: hipLaunchKernelGGL(ffn_tiled_kernel<2>, grid, block, 0, stream, p, n_tiles_n, (int)max_entries); break;
-      case 1: hipLaunchKernelGGL(ffn_tiled_kernel<1>, grid, block, 0, stream, p, n_tiles_n, (int)max_entries); break;
-      case 0: hipLaunchKernelGGL(ffn_tiled_kernel<0>, grid, block, 0, stream, p, n_tiles_n, (int)max_entries); break;
-      default: hipLaunchKernelGGL(ffn_tiled_kernel<-1>, grid, block, 0, stream, p, n_tiles_n, (int)max_entries); break;
+      case 2: hipLaunchKernelGGL(ffn_tiled_kernel<2>, g, block, 0, stream, p, n_tiles_n); break;
+      case 1: hipLaunchKernelGGL(ffn_tiled_kernel<1>, g, block, 0, stream, p, n_tiles_n); break;
+      case 0: hipLaunchKernelGGL(ffn_tiled_kernel<0>, g, block, 0, stream, p, n_tiles_n); break;
+      default: hipLaunchKernelGGL(ffn_tiled_kernel<-1>, g, block, 0, stream, p, n_tiles_n); break;
     }
   }
   return hipGetLastError();
