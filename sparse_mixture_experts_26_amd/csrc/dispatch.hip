@@ -15,6 +15,8 @@
 //   2. scan:   one block turns the chunk histograms into per-chunk bases (chunk
 //              order), counts, kept = min(counts, C) and the offsets.
 //   3. assign: rank = base + local rank; kept iff rank < C; dest and row_token.
+// A batch of at most one chunk (decode-sized) runs all three steps in a single
+// block of 16 waves, one slice per wave, with the tables kept in LDS.
 // Every step is ordered, so the integer outputs are exact and deterministic.
 #include "launch.hpp"
 
@@ -24,6 +26,78 @@ namespace {
 
 constexpr int kSlices = kDispatchChunk / 64;  // 16 slices of 64 per chunk
 constexpr int kInvalid = 511;                 // expert id that matches no expert
+
+// Stable rank of lane's expert among the 64 lanes of its slice; `count` gets
+// the number of lanes holding the same expert.
+__device__ __forceinline__ int slice_rank(int e, int lane, int& count) {
+  uint64_t peers = ~0ull;
+#pragma unroll
+  for (int b = 0; b < 9; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    peers &= bit ? bal : ~bal;
+  }
+  count = __popcll(peers);
+  return __popcll(peers & ((1ull << lane) - 1ull));
+}
+
+// n <= kDispatchChunk: rank, scan and assign in one block; wave w = slice w.
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchParams p) {
+  __shared__ int hist[kSlices][256];
+  __shared__ int sscan[256];
+  __shared__ int soff[256];
+  const int lane = threadIdx.x & 63, s = threadIdx.x >> 6, x = threadIdx.x;
+  for (int i = x; i < kSlices * 256; i += 1024) (&hist[0][0])[i] = 0;
+  __syncthreads();
+  const int i = s * 64 + lane;
+  int e = kInvalid;
+  if (i < p.n) {
+    e = p.idx[i];
+    if (e < 0 || e >= p.E) e = kInvalid;
+  }
+  int cnt;
+  const int r = slice_rank(e, lane, cnt);
+  if (e != kInvalid && r == 0) hist[s][e] = cnt;
+  __syncthreads();
+  int kept = 0;
+  if (x < 256) {
+    if (x < p.E) {
+      int run = 0;
+      for (int q = 0; q < kSlices; ++q) {
+        const int c = hist[q][x];
+        hist[q][x] = run;
+        run += c;
+      }
+      p.counts[x] = run;
+      kept = run < p.C ? run : p.C;
+    }
+    sscan[x] = kept;
+  }
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {  // Hillis-Steele inclusive scan
+    const int v = (x < 256 && x >= o) ? sscan[x - o] : 0;
+    __syncthreads();
+    if (x < 256) sscan[x] += v;
+    __syncthreads();
+  }
+  if (x < p.E) {
+    soff[x] = sscan[x] - kept;
+    p.offsets[x] = sscan[x] - kept;
+    if (x == p.E - 1) p.offsets[p.E] = sscan[x];
+  }
+  __syncthreads();
+  if (i < p.n) {
+    int d = -1;
+    if (e != kInvalid) {
+      const int rank = hist[s][e] + r;
+      if (rank < p.C) {
+        d = soff[e] + rank;
+        p.row_token[d] = i / p.k;
+      }
+    }
+    p.dest[i] = d;
+  }
+}
 
 __global__ __launch_bounds__(256) void dispatch_rank_kernel(DispatchParams p) {
   __shared__ int hist[kSlices][256];
@@ -41,15 +115,9 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(DispatchParams p) {
       e = p.idx[i];
       if (e < 0 || e >= p.E) e = kInvalid;
     }
-    uint64_t peers = ~0ull;
-#pragma unroll
-    for (int b = 0; b < 9; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bal = __ballot(bit);
-      peers &= bit ? bal : ~bal;
-    }
-    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
-    if (e != kInvalid && rank == 0) hist[s][e] = __popcll(peers);
+    int cnt;
+    const int rank = slice_rank(e, lane, cnt);
+    if (e != kInvalid && rank == 0) hist[s][e] = cnt;
     my_e[r] = e;
     my_r[r] = rank;
   }
@@ -137,6 +205,10 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* x, const int3
 
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t stream) {
   const int chunks = dispatch_chunks(p.n);
+  if (chunks == 1) {
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, stream, p);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(dispatch_rank_kernel, dim3(chunks), dim3(256), 0, stream, p);
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, stream, p, chunks);
   hipLaunchKernelGGL(dispatch_assign_kernel, dim3(chunks), dim3(256), 0, stream, p);

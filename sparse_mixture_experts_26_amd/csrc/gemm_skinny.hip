@@ -5,14 +5,20 @@
 // expert's weights ("Mixture-of-Experts & Sparse Model Scaling", Computational
 // Considerations: MoE layers are more memory-bound than dense ones of equal
 // active size), so the kernel is built to keep HBM busy rather than to reuse
-// operands: every block owns one expert and a 64-column slab of its weight
-// rows, reads that slab exactly once with 16-byte loads, and splits the
-// reduction axis over its 4 waves so each wave keeps many independent loads in
-// flight.  The expert's <= 32 operand rows ride along as the A operand of
-// v_mfma_f32_16x16x32_bf16 (two 16-row fragments; the second is skipped when the
-// expert holds 16 rows or fewer).  The 4 partial products are summed in LDS in
-// wave order (deterministic) and the activation is applied there.  Experts
-// that received no rows read no weights at all.
+// operands.  Work is cut into units of (expert, 32-column slab of its weight
+// rows); the grid is two resident blocks per CU and each block walks an equal,
+// contiguous run of units, so neighbouring slabs of one expert stream through
+// the same CU and no partial last wave of blocks is left.  Each unit's weight
+// rows are read exactly once with 16-byte buffer loads; the 4 waves of a block
+// split the reduction axis, and each wave keeps the next 64-deep step's loads
+// in flight (register double buffer) while it multiplies the current one.  The
+// expert's <= 32 operand rows ride along as the A operand of
+// v_mfma_f32_16x16x32_bf16 (two 16-row fragments; the second reads zeros when
+// the expert holds 16 rows or fewer).  The 4 partial products are summed in
+// LDS in wave order (deterministic) and the activation is applied there.
+// Experts that received no rows read no weights at all.
+#include <algorithm>
+
 #include "launch.hpp"
 
 namespace moe {
@@ -20,161 +26,242 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int NF = 4;  // 16-column fragments per block: 64 output columns
+constexpr int NF = 2;      // 16-column fragments per unit: 32 output columns
+constexpr int kCols = NF * 16;
+constexpr int UNR = 2;     // 32-deep k-steps per pipeline stage
+constexpr int kStep = 32 * UNR;  // depth of one pipeline stage
+constexpr uint32_t kOOB = 0x80000000u;
+#ifndef MOE_SKINNY_BLOCKS_PER_CU
+#define MOE_SKINNY_BLOCKS_PER_CU 2
+#endif
+constexpr int kBlocksPerCU = MOE_SKINNY_BLOCKS_PER_CU;
+
+// Where a unit's operands live: the load side runs one pipeline step ahead of
+// the multiply side, so each keeps its own copy across unit boundaries.
+struct UnitDesc {
+  int g, rows, c_row0;
+  uint32_t a_off[2];
+  uint32_t b_off[NF];
+  const uint16_t* W;
+  const uint16_t* U;
+  const void* A;
+};
 
 template <int ACT>
-__global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n_slabs) {
+__global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n_slabs,
+                                                              int n_units) {
   constexpr bool GATED = ACT == 2;
   constexpr int NB = GATED ? 2 : 1;           // weight sets (w1 and w3 when gated)
   constexpr int NFRAG = 2 * NF * NB;          // (row fragment, column fragment, set)
-  constexpr int UNR = GATED ? 2 : 4;          // k-steps of 32 loaded ahead
   __shared__ float red[4][NFRAG][4][64];
 
-  const int g = blockIdx.x / n_slabs, slab = blockIdx.x - g * n_slabs;
-  const bool routed = g < p.G;
-  int rows, a_row0, c_row0;
-  if (routed) {
-    a_row0 = p.offsets[g];
-    rows = p.offsets[g + 1] - a_row0;
-    c_row0 = a_row0;
-  } else {
-    a_row0 = 0;
-    rows = p.T;
-    c_row0 = (int)(p.rows_bound + (int64_t)(g - p.G) * p.T);
-  }
-  rows = min(rows, 32);
-  if (rows <= 0) return;
-  const bool two = rows > 16;
-  const int gw = routed ? g : g - p.G;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int K = p.K, N = p.N;
   const int64_t wstride = (int64_t)N * K;
-  const uint16_t* W = static_cast<const uint16_t*>(routed ? p.w_main : p.w_shared) + gw * wstride;
-  const uint16_t* U = W;
-  if (GATED) U = static_cast<const uint16_t*>(routed ? p.u_main : p.u_shared) + gw * wstride;
-  const uint16_t* A = static_cast<const uint16_t*>(routed ? p.a_main : p.a_shared);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-
-  uint32_t a_off[2];
-  bool a_ok[2];
-#pragma unroll
-  for (int mf = 0; mf < 2; ++mf) {
-    const int r = mf * 16 + (lane & 15);
-    a_ok[mf] = r < rows;
-    int arow = p.a_from_c ? c_row0 + r : a_row0 + r;
-    if (a_ok[mf] && routed && p.gather && !p.a_from_c) arow = p.gather[arow];
-    a_off[mf] = (uint32_t)(a_ok[mf] ? arow : 0) * (uint32_t)K;
-  }
-  uint32_t b_off[NF];
-  bool b_ok[NF];
-#pragma unroll
-  for (int nf = 0; nf < NF; ++nf) {
-    const int n = slab * 64 + nf * 16 + (lane & 15);
-    b_ok[nf] = n < N;
-    b_off[nf] = (uint32_t)(b_ok[nf] ? n : 0) * (uint32_t)K;
-  }
-
-  const int kch = (K + 31) / 32, per = (kch + 3) / 4;
-  const int kb = min(K, w * per * 32), ke = min(K, (w + 1) * per * 32);
+  const int u_begin = (int)((int64_t)blockIdx.x * n_units / gridDim.x);
+  const int u_end = (int)((int64_t)(blockIdx.x + 1) * n_units / gridDim.x);
+  // this wave's contiguous reduction range; every wave runs `per` steps
+  // per unit (steps past its range read zeros), so the waves stay in step
+  const int kch = (K + kStep - 1) / kStep, per = (kch + 3) / 4;
+  const int kb = min(K, w * per * kStep), ke = min(K, (w + 1) * per * kStep);
   const int kl = (lane >> 4) * 8;
-  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  const int total = (u_end - u_begin) * per;
+
+  // Unit descriptor.  The expert's row range and gathered rows are re-read only
+  // when the expert changes (consecutive units are slabs of one expert).
+  int cached_g = -1, cached_rows = 0, cached_r0 = 0;
+  uint32_t cached_a[2] = {kOOB, kOOB};
+  auto describe = [&](int u, UnitDesc& d) __attribute__((always_inline)) {
+    const int g = u / n_slabs, slab = u - g * n_slabs;
+    const bool routed = g < p.G;
+    if (g != cached_g) {
+      int rows, a_row0;
+      if (routed) {
+        a_row0 = p.offsets[g];
+        rows = p.offsets[g + 1] - a_row0;
+        cached_r0 = a_row0;
+      } else {
+        a_row0 = 0;
+        rows = p.T;
+        cached_r0 = (int)(p.rows_bound + (int64_t)(g - p.G) * p.T);
+      }
+      rows = min(rows, 32);
+#pragma unroll
+      for (int mf = 0; mf < 2; ++mf) {
+        const int r = mf * 16 + (lane & 15);
+        const bool ok = r < rows;
+        int arow = p.a_from_c ? cached_r0 + r : a_row0 + r;
+        if (ok && routed && p.gather && !p.a_from_c) arow = p.gather[arow];
+        cached_a[mf] = ok ? ((uint32_t)arow * (uint32_t)K + kl) * 2u : kOOB;
+      }
+      cached_g = g;
+      cached_rows = rows;
+    }
+    const int gw = routed ? g : g - p.G;
+    d.g = g;
+    d.rows = cached_rows;
+    d.c_row0 = cached_r0;
+    d.a_off[0] = cached_a[0];
+    d.a_off[1] = cached_a[1];
+    d.W = static_cast<const uint16_t*>(routed ? p.w_main : p.w_shared) + gw * wstride;
+    d.U = GATED ? static_cast<const uint16_t*>(routed ? p.u_main : p.u_shared) + gw * wstride : d.W;
+    d.A = routed ? p.a_main : p.a_shared;
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf) {
+      const int n = slab * kCols + nf * 16 + (lane & 15);
+      // an expert with no rows reads no weights: every offset is out of range
+      d.b_off[nf] = (n < N && cached_rows > 0) ? ((uint32_t)n * (uint32_t)K + kl) * 2u : kOOB;
+    }
+  };
 
   f32x4 acc[2][NF][NB];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int mf = 0; mf < 2; ++mf)
-#pragma unroll
-    for (int nf = 0; nf < NF; ++nf)
-#pragma unroll
-      for (int s = 0; s < NB; ++s) acc[mf][nf][s] = f32x4{};
-
-  for (int k0 = kb; k0 < ke; k0 += 32 * UNR) {
-    u32x4 av[UNR][2], bv[UNR][NF][NB];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int kk = k0 + u * 32 + kl;
-      const bool k_ok = kk < ke;
-#pragma unroll
-      for (int mf = 0; mf < 2; ++mf)
-        av[u][mf] = (k_ok && a_ok[mf] && (mf == 0 || two))
-                        ? *reinterpret_cast<const u32x4*>(A + a_off[mf] + kk)
-                        : z4;
+    for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
       for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
-        for (int s = 0; s < NB; ++s)
-          bv[u][nf][s] = (k_ok && b_ok[nf])
-                             ? *reinterpret_cast<const u32x4*>((s ? U : W) + b_off[nf] + kk)
-                             : z4;
-    }
+        for (int s = 0; s < NB; ++s) acc[mf][nf][s] = f32x4{};
+  };
+
+  struct Stage { u32x4 a[UNR][2], b[UNR][NF][NB]; };
+  // loads of step `st` (0..per-1) of the unit described by d
+  auto load = [&](Stage& sg, const UnitDesc& d, int st) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(d.A), (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(d.W), (short)0, (int)(wstride * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t u_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(d.U), (short)0, (int)(wstride * 2), 0x00020000);
+    const int k0 = kb + st * kStep;
 #pragma unroll
-    for (int u = 0; u < UNR; ++u)
+    for (int v = 0; v < UNR; ++v) {
+      const int kk = k0 + v * 32 + kl;
+      const uint32_t kadd = kk < ke ? (uint32_t)(k0 + v * 32) * 2u : kOOB;
+#pragma unroll
+      for (int mf = 0; mf < 2; ++mf)
+        sg.a[v][mf] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, d.a_off[mf] + kadd, 0, 0);
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf) {
+        sg.b[v][nf][0] = __builtin_amdgcn_raw_buffer_load_b128(w_rs, d.b_off[nf] + kadd, 0, 0);
+        if (GATED) sg.b[v][nf][NB - 1] = __builtin_amdgcn_raw_buffer_load_b128(u_rs, d.b_off[nf] + kadd, 0, 0);
+      }
+    }
+  };
+  // Both row fragments are always multiplied: the second reads zeros when the
+  // expert holds 16 rows or fewer, and branch-free code keeps the compiler's
+  // wait counts exact (MFMA time is negligible here).
+  auto compute = [&](const Stage& sg) __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < UNR; ++v)
 #pragma unroll
       for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
         for (int s = 0; s < NB; ++s) {
-          const bf16x8 b = __builtin_bit_cast(bf16x8, bv[u][nf][s]);
-          acc[0][nf][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, av[u][0]), b, acc[0][nf][s], 0, 0, 0);
-          if (two)
-            acc[1][nf][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, av[u][1]), b, acc[1][nf][s], 0, 0, 0);
+          const bf16x8 b = __builtin_bit_cast(bf16x8, sg.b[v][nf][s]);
+#pragma unroll
+          for (int mf = 0; mf < 2; ++mf)
+            acc[mf][nf][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, sg.a[v][mf]), b, acc[mf][nf][s], 0, 0, 0);
         }
-  }
-
-  // 16x16 result layout: lane holds column lane%16, rows 4*(lane/16) + i.
+  };
+  // sum the 4 waves' partial products in wave order, activation, store
+  auto finish = [&](const UnitDesc& d, int u) __attribute__((always_inline)) {
 #pragma unroll
-  for (int mf = 0; mf < 2; ++mf)
+    for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
-    for (int nf = 0; nf < NF; ++nf)
+      for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
-      for (int s = 0; s < NB; ++s)
+        for (int s = 0; s < NB; ++s)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[w][(mf * NF + nf) * NB + s][i][lane] = acc[mf][nf][s][i];
-  __syncthreads();
-
-  const float* bias = routed ? p.bias_main : p.bias_shared;
-  for (int o = threadIdx.x; o < 2 * NF * 256; o += kThreads) {
-    const int mf = o / (NF * 256), rem = o - mf * NF * 256;
-    const int nf = rem >> 8, i = (rem >> 6) & 3, l = rem & 63;
-    const int row = mf * 16 + (l >> 4) * 4 + i;
-    const int col = slab * 64 + nf * 16 + (l & 15);
-    if (row >= rows || col >= N) continue;
-    const int f0 = (mf * NF + nf) * NB;
-    float a = ((red[0][f0][i][l] + red[1][f0][i][l]) + red[2][f0][i][l]) + red[3][f0][i][l];
-    if (bias) a += bias[(int64_t)gw * N + col];
-    float out;
-    if (GATED) {
-      const float u = ((red[0][f0 + 1][i][l] + red[1][f0 + 1][i][l]) + red[2][f0 + 1][i][l]) +
-                      red[3][f0 + 1][i][l];
-      out = silu_f32(a) * u;
-    } else if (ACT == 0) {
-      out = gelu_f32(a);
-    } else if (ACT == 1) {
-      out = fmaxf(a, 0.f);
-    } else {
-      out = a;
+          for (int i = 0; i < 4; ++i) red[w][(mf * NF + nf) * NB + s][i][lane] = acc[mf][nf][s][i];
+    __syncthreads();
+    const bool routed = d.g < p.G;
+    const int gw = routed ? d.g : d.g - p.G;
+    const int slab = u - d.g * n_slabs;
+    const float* bias = routed ? p.bias_main : p.bias_shared;
+    for (int o = threadIdx.x; o < 2 * NF * 256; o += kThreads) {
+      const int mf = o / (NF * 256), rem = o - mf * NF * 256;
+      const int nf = rem >> 8, i = (rem >> 6) & 3, l = rem & 63;
+      const int row = mf * 16 + (l >> 4) * 4 + i;
+      const int col = slab * kCols + nf * 16 + (l & 15);
+      if (row >= d.rows || col >= N) continue;
+      const int f0 = (mf * NF + nf) * NB;
+      float a = ((red[0][f0][i][l] + red[1][f0][i][l]) + red[2][f0][i][l]) + red[3][f0][i][l];
+      if (bias) a += bias[(int64_t)gw * N + col];
+      float out;
+      if (GATED) {
+        const float up = ((red[0][f0 + 1][i][l] + red[1][f0 + 1][i][l]) + red[2][f0 + 1][i][l]) +
+                         red[3][f0 + 1][i][l];
+        out = silu_f32(a) * up;
+      } else if (ACT == 0) {
+        out = gelu_f32(a);
+      } else if (ACT == 1) {
+        out = fmaxf(a, 0.f);
+      } else {
+        out = a;
+      }
+      const int64_t idx = (int64_t)(d.c_row0 + row) * N + col;
+      if (p.out_bf16) {
+        static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(out);
+      } else {
+        float* dst = static_cast<float*>(p.out) + idx;
+        *dst = p.accumulate ? *dst + out : out;
+      }
     }
-    const int64_t idx = (int64_t)(c_row0 + row) * N + col;
-    if (p.out_bf16) {
-      static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(out);
-    } else {
-      float* dst = static_cast<float*>(p.out) + idx;
-      *dst = p.accumulate ? *dst + out : out;
-    }
+    __syncthreads();  // red is reused by the next unit
+  };
+
+  // One continuous pipeline over the block's units: the loads of step i+1 (of
+  // this unit or the next) are in flight while step i is multiplied, so a
+  // unit's reduction and stores overlap the next unit's first loads.
+  if (total <= 0) return;
+  UnitDesc ld, cd;  // load side, multiply side
+  describe(u_begin, ld);
+  cd = ld;
+  zero_acc();
+  Stage s0, s1;
+  load(s0, ld, 0);
+#define MOE_SKINNY_STEP(Scur, Snext, i)                             \
+  {                                                                 \
+    const int nl = (i) + 1;                                         \
+    if (nl < total) {                                               \
+      if (nl % per == 0) describe(u_begin + nl / per, ld);          \
+      load(Snext, ld, nl % per);                                    \
+    }                                                               \
+    compute(Scur);                                                  \
+    if ((i) % per == per - 1) {                                     \
+      finish(cd, u_begin + (i) / per);                              \
+      zero_acc();                                                   \
+      cd = ld;                                                      \
+    }                                                               \
   }
+  for (int i = 0; i < total; i += 2) {
+    MOE_SKINNY_STEP(s0, s1, i)
+    if (i + 1 >= total) break;
+    MOE_SKINNY_STEP(s1, s0, i + 1)
+  }
+#undef MOE_SKINNY_STEP
 }
 
 }  // namespace
 
+int device_cus();
+
 hipError_t launch_ffn_skinny(const FfnParams& p, hipStream_t stream) {
-  const int n_slabs = (p.N + 63) / 64;
-  const int64_t blocks = (int64_t)(p.G + p.S) * n_slabs;
-  if (blocks > 0) {
-    const dim3 grid((unsigned)blocks), block(kThreads);
+  const int n_slabs = (p.N + kCols - 1) / kCols;
+  const int64_t n_units = (int64_t)(p.G + p.S) * n_slabs;
+  // two resident blocks per CU walk equal runs of units
+  const int64_t grid = std::min<int64_t>(n_units, (int64_t)device_cus() * kBlocksPerCU);
+  if (grid > 0) {
+    const dim3 g((unsigned)grid), block(kThreads);
+    const int nu = (int)n_units;
     switch (p.act) {
-      case 2: hipLaunchKernelGGL(ffn_skinny_kernel<2>, grid, block, 0, stream, p, n_slabs); break;
-      case 1: hipLaunchKernelGGL(ffn_skinny_kernel<1>, grid, block, 0, stream, p, n_slabs); break;
-      case 0: hipLaunchKernelGGL(ffn_skinny_kernel<0>, grid, block, 0, stream, p, n_slabs); break;
-      default: hipLaunchKernelGGL(ffn_skinny_kernel<-1>, grid, block, 0, stream, p, n_slabs); break;
+      case 2: hipLaunchKernelGGL(ffn_skinny_kernel<2>, g, block, 0, stream, p, n_slabs, nu); break;
+      case 1: hipLaunchKernelGGL(ffn_skinny_kernel<1>, g, block, 0, stream, p, n_slabs, nu); break;
+      case 0: hipLaunchKernelGGL(ffn_skinny_kernel<0>, g, block, 0, stream, p, n_slabs, nu); break;
+      default: hipLaunchKernelGGL(ffn_skinny_kernel<-1>, g, block, 0, stream, p, n_slabs, nu); break;
     }
   }
   return hipGetLastError();

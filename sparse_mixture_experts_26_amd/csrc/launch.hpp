@@ -24,7 +24,7 @@ struct RouteParams {
   int T, d, E, k;
   int bf16;
 };
-constexpr int kRouteTokens = 64;  // tokens per routing block
+constexpr int kRouteTokens = 16;  // tokens per routing block
 inline int route_blocks(int64_t T) { return (int)((T + kRouteTokens - 1) / kRouteTokens); }
 hipError_t launch_route(const RouteParams& p, hipStream_t stream);
 

@@ -6,60 +6,70 @@
 // eps * softplus(x W_noise) on the logits and a softmax over the selected
 // logits; "Mixture-of-experts Models", Level 2: a fixed tie rule.
 //
-// One block handles 64 tokens.  Phase 1 (skipped when replaying logits) computes
-// the [64, E(+E)] logit tile with bf16 MFMA 16x16x32 (float32 accumulate): each
-// wave owns 16 tokens and walks all expert columns 64 at a time.  The tile lands
-// in LDS, bias and noise are applied and the logits are written out.  Phase 2
-// gives every token to one wave: lanes hold experts e = lane + 64j, k rounds of a
-// wave-wide argmax on (value desc, index asc) pick the experts, and the same
-// registers yield the full softmax whose per-expert sums are reduced per block
-// in a fixed order (no atomics, so the result is deterministic).
+// One block handles 16 tokens with 4 or 16 waves.  Phase 1 (skipped when
+// replaying logits) computes the [16, E(+E)] logit tile with bf16 MFMA 16x16x32
+// (float32 accumulate): the waves split the model width into contiguous
+// ranges, so even a decode batch of a few tokens keeps many waves streaming x
+// and W_g, and the partial tiles are summed in LDS in a fixed order.  Bias and
+// noise are applied and the logits written out.  Phase 2 gives every token to
+// one wave: lanes hold experts e = lane + 64j, k rounds of a wave-wide argmax
+// on (value desc, index asc) pick the experts, and the same registers yield
+// the full softmax, whose per-expert sums over the block's tokens are written
+// per block and reduced in a fixed order by a second kernel (no atomics, so
+// results are deterministic).
 #include "launch.hpp"
 
 namespace moe {
 
 namespace {
 
-constexpr int kThreads = 256;
+// 16 waves split the model width when the logit tile is narrow (decode-sized
+// batches then still keep many loads in flight), 4 waves otherwise.
+constexpr int kMaxWaves = 16;
+constexpr int kMaxThreads = 64 * kMaxWaves;
+constexpr uint32_t kOOB = 0x80000000u;
 
-__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
-  uint4 v = *reinterpret_cast<const uint4*>(p);
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// Phase 1, bf16: raw products into sH[m*ldh + n], n < ncols (gate columns,
-// then noise columns).
-__device__ void router_tile_bf16(const RouteParams& p, float* sH, int ldh, int t_base,
-                                 int ncols) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const uint16_t* x = static_cast<const uint16_t*>(p.x);
-  const uint16_t* wg = static_cast<const uint16_t*>(p.w_g);
-  const uint16_t* wn = static_cast<const uint16_t*>(p.w_noise);
-  const int row = t_base + w * 16 + (lane & 15);
-  const bool row_ok = row < p.T;
-  const uint16_t* xrow = x + (int64_t)(row_ok ? row : 0) * p.d;
+// Phase 1, bf16: this wave's partial products over its model-width range into
+// part[m*ldh + n], n < ncols (gate columns, then noise columns).  The block's
+// nw waves split the model width into nw contiguous ranges.
+__device__ void router_tile_bf16(const RouteParams& p, float* part, int ldh, int t_base,
+                                 int ncols, int nw) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int d = p.d;
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.x), (short)0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.w_g), (short)0, (int)((int64_t)p.E * d * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t nr = p.w_noise ? __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.w_noise), (short)0, (int)((int64_t)p.E * d * 2), 0x00020000) : gr;
+  const int row = t_base + (lane & 15);
   const int kofs = (lane >> 4) * 8;
-  const bf16x8 zero = {};
+  const uint32_t a_base = row < p.T ? (uint32_t)row * (uint32_t)d * 2u : kOOB;
+  // contiguous model-width range of this wave, in steps of 32
+  const int steps = (d + 31) / 32, per = (steps + nw - 1) / nw;
+  const int kb = w * per * 32, ke = min(d, (w + 1) * per * 32);
   for (int nb = 0; nb < ncols; nb += 64) {
-    const uint16_t* wrow[4];
-    bool n_ok[4];
+    uint32_t b_base[4];
+    bool noise_col[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = nb + j * 16 + (lane & 15);
-      n_ok[j] = n < ncols;
-      const int nn = n_ok[j] ? n : 0;
-      wrow[j] = nn < p.E ? wg + (int64_t)nn * p.d : wn + (int64_t)(nn - p.E) * p.d;
+      noise_col[j] = n >= p.E;
+      const int nn = noise_col[j] ? n - p.E : n;
+      b_base[j] = n < ncols ? (uint32_t)nn * (uint32_t)d * 2u : kOOB;
     }
     f32x4 acc[4] = {};
 #pragma unroll 4
-    for (int k0 = 0; k0 < p.d; k0 += 32) {
+    for (int k0 = kb; k0 < ke; k0 += 32) {
       const int kk = k0 + kofs;
-      const bool k_ok = kk < p.d;
-      const bf16x8 a = (row_ok && k_ok) ? load_bf16x8(xrow + kk) : zero;
+      const uint32_t kadd = kk < ke ? (uint32_t)kk * 2u : kOOB;
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, a_base + kadd, 0, 0));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bf16x8 b = (n_ok[j] && k_ok) ? load_bf16x8(wrow[j] + kk) : zero;
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+        const u32x4 bv = noise_col[j] ? __builtin_amdgcn_raw_buffer_load_b128(nr, b_base[j] + kadd, 0, 0)
+                                      : __builtin_amdgcn_raw_buffer_load_b128(gr, b_base[j] + kadd, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bv), acc[j], 0, 0, 0);
       }
     }
     // 16x16 result layout: lane holds column lane%16, rows 4*(lane/16) + i.
@@ -68,7 +78,7 @@ __device__ void router_tile_bf16(const RouteParams& p, float* sH, int ldh, int t
       const int n = nb + j * 16 + (lane & 15);
       if (n < ncols) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sH[(w * 16 + (lane >> 4) * 4 + i) * ldh + n] = acc[j][i];
+        for (int i = 0; i < 4; ++i) part[((lane >> 4) * 4 + i) * ldh + n] = acc[j][i];
       }
     }
   }
@@ -80,7 +90,7 @@ __device__ void router_tile_f32(const RouteParams& p, float* sH, int ldh, int t_
   const float* x = static_cast<const float*>(p.x);
   const float* wg = static_cast<const float*>(p.w_g);
   const float* wn = static_cast<const float*>(p.w_noise);
-  for (int i = threadIdx.x; i < kRouteTokens * ncols; i += kThreads) {
+  for (int i = threadIdx.x; i < kRouteTokens * ncols; i += blockDim.x) {
     const int m = i / ncols, n = i - m * ncols, t = t_base + m;
     if (t >= p.T) continue;
     const float* xr = x + (int64_t)t * p.d;
@@ -91,20 +101,32 @@ __device__ void router_tile_f32(const RouteParams& p, float* sH, int ldh, int t_
   }
 }
 
-__global__ __launch_bounds__(kThreads) void route_kernel(RouteParams p) {
-  extern __shared__ float sH[];
-  __shared__ double sP[4][256];
+__global__ __launch_bounds__(kMaxThreads) void route_kernel(RouteParams p) {
+  extern __shared__ float lds[];  // nw partial tiles [16][ldh]; tile 0 becomes the logits
+  __shared__ double sP[kMaxWaves][256];
+  const int nt = blockDim.x, nw = nt >> 6;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t_base = blockIdx.x * kRouteTokens;
   const bool noise = p.w_noise != nullptr;
   const int ncols = p.E * (noise ? 2 : 1);
   const int ldh = ncols + 1;
+  const int tile = kRouteTokens * ldh;
+  float* sH = lds;
 
   if (p.x != nullptr) {
-    if (p.bf16) router_tile_bf16(p, sH, ldh, t_base, ncols);
-    else router_tile_f32(p, sH, ldh, t_base, ncols);
+    if (p.bf16) {
+      router_tile_bf16(p, lds + w * tile, ldh, t_base, ncols, nw);
+      __syncthreads();
+      for (int i = threadIdx.x; i < tile; i += nt) {
+        float v = lds[i];
+        for (int q = 1; q < nw; ++q) v += lds[q * tile + i];  // fixed order
+        sH[i] = v;
+      }
+    } else {
+      router_tile_f32(p, sH, ldh, t_base, ncols);
+    }
     __syncthreads();
-    for (int i = threadIdx.x; i < kRouteTokens * p.E; i += kThreads) {
+    for (int i = threadIdx.x; i < kRouteTokens * p.E; i += nt) {
       const int m = i / p.E, e = i - m * p.E, t = t_base + m;
       if (t >= p.T) continue;
       float v = sH[m * ldh + e];
@@ -114,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteParams p) {
       p.logits[(int64_t)t * p.E + e] = v;
     }
   } else {
-    for (int i = threadIdx.x; i < kRouteTokens * p.E; i += kThreads) {
+    for (int i = threadIdx.x; i < kRouteTokens * p.E; i += nt) {
       const int m = i / p.E, e = i - m * p.E, t = t_base + m;
       if (t < p.T) sH[m * ldh + e] = p.logits[(int64_t)t * p.E + e];
     }
@@ -124,8 +146,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteParams p) {
   // Phase 2: one token per wave iteration; lane owns experts lane + 64*j.
   const int nj = (p.E + 63) >> 6;
   float pacc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int mi = 0; mi < 16; ++mi) {
-    const int m = w * 16 + mi, t = t_base + m;
+  const int tpw = kRouteTokens / nw;  // tokens per wave
+  for (int mi = 0; mi < tpw; ++mi) {
+    const int m = w * tpw + mi, t = t_base + m;
     if (t >= p.T) break;
     float v[4];
     float mx = -INFINITY;
@@ -190,19 +213,24 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteParams p) {
     if (e < 256) sP[w][e] = (double)pacc[j];
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < p.E; e += kThreads)
-    p.prob_partial[(int64_t)blockIdx.x * p.E + e] =
-        (float)(((sP[0][e] + sP[1][e]) + sP[2][e]) + sP[3][e]);
+  for (int e = threadIdx.x; e < p.E; e += nt) {
+    double v = sP[0][e];
+    for (int q = 1; q < nw; ++q) v += sP[q][e];  // fixed order
+    p.prob_partial[(int64_t)blockIdx.x * p.E + e] = (float)v;
+  }
 }
 
-// prob_sum[e] = sum over routing blocks, in block order, accumulated in double.
+// prob_sum[e] = sum over routing blocks: one wave per expert, each lane sums a
+// fixed strided subset in double, then a fixed butterfly; deterministic.
 __global__ __launch_bounds__(256) void prob_reduce_kernel(const float* partial, float* out,
                                                           int nblocks, int E) {
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    double s = 0.0;
-    for (int b = 0; b < nblocks; ++b) s += (double)partial[(int64_t)b * E + e];
-    out[e] = (float)s;
-  }
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (e >= E) return;
+  double s = 0.0;
+  for (int b = lane; b < nblocks; b += 64) s += (double)partial[(int64_t)b * E + e];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
+  if (lane == 0) out[e] = (float)s;
 }
 
 }  // namespace
@@ -210,9 +238,10 @@ __global__ __launch_bounds__(256) void prob_reduce_kernel(const float* partial, 
 hipError_t launch_route(const RouteParams& p, hipStream_t stream) {
   const int blocks = route_blocks(p.T);
   const int ncols = p.E * (p.w_noise ? 2 : 1);
-  const size_t lds = (size_t)kRouteTokens * (ncols + 1) * sizeof(float);
-  hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(kThreads), lds, stream, p);
-  hipLaunchKernelGGL(prob_reduce_kernel, dim3(1), dim3(256), 0, stream,
+  const int nw = (p.bf16 && p.x && ncols <= 64) ? kMaxWaves : 4;
+  const size_t lds = (size_t)nw * kRouteTokens * (ncols + 1) * sizeof(float);
+  hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(64 * nw), lds, stream, p);
+  hipLaunchKernelGGL(prob_reduce_kernel, dim3((p.E + 3) / 4), dim3(256), 0, stream,
                      (const float*)p.prob_partial, p.prob_sum, blocks, p.E);
   return hipGetLastError();
 }
