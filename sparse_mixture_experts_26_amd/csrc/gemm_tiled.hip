@@ -19,11 +19,15 @@
 // gated (SwiGLU) form the 256 weight rows are 128 rows of w1 and the same 128
 // rows of w3, and every wave holds matching gate and up tiles, so
 // silu(gate) * up is formed in registers.  Operands travel global -> LDS with
-// direct-to-LDS buffer loads (no register staging) through a ring of five
-// 32-deep stages (the whole 160 KiB of LDS), four in flight while one is
-// consumed; each wave waits only for its own loads of the next stage, then a
-// plain s_barrier publishes it.  The 16-byte chunks of every 64-byte LDS row
-// are XOR-swizzled by row so the MFMA operand reads are bank-conflict-free.
+// direct-to-LDS buffer loads (no register staging) in 64-deep stages, so every
+// row of a stage is one whole 128-byte line: the vector L1 then issues
+// full-line requests, which move about a third more data per clock from L2
+// than half-line ones.  A stage is four 16 KiB quarters (A rows 0-127 and
+// 128-255, B rows 0-127 and 128-255) and the ring holds ten quarters (the
+// whole 160 KiB), i.e. 2.5 stages; each wave waits only for its own loads and
+// a plain s_barrier publishes a stage.  The 16-byte chunks of every 128-byte
+// LDS row are XOR-swizzled by row so the MFMA operand reads are
+// bank-conflict-free.
 // Routed rows are gathered from the token matrix through row_token, which
 // removes the separate permuted copy from the layer.  The epilogue stages each
 // wave's results through LDS and stores 16-byte row chunks.
@@ -37,21 +41,23 @@ namespace {
 
 constexpr int BM = 256;      // output rows per tile
 constexpr int BR = 256;      // weight rows per tile
-constexpr int BK = 32;       // reduction depth per stage
+constexpr int BK = 64;       // reduction depth per stage (one 128-byte line per row)
 constexpr int kThreads = 512;  // 8 waves: 2 per SIMD
 constexpr int kGroupM = 8;   // row-tiles that sweep the columns together
-constexpr int kTileBytes = BM * BK * 2;  // one operand tile, 16 KiB
-constexpr int kStageBytes = 2 * kTileBytes;  // A tile then B tile
+constexpr int kQuarter = 128 * BK * 2;  // 128 rows of one operand, 16 KiB
+constexpr int kSlots = 10;              // ring of quarters: the whole 160 KiB
 
 // Kept out of line so the fully unrolled epilogue stays small enough to keep
 // every accumulator in registers.
 __device__ __noinline__ float gelu_outlined(float a) { return gelu_f32(a); }
 
-// Slot of 16-byte chunk kc (0..3) of a 64-byte LDS row: XOR with bits 1-3 of
-// the row, so 8 consecutive rows (one 128-byte bank sweep) and 16 consecutive
-// rows (two sweeps) both hit distinct banks for a fixed chunk.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
-__device__ __forceinline__ int lds_off(int row, int kc) { return row * 64 + ((kc ^ swz(row)) << 4); }
+// Slot of 16-byte chunk kc (0..7) of a 128-byte LDS row: XOR with
+// (r ^ r >> 3) & 7 of the row's low 5 bits, so any 8 aligned rows, and the even
+// and the odd rows of any 16 aligned rows, hold a given chunk in distinct slots:
+// bank-conflict-free operand reads whether the LDS serves 8 or 16 lanes of a
+// 16-byte read per cycle.  Fragment rows are 32-aligned, so the swizzle depends
+// on the lane only.
+__device__ __forceinline__ int swz(int row) { return (row ^ ((row & 31) >> 3)) & 7; }
 
 #define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -120,11 +126,7 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* offsets
 template <int ACT>
 __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int n_tiles_n) {
   constexpr bool GATED = ACT == 2;
-  __shared__ __attribute__((aligned(16))) char S0[kStageBytes];
-  __shared__ __attribute__((aligned(16))) char S1[kStageBytes];
-  __shared__ __attribute__((aligned(16))) char S2[kStageBytes];
-  __shared__ __attribute__((aligned(16))) char S3[kStageBytes];
-  __shared__ __attribute__((aligned(16))) char S4[kStageBytes];
+  __shared__ __attribute__((aligned(16))) char L[kSlots * kQuarter];
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform per wave; say so, or LDS-destination and buffer
   // resource operands that depend on it become per-lane (waterfall) loops
@@ -141,16 +143,20 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
   const int nk = (K + BK - 1) / BK;
   constexpr uint32_t kOOB = 0x80000000u;
 
-  // LDS read offsets (fragment rows are 32-aligned, so the swizzle depends on lr)
-  int rd_a[2], rd_b[2][2];
+  // Operand reads.  Quarter layout: rows of 128 bytes, chunk c of row r at
+  // r*128 + ((c ^ swz(r)) << 4).  Sub-step s (16 deep) reads chunk 2s + lh.
+  // the chunk field is bits 4-6 and the row bits 7+, so sub-step s's offset
+  // is rd0 ^ (s << 5)
+  const int rd0 = lr * 128 + ((lh ^ swz(lr)) << 4);
+  // quarter (0 A rows 0-127, 1 A rows 128-255, 2 B rows 0-127, 3 B rows 128-255)
+  // and row inside it of this wave's fragments
+  const int qa = wm;
+  int qb[2], rb[2];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    rd_a[kk] = lds_off(wm * 128 + lr, kk * 2 + lh);
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int br = GATED ? ni * 128 + wn * 32 : wn * 64 + ni * 32;
-      rd_b[kk][ni] = kTileBytes + lds_off(br + lr, kk * 2 + lh);
-    }
+  for (int ni = 0; ni < 2; ++ni) {
+    const int br = GATED ? ni * 128 + wn * 32 : wn * 64 + ni * 32;
+    qb[ni] = 2 + (br >> 7);
+    rb[ni] = br & 127;
   }
 
   for (int t = xcd * per + q; t < t_end; t += nq) {
@@ -169,29 +175,35 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     const uint16_t* A = static_cast<const uint16_t*>(routed ? p.a_main : p.a_shared);
     const int n_out0 = n_idx * (GATED ? BR / 2 : BR);
 
-    // ---- direct-to-LDS loads: a stage is 16 A and 16 B loads of 1 KiB (16 rows x
-    // 64 bytes); wave w issues A blocks 2w, 2w+1 and B blocks 2w, 2w+1.  Lane i
-    // fills row i/4, slot i%4 of its block, so it fetches the chunk the swizzle
-    // stores there.  Buffer resources return zeros past their end: rows past
-    // the tile, weight rows past N and chunks past K need no branches.
+    // ---- direct-to-LDS loads.  A quarter is 16 loads of 1 KiB (8 rows x 128
+    // bytes, whole cache lines); wave w fills rows 16w .. 16w+15 of every
+    // quarter with two loads.  Lane i fills row i/8, slot i%8 of its load, so it
+    // fetches the chunk the swizzle stores there.  Buffer resources return
+    // zeros past their end: rows past the tile, weight rows past N and chunks
+    // past K need no branches.
     const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(A), (short)0, 0x7fffffff, 0x00020000);
-    const uint16_t* Bsrc = (GATED && wid >= 4) ? U : W;  // B rows 128.. are w3's
-    const __amdgpu_buffer_rsrc_t b_rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(Bsrc), (short)0, (int)(wstride * 2), 0x00020000);
-    uint32_t a_off[2], b_off[2];
+    const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(W), (short)0, (int)(wstride * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t u_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(U), (short)0, (int)(wstride * 2), 0x00020000);
+    uint32_t off[4][2];  // [quarter][load]
     int l_kc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int row = (wid * 2 + j) * 16 + (lane >> 2);  // tile row 0..255
-      const int kc = (lane & 3) ^ swz(row);
+      const int rq = (wid * 2 + j) * 8 + (lane >> 3);  // row inside a quarter
+      const int kc = (lane & 7) ^ swz(rq);
       l_kc[j] = kc;
-      const bool ok = row < te.rows;
-      int arow = p.a_from_c ? te.c_row0 + row : te.a_row0 + row;
-      if (ok && routed && p.gather && !p.a_from_c) arow = p.gather[arow];
-      a_off[j] = ok ? ((uint32_t)arow * (uint32_t)K + kc * 8) * 2u : kOOB;
-      const int n = n_out0 + (GATED ? (row & 127) : row);
-      b_off[j] = n < N ? ((uint32_t)n * (uint32_t)K + kc * 8) * 2u : kOOB;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = h * 128 + rq;  // tile row
+        const bool ok = row < te.rows;
+        int arow = p.a_from_c ? te.c_row0 + row : te.a_row0 + row;
+        if (ok && routed && p.gather && !p.a_from_c) arow = p.gather[arow];
+        off[h][j] = ok ? ((uint32_t)arow * (uint32_t)K + kc * 8) * 2u : kOOB;
+        const int n = n_out0 + (GATED ? rq : row);
+        off[2 + h][j] = n < N ? ((uint32_t)n * (uint32_t)K + kc * 8) * 2u : kOOB;
+      }
     }
 
     f32x16 acc[4][2];
@@ -200,25 +212,32 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x16{};
 
-    auto issue = [&](char* Sx, int kt) __attribute__((always_inline)) {
-      const int k0 = kt * BK;  // stages past the end (kt >= nk) read zeros
+    // quarter qq (0..3) of stage kt into ring slot `slot`; stages past the
+    // end read zeros
+    auto issue = [&](int slot, int qq, int kt) __attribute__((always_inline)) {
+      const int k0 = kt * BK;
+      const __amdgpu_buffer_rsrc_t rs = qq < 2 ? a_rs : (GATED && qq == 3 ? u_rs : w_rs);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const uint32_t kadd = (k0 + l_kc[j] * 8 < K) ? (uint32_t)k0 * 2u : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, MOE_LDS(Sx + (wid * 2 + j) * 1024), 16,
-                                                 a_off[j] + kadd, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, MOE_LDS(Sx + kTileBytes + (wid * 2 + j) * 1024),
-                                                 16, b_off[j] + kadd, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, MOE_LDS(L + slot * kQuarter + (wid * 2 + j) * 1024), 16, off[qq][j] + kadd, 0, 0, 0);
       }
     };
-    // Fragments of one 16-deep half of a stage: 4 A and 2 B operands.
     struct Frags { bf16x8 a[4], b[2]; };
-    auto read = [&](Frags& f, const char* Sx, int kk) __attribute__((always_inline)) {
+    // sub-step s of the stage whose quarters start at ring slot base
+    auto read = [&](Frags& f, int base, int s) __attribute__((always_inline)) {
+      // opaque per step, so the slot addresses are formed here (one add per
+      // operand) instead of being kept live across the loop for every slot
+      int r = rd0;
+      asm volatile("" : "+v"(r));
+      r ^= s << 5;
+      const int sa = base + qa, sb0 = base + qb[0], sb1 = base + qb[1];
+      const char* pa = L + (sa >= kSlots ? sa - kSlots : sa) * kQuarter + r;
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        f.a[mi] = *reinterpret_cast<const bf16x8*>(Sx + rd_a[kk] + mi * 32 * 64);
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) f.b[ni] = *reinterpret_cast<const bf16x8*>(Sx + rd_b[kk][ni]);
+      for (int mi = 0; mi < 4; ++mi) f.a[mi] = *reinterpret_cast<const bf16x8*>(pa + mi * 32 * 128);
+      f.b[0] = *reinterpret_cast<const bf16x8*>(L + (sb0 >= kSlots ? sb0 - kSlots : sb0) * kQuarter + rb[0] * 128 + r);
+      f.b[1] = *reinterpret_cast<const bf16x8*>(L + (sb1 >= kSlots ? sb1 - kSlots : sb1) * kQuarter + rb[1] * 128 + r);
     };
     auto mfma = [&](const Frags& f) __attribute__((always_inline)) {
 #pragma unroll
@@ -229,71 +248,80 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     };
     auto barrier = [&]() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
 
-    // Pipeline (stage = 32 deep in two 16-deep halves; ring of five LDS
-    // stages, the whole 160 KiB): at the top of step kt stage kt is published
-    // and the first half of its fragments is in registers.  The step waits for
-    // this wave's loads of stage kt+1 (the 8 loads of stages kt+2 and kt+3 may
-    // stay in flight); the barrier publishes stage kt+1 and frees the slot of
-    // stage kt-1, which is refilled with stage kt+4.  The second half of stage
-    // kt and the first half of stage kt+1 are read while the MFMAs run.  Every
-    // step issues its 4 loads, past the end too (they read zeros), so the wait
-    // counts are fixed.  Four stages in flight cover the load latency of the
-    // streamed operands.
-    //
-    // Instruction order inside a step, fixed with sched_group_barrier:
-    //   MFMAs 1-8  on f0: an LDS read into f1 after MFMA 1-6, loads after 2 and 6
-    //   MFMAs 9-16 on f1: an LDS read into f0 after MFMA 9-14, loads after 10 and 14
+    // Pipeline.  The ring holds 2.5 stages: quarters are loaded in the order
+    // (stage, quarter) and quarter j of that order goes to slot j % 10.  Step
+    // kt waits for this wave's loads of stage kt (the 4 loads of stage kt+1's
+    // first half may stay in flight); the barrier publishes stage kt and frees
+    // the slots of stage kt-1, which take stage kt+1's second half and stage
+    // kt+2's first half.  Every wave has completed its reads of stage kt-1
+    // before the barrier (lgkmcnt 0): the last 16-deep sub-step of each stage
+    // is read before the barrier and multiplied after it, so the MFMAs cover
+    // the first read of the next stage.  Every step issues its 8 loads, past
+    // the end too (they read zeros), so the wait counts are fixed.
 #define MOE_PATTERN()                                                    \
   {                                                                      \
-    _Pragma("unroll") for (int i = 0; i < 16; ++i) {                     \
+    _Pragma("unroll") for (int i = 0; i < 32; ++i) {                     \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 \
       if ((i & 7) < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); \
       if ((i & 3) == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); \
     }                                                                    \
   }
-#define MOE_STEP(Scur, Snext, Sfill, kt) \
-  {                                      \
-    wait_vmcnt<8>();                     \
-    barrier();                           \
-    issue(Sfill, (kt) + 4);              \
-    read(f1, Scur, 1);                   \
-    mfma(f0);                            \
-    read(f0, Snext, 0);                  \
-    mfma(f1);                            \
-    MOE_PATTERN()                        \
+#define MOE_STEP(B, kt)                                        \
+  {                                                            \
+    wait_vmcnt<4>();                                           \
+    __builtin_amdgcn_s_waitcnt(0xc07f); /* lgkmcnt(0) */        \
+    barrier();                                                 \
+    issue(((B) + 6) % kSlots, 2, (kt) + 1);                    \
+    issue(((B) + 7) % kSlots, 3, (kt) + 1);                    \
+    issue(((B) + 8) % kSlots, 0, (kt) + 2);                    \
+    issue(((B) + 9) % kSlots, 1, (kt) + 2);                    \
+    read(f0, (B), 0);                                          \
+    mfma(f1);                                                  \
+    read(f1, (B), 1);                                          \
+    mfma(f0);                                                  \
+    read(f0, (B), 2);                                          \
+    mfma(f1);                                                  \
+    read(f1, (B), 3);                                          \
+    mfma(f0);                                                  \
+    MOE_PATTERN()                                              \
   }
     Frags f0, f1;
-    barrier();  // the previous tile's last reads are done
-    issue(S0, 0);
-    issue(S1, 1);
-    issue(S2, 2);
-    issue(S3, 3);
-    wait_vmcnt<12>();
-    barrier();
-    read(f0, S0, 0);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) f1.a[mi] = bf16x8{};
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) f1.b[ni] = bf16x8{};
+    barrier();  // the previous tile's epilogue is done with the ring
+    issue(0, 0, 0);
+    issue(1, 1, 0);
+    issue(2, 2, 0);
+    issue(3, 3, 0);
+    issue(4, 0, 1);
+    issue(5, 1, 1);
     int kt = 0;
     for (; kt + 5 <= nk; kt += 5) {
-      MOE_STEP(S0, S1, S4, kt)
-      MOE_STEP(S1, S2, S0, kt + 1)
-      MOE_STEP(S2, S3, S1, kt + 2)
-      MOE_STEP(S3, S4, S2, kt + 3)
-      MOE_STEP(S4, S0, S3, kt + 4)
+      MOE_STEP(0, kt)
+      MOE_STEP(4, kt + 1)
+      MOE_STEP(8, kt + 2)
+      MOE_STEP(2, kt + 3)
+      MOE_STEP(6, kt + 4)
     }
-    if (kt < nk) MOE_STEP(S0, S1, S4, kt)
-    if (kt + 1 < nk) MOE_STEP(S1, S2, S0, kt + 1)
-    if (kt + 2 < nk) MOE_STEP(S2, S3, S1, kt + 2)
-    if (kt + 3 < nk) MOE_STEP(S3, S4, S2, kt + 3)
+    if (kt < nk) MOE_STEP(0, kt)
+    if (kt + 1 < nk) MOE_STEP(4, kt + 1)
+    if (kt + 2 < nk) MOE_STEP(8, kt + 2)
+    if (kt + 3 < nk) MOE_STEP(2, kt + 3)
 #undef MOE_STEP
 #undef MOE_PATTERN
-    // loads issued past the end (zeros) land before the LDS is reused or freed
+    mfma(f1);  // the last sub-step
+    // loads issued past the end (zeros) land before the LDS is reused
     wait_vmcnt<0>();
 
     // ---- epilogue.  32x32 result layout: lane holds column lane%32, rows
     // 8*(v/4) + 4*(lane/32) + v%4 for v = 0..15.  Each wave stages its block
-    // through a private LDS region (rows padded by 16 bytes so the two lane
-    // halves, 4 rows apart, hit different banks) and writes it back as 16-byte
-    // row chunks, instead of 2-byte scattered stores.  A wave's LDS operations
-    // complete in order, so only the barrier that frees the ring is needed.
+    // through a private 16 KiB LDS region (rows padded by 16 bytes so the two
+    // lane halves, 4 rows apart, hit different banks) and writes it back as
+    // 16-byte row chunks, instead of 2-byte scattered stores.  A wave's LDS
+    // operations complete in order, so only the barrier that frees the ring is
+    // needed.
     barrier();
     const float* bias = routed ? p.bias_main : p.bias_shared;
     // Up projections (ACT >= 0) write the bf16 hidden layer; the down projection
@@ -303,12 +331,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     constexpr int COLS = NJ * 32;                // columns per wave
     constexpr int esz = OUT_BF16 ? 2 : 4;
     constexpr int row_bytes = COLS * esz + 16;
-    // Each wave owns half of one 32 KiB stage array (arrays need not be
-    // adjacent); rows per pass keep the block within those 16 KiB.
     constexpr int rows_pass = (128 * row_bytes <= 16384) ? 128 : (64 * row_bytes <= 16384 ? 64 : 32);
     static_assert(rows_pass * row_bytes <= 16384, "staging block exceeds the wave's region");
-    char* const stage_of_wave = wid < 2 ? S0 : wid < 4 ? S1 : wid < 6 ? S2 : S3;
-    char* const region = stage_of_wave + (wid & 1) * 16384;
+    char* const region = L + wid * 16384;
     const int col0 = n_out0 + (GATED ? wn * 32 : wn * 64);  // first column of the wave block
     float bcol[NJ];
 #pragma unroll
