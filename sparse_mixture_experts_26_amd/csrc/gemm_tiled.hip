@@ -22,8 +22,8 @@
 // direct-to-LDS buffer loads (no register staging) in 64-deep stages, so every
 // row of a stage is one whole 128-byte line: the vector L1 then issues
 // full-line requests, which move about a third more data per clock from L2
-// than half-line ones.  A stage is four 16 KiB quarters (A rows 0-127 and
-// 128-255, B rows 0-127 and 128-255) and the ring holds ten quarters (the
+// than half-line ones.  A stage is four 16 KiB quarters (B rows 0-127 and
+// 128-255, A rows 0-127 and 128-255) and the ring holds ten quarters (the
 // whole 160 KiB), i.e. 2.5 stages; each wave waits only for its own loads and
 // a plain s_barrier publishes a stage.  The 16-byte chunks of every 128-byte
 // LDS row are XOR-swizzled by row so the MFMA operand reads are
@@ -148,14 +148,17 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
   // the chunk field is bits 4-6 and the row bits 7+, so sub-step s's offset
   // is rd0 ^ (s << 5)
   const int rd0 = lr * 128 + ((lh ^ swz(lr)) << 4);
-  // quarter (0 A rows 0-127, 1 A rows 128-255, 2 B rows 0-127, 3 B rows 128-255)
-  // and row inside it of this wave's fragments
-  const int qa = wm;
+  // quarter (0 B rows 0-127, 1 B rows 128-255, 2 A rows 0-127, 3 A rows
+  // 128-255) and row inside it of this wave's fragments.  The weights come
+  // first: they stream from HBM, while the token rows are re-read by every
+  // column sweep and mostly hit the MALL, so the weights get the longer
+  // lookahead (their quarters are issued two steps ahead, the token rows' one).
+  const int qa = 2 + wm;
   int qb[2], rb[2];
 #pragma unroll
   for (int ni = 0; ni < 2; ++ni) {
     const int br = GATED ? ni * 128 + wn * 32 : wn * 64 + ni * 32;
-    qb[ni] = 2 + (br >> 7);
+    qb[ni] = br >> 7;
     rb[ni] = br & 127;
   }
 
@@ -200,9 +203,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
         const bool ok = row < te.rows;
         int arow = p.a_from_c ? te.c_row0 + row : te.a_row0 + row;
         if (ok && routed && p.gather && !p.a_from_c) arow = p.gather[arow];
-        off[h][j] = ok ? ((uint32_t)arow * (uint32_t)K + kc * 8) * 2u : kOOB;
+        off[2 + h][j] = ok ? ((uint32_t)arow * (uint32_t)K + kc * 8) * 2u : kOOB;
         const int n = n_out0 + (GATED ? rq : row);
-        off[2 + h][j] = n < N ? ((uint32_t)n * (uint32_t)K + kc * 8) * 2u : kOOB;
+        off[h][j] = n < N ? ((uint32_t)n * (uint32_t)K + kc * 8) * 2u : kOOB;
       }
     }
 
@@ -216,7 +219,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     // end read zeros
     auto issue = [&](int slot, int qq, int kt) __attribute__((always_inline)) {
       const int k0 = kt * BK;
-      const __amdgpu_buffer_rsrc_t rs = qq < 2 ? a_rs : (GATED && qq == 3 ? u_rs : w_rs);
+      const __amdgpu_buffer_rsrc_t rs = qq >= 2 ? a_rs : (GATED && qq == 1 ? u_rs : w_rs);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const uint32_t kadd = (k0 + l_kc[j] * 8 < K) ? (uint32_t)k0 * 2u : kOOB;
