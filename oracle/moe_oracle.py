@@ -42,6 +42,22 @@ design notes):
       capacity and the statistics ([MoE&SMS] "Advanced Theory & Extensions").
   R8  GELU is the exact erf form; SwiGLU is silu(x W1^T) * (x W3^T) then W2.
 
+Expert-choice routing ([MoE&SMS] "Advanced Theory & Extensions": every expert
+takes the tokens it scores highest, up to its capacity, so a token may be
+processed by no expert or by several).  The page fixes neither the score nor
+the tie rule; the readings:
+  EC1 The score of token t for expert e is the softmax over experts of t's
+      logits (the same probabilities P is built from), rounded once to
+      float32; the ranking is decided on those float32 scores.
+  EC2 Each expert takes C' = min(C, T) tokens, C = floor(factor * T * k / E)
+      as in R3, k read as the average number of experts per token.
+  EC3 Equal scores go to the lower token index.
+  EC4 The gate of a (token, expert) pair is the token's float32 score for
+      that expert, not renormalised over the experts that took the token.
+  EC5 An expert's rows are laid out in ascending token order (layout only).
+  EC6 f_i = rows of expert i / all rows (1/E here), P and L_aux as in R5, and
+      the drop rate is the fraction of tokens that no expert took.
+
 Layouts (row-major, every weight in out x in form, as an nn.Linear stores it):
   x [T,d]; w_g, w_noise [E,d]; b_g [E]; eps [T,E]; w1, w3 [E,h,d]; w2 [E,d,h];
   b1 [E,h]; b2 [E,d]; ws1, ws3 [S,h,d]; ws2 [S,d,h].
@@ -58,7 +74,8 @@ __all__ = [
     "to_f64", "softplus", "router_logits", "select_top_k", "selected_gates",
     "full_softmax", "capacity", "dispatch_in_arrival_order", "dispatch",
     "activation", "expert_ffn", "combine", "balance_stats", "moe_forward",
-    "overflow_record",
+    "overflow_record", "expert_choice_scores", "expert_choice_select",
+    "expert_choice_combine", "moe_forward_expert_choice",
 ]
 
 
@@ -350,3 +367,91 @@ def overflow_record(idx: np.ndarray, dest: np.ndarray) -> list:
                         "fallback": "drop", "dropped": lost})
     return rec
 
+
+def expert_choice_scores(H32: np.ndarray) -> np.ndarray:
+    """Scores for expert-choice routing (EC1): the per-token softmax over the
+    experts, computed in float64 from the float32 logits, rounded to float32."""
+    return full_softmax(H32).astype(np.float32)
+
+
+def expert_choice_select(S32: np.ndarray, C: int) -> dict:
+    """Every expert takes the min(C, T) tokens with the highest float32 score,
+    equal scores to the lower token index (EC2, EC3): a stable sort of the
+    negated column.  Rows are expert-contiguous, each expert's tokens in
+    ascending order (EC5).  ``slot[t, e]`` is the row holding (t, e), or -1."""
+    S32 = np.asarray(S32, np.float32)
+    T, E = S32.shape
+    Cp = min(int(C), T)
+    row_token = np.empty(E * Cp, np.int32)
+    slot = np.full((T, E), -1, np.int32)
+    for e in range(E):
+        chosen = np.sort(np.argsort(-S32[:, e], kind="stable")[:Cp])
+        row_token[e * Cp:(e + 1) * Cp] = chosen
+        slot[chosen, e] = e * Cp + np.arange(Cp, dtype=np.int32)
+    counts = np.full(E, Cp, np.int64)
+    offsets = np.arange(E + 1, dtype=np.int64) * Cp
+    return {"counts": counts, "offsets": offsets, "row_token": row_token, "slot": slot,
+            "capacity_used": Cp}
+
+
+def expert_choice_combine(d, S32, slot, rows_out, tokens, shared_out=None) -> np.ndarray:
+    """y_t = shared experts + sum over e in ascending order of the experts that
+    took t of S[t, e] * FFN_e(x_t), in float64 (EC4); a token no expert took
+    gets the shared part only."""
+    y = np.zeros((len(tokens), d), np.float64) if shared_out is None else np.array(shared_out, np.float64)
+    for i, t in enumerate(tokens):
+        for e in range(slot.shape[1]):
+            r = int(slot[t, e])
+            if r >= 0:
+                y[i] += np.float64(S32[t, e]) * rows_out[r]
+    return y
+
+
+def moe_forward_expert_choice(x, w_g, w1, w2, *, k: int, act: str, capacity_factor: float,
+                              w3=None, b_g=None, w_noise=None, eps=None, b1=None, b2=None,
+                              ws1=None, ws3=None, ws2=None, logits=None, scores=None,
+                              tokens=None) -> dict:
+    """The layer forward with expert-choice routing.
+
+    1. router logits H (or the supplied float32 ``logits``);
+    2. scores S (EC1, or the supplied float32 ``scores``), P from H as in R5;
+    3. every expert takes its min(C, T) best tokens (EC2, EC3);
+    4. every expert on its rows (restricted to ``tokens`` if given);
+    5. y_t = shared experts + the sum over the experts that took t, in expert
+       order, of S[t, e] * FFN_e(x_t) (EC4); statistics (EC6).
+    """
+    T, d = np.asarray(x).shape
+    E = np.asarray(w_g).shape[0]
+    H = router_logits(x, w_g, b_g, w_noise, eps) if logits is None else np.asarray(logits, np.float32)
+    S = expert_choice_scores(H) if scores is None else np.asarray(scores, np.float32)
+    P = full_softmax(H).mean(axis=0)
+    C = capacity(capacity_factor, T, k, E)
+    sel = expert_choice_select(S, C)
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    want = np.zeros(T, bool)
+    want[tokens] = True
+
+    xs = np.asarray(x)
+    rows_out = {}
+    for e in range(E):
+        rows = np.arange(sel["offsets"][e], sel["offsets"][e + 1])
+        rows = rows[want[sel["row_token"][rows]]]
+        if rows.size == 0:
+            continue
+        ye = expert_ffn(xs[sel["row_token"][rows]], w1[e], w2[e], act, None if w3 is None else w3[e],
+                        None if b1 is None else b1[e], None if b2 is None else b2[e])
+        for r, v in zip(rows, ye):
+            rows_out[int(r)] = v
+    shared = None
+    if ws1 is not None:
+        shared = np.zeros((len(tokens), d), np.float64)
+        for s_ in range(ws1.shape[0]):
+            shared += expert_ffn(xs[tokens], ws1[s_], ws2[s_], act, None if ws3 is None else ws3[s_])
+    y = expert_choice_combine(d, S, sel["slot"], rows_out, tokens, shared)
+    counts = sel["counts"]
+    f = counts / max(1, counts.sum())
+    covered = (sel["slot"] >= 0).any(axis=1)
+    return {"logits": H, "scores": S, "prob_mean": P, "capacity": C, **sel, "f": f, "P": P,
+            "l_aux": float(E * np.sum(f * P)), "drop_rate": float(1.0 - covered.mean()) if T else 0.0,
+            "experts_per_token": (sel["slot"] >= 0).sum(axis=1), "y": y, "tokens": tokens,
+            "shared": shared}

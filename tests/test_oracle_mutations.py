@@ -13,6 +13,7 @@ from scipy.special import expit
 
 import oracle
 import oracle.moe_oracle as M
+import tests.test_oracle_expert_choice as ecpins
 import tests.test_oracle_pins as pins
 
 ORIG = {n: getattr(M, n) for n in M.__all__}
@@ -106,6 +107,62 @@ def _forward_sparse_P(*a, **kw):
     return out
 
 
+def _ec_ties_high(S32, C):
+    S32 = np.asarray(S32, np.float32)
+    T = S32.shape[0]
+    out = ORIG["expert_choice_select"](S32[::-1].copy(), C)
+    Cp = out["capacity_used"]
+    E = S32.shape[1]
+    rt = (T - 1 - out["row_token"]).reshape(E, Cp) if Cp else out["row_token"].reshape(E, 0)
+    rt = np.sort(rt, axis=1).reshape(-1).astype(np.int32)
+    slot = np.full((T, E), -1, np.int32)
+    for e in range(E):
+        slot[rt[e * Cp:(e + 1) * Cp], e] = e * Cp + np.arange(Cp)
+    out.update(row_token=rt, slot=slot)
+    return out
+
+
+def _ec_softmax_over_tokens(H32):
+    H = np.asarray(H32, np.float64)
+    w = np.exp(H - H.max(axis=0, keepdims=True))
+    return (w / w.sum(axis=0, keepdims=True)).astype(np.float32)
+
+
+def _ec_combine_renormalised(d, S32, slot, rows_out, tokens, shared_out=None):
+    took = slot >= 0
+    S = np.asarray(S32, np.float64) * took
+    tot = S.sum(1, keepdims=True)
+    S = np.divide(S, tot, out=np.zeros_like(S), where=tot > 0)
+    return ORIG["expert_choice_combine"](d, S, slot, rows_out, tokens, shared_out)
+
+
+def _ec_no_clip(S32, C):
+    S32 = np.asarray(S32, np.float32)
+    T, E = S32.shape
+    row_token = np.empty(E * C, np.int32)
+    slot = np.full((T, E), -1, np.int32)
+    for e in range(E):
+        chosen = np.sort(np.argsort(-S32[:, e], kind="stable")[:C])
+        row_token[e * C:(e + 1) * C] = chosen
+        slot[chosen, e] = e * C + np.arange(C)
+    return {"counts": np.full(E, C), "offsets": np.arange(E + 1) * C, "row_token": row_token,
+            "slot": slot, "capacity_used": C}
+
+
+def _ec_rows_in_score_order(S32, C):
+    out = ORIG["expert_choice_select"](S32, C)
+    S32 = np.asarray(S32, np.float32)
+    T, E = S32.shape
+    Cp = out["capacity_used"]
+    rt = out["row_token"].copy()
+    for e in range(E):
+        seg = rt[e * Cp:(e + 1) * Cp]
+        rt[e * Cp:(e + 1) * Cp] = seg[np.argsort(-S32[seg, e], kind="stable")]
+        out["slot"][rt[e * Cp:(e + 1) * Cp], e] = e * Cp + np.arange(Cp)
+    out["row_token"] = rt
+    return out
+
+
 MUTATIONS = {
     "router drops the bias": ("router_logits", _router_no_bias),
     "noise without softplus": ("router_logits", _router_linear_noise),
@@ -123,6 +180,11 @@ MUTATIONS = {
     "f indices reversed": ("balance_stats", _stats_f_swapped),
     "f divided by T, not T*k": ("balance_stats", _stats_f_over_T),
     "P from the sparse gates": ("moe_forward", _forward_sparse_P),
+    "expert choice: ties to the higher token": ("expert_choice_select", _ec_ties_high),
+    "expert choice: softmax over tokens": ("expert_choice_scores", _ec_softmax_over_tokens),
+    "expert choice: gates renormalised": ("expert_choice_combine", _ec_combine_renormalised),
+    "expert choice: capacity not clipped at T": ("expert_choice_select", _ec_no_clip),
+    "expert choice: rows in score order": ("expert_choice_select", _ec_rows_in_score_order),
 }
 
 PIN_TESTS = [
@@ -139,6 +201,15 @@ PIN_TESTS = [
     pins.test_identical_experts_and_drops,
     pins.test_laux_closed_forms,
     pins.test_activations_match_library_forms,
+    ecpins.test_ec_hand_example,
+    ecpins.test_ec_ranks_on_scores_not_logits,
+    ecpins.test_ec_uniform_scores_take_lowest_indices,
+    lambda: ecpins.test_ec_brute_force_with_ties(3, 2),
+    ecpins.test_ec_every_expert_full_and_stats,
+    ecpins.test_ec_full_capacity_identical_experts_is_the_dense_ffn,
+    ecpins.test_ec_single_expert_is_exactly_dense,
+    ecpins.test_ec_partial_coverage_gates_are_raw_scores,
+    ecpins.test_ec_capacity_above_batch_and_zero,
 ]
 
 
