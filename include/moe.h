@@ -64,6 +64,11 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 /* Expert non-linearity: exact-erf GELU, ReLU, or SwiGLU silu(x w1^T) * (x w3^T). */
 typedef enum { MOE_ACT_GELU = 0, MOE_ACT_RELU = 1, MOE_ACT_SWIGLU = 2 } moe_act_t;
 
+/* Who chooses: every token its k best experts (top-k, capacity drops in
+ * arrival order), or every expert its C' best tokens (expert choice,
+ * [MoE&SMS] Advanced Theory & Extensions). */
+typedef enum { MOE_ROUTE_TOKEN_CHOICE = 0, MOE_ROUTE_EXPERT_CHOICE = 1 } moe_routing_t;
+
 typedef struct moe_config {
   int64_t T;                /* tokens in the batch                               */
   int64_t d;                /* model width                                       */
@@ -77,6 +82,7 @@ typedef struct moe_config {
   int32_t ffn_bias;         /* nonzero: b1 [E,h], b2 [E,d] are given             */
   int32_t router_bias;      /* nonzero: b_g [E] is given                         */
   int32_t router_noise;     /* nonzero: w_noise [E,d] and eps [T,E] are given    */
+  int32_t routing;          /* moe_routing_t (0 = token choice)                  */
 } moe_config_t;
 
 /* Device pointers to the layer's parameters (unused ones may be NULL). */
@@ -100,6 +106,8 @@ typedef struct moe_aux {
   int32_t* dest;        /* [T,k]                                              */
   int32_t* row_token;   /* [T*k]                                              */
   float*   stats;       /* [2E+2]                                             */
+  float*   scores;      /* [T,E]   expert choice only                         */
+  int32_t* slot;        /* [T,E]   expert choice only                         */
 } moe_aux_t;
 
 /* (host) Human-readable name of a status code; never NULL. */
@@ -114,7 +122,8 @@ const char* moe_status_string(int status);
 int64_t moe_capacity(const moe_config_t* cfg);
 
 /* (host) Upper bound on the rows any routed expert buffer can hold in total:
- * min(T*k, E*C).  Returns -1 for an invalid config. */
+ * min(T*k, E*C) for token choice, E*min(C, T) (exactly) for expert choice.
+ * Returns -1 for an invalid config. */
 int64_t moe_routed_rows_bound(const moe_config_t* cfg);
 
 /* (host) Workspace bytes that suffice for every entry point below and for
@@ -227,11 +236,49 @@ moe_status_t moe_combine(const moe_config_t* cfg, const float* y_rows,
                          hipStream_t stream);
 
 /*
+ * Expert-choice routing ([MoE&SMS] Advanced Theory & Extensions: every expert
+ * takes the tokens it scores highest, up to its capacity; a token may be
+ * taken by no expert or by several).  cfg->routing must be
+ * MOE_ROUTE_EXPERT_CHOICE.  With C = moe_capacity(cfg) and C' = min(C, T):
+ *   scores[t,e]   softmax over experts of logits[t,:], float32 (written when
+ *                 logits != NULL; with logits == NULL `scores` is an INPUT,
+ *                 e.g. scores computed elsewhere, which this call only ranks)
+ *   expert e takes the C' tokens with the largest float32 score; equal
+ *   scores go to the lower token index
+ *   counts[e] = C'; offsets[e] = e*C' ([E+1])
+ *   row_token[e*C' + i]  the i-th taken token of e, in ascending token order
+ *   slot[t,e]            row of (t, e), or -1 when e did not take t
+ * Exact and deterministic; no workspace.
+ */
+moe_status_t moe_expert_choice(const moe_config_t* cfg, const float* logits, float* scores,
+                               int32_t* counts, int32_t* offsets, int32_t* row_token,
+                               int32_t* slot, hipStream_t stream);
+
+/*
+ * Combine and statistics for expert-choice routing:
+ *   y[t,:] = sum_{s < n_shared} y_shared[s,t,:] + sum_{e ascending, slot[t,e] >= 0}
+ *            scores[t,e] * y_rows[slot[t,e],:]
+ * in float32 in that order, stored in the config dtype; the gate is the raw
+ * score (not renormalised over the experts that took t); a token no expert
+ * took gets the shared part only.
+ *   stats  optional [2E+2]: f[e] = counts[e] / sum(counts), P[e] = prob_sum/T,
+ *          L_aux = E * sum f P, drop_rate = fraction of tokens no expert took
+ */
+moe_status_t moe_combine_expert_choice(const moe_config_t* cfg, const float* y_rows,
+                                       const int32_t* slot, const float* scores,
+                                       const float* y_shared, const int32_t* counts,
+                                       const float* prob_sum, void* y, float* stats,
+                                       hipStream_t stream);
+
+/*
  * The whole layer: moe_route -> moe_dispatch -> grouped FFN over the routed
  * experts and the shared experts -> moe_combine, on one stream, with no host
  * synchronisation.  `logits_in` != NULL replays supplied float32 logits [T,E]
  * instead of computing them (w_g, b_g, w_noise and eps are then unused).
  * `eps` is the [T,E] noise for noisy gating (required when router_noise).
+ * With cfg->routing == MOE_ROUTE_EXPERT_CHOICE the dispatch and combine steps
+ * are moe_expert_choice and moe_combine_expert_choice (aux->topk_idx,
+ * topk_gate and dest are then not written).
  * Intermediates live in `ws` unless `aux` names a buffer for them.
  */
 moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w,

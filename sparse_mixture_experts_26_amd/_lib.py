@@ -18,7 +18,9 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_GELU, MOE_ACT_RELU, MOE_ACT_SWIGLU = 0, 1, 2
+MOE_ROUTE_TOKEN_CHOICE, MOE_ROUTE_EXPERT_CHOICE = 0, 1
 ACT_CODES = {"gelu": MOE_ACT_GELU, "relu": MOE_ACT_RELU, "swiglu": MOE_ACT_SWIGLU}
+ROUTING_CODES = {"token": MOE_ROUTE_TOKEN_CHOICE, "expert": MOE_ROUTE_EXPERT_CHOICE}
 DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16}
 
 
@@ -26,7 +28,7 @@ class MoeConfig(ctypes.Structure):
     _fields_ = [("T", c_int64), ("d", c_int64), ("E", c_int64), ("k", c_int64), ("h", c_int64),
                 ("n_shared", c_int64), ("capacity_factor", c_double), ("act", c_int32),
                 ("dtype", c_int32), ("ffn_bias", c_int32), ("router_bias", c_int32),
-                ("router_noise", c_int32)]
+                ("router_noise", c_int32), ("routing", c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -36,7 +38,8 @@ class MoeWeights(ctypes.Structure):
 
 class MoeAux(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("logits", "topk_idx", "topk_gate", "prob_sum", "counts",
-                                        "offsets", "dest", "row_token", "stats")]
+                                        "offsets", "dest", "row_token", "stats", "scores",
+                                        "slot")]
 
 
 class MoeError(RuntimeError):
@@ -72,6 +75,8 @@ def lib() -> ctypes.CDLL:
             "moe_expert_down": (st, [cfgp, c_int64, vp, vp, c_int64, c_int64, vp, vp, vp, c_int,
                                      vp, c_size_t, vp]),
             "moe_combine": (st, [cfgp] + [vp] * 9),
+            "moe_expert_choice": (st, [cfgp] + [vp] * 7),
+            "moe_combine_expert_choice": (st, [cfgp] + [vp] * 9),
             "moe_layer_forward": (st, [cfgp, POINTER(MoeWeights), vp, vp, vp, vp,
                                        POINTER(MoeAux), vp, c_size_t, vp]),
         }
@@ -84,17 +89,19 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("moe_status_string", "moe_capacity", "moe_routed_rows_bound", "moe_workspace_bytes",
            "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
-           "moe_combine", "moe_layer_forward")
+           "moe_combine", "moe_expert_choice", "moe_combine_expert_choice", "moe_layer_forward")
 
 
 def make_config(T, d, E, k, h, *, act="swiglu", dtype="bf16", capacity_factor=0.0,
-                n_shared=0, ffn_bias=False, router_bias=False, router_noise=False) -> MoeConfig:
+                n_shared=0, ffn_bias=False, router_bias=False, router_noise=False,
+                routing="token") -> MoeConfig:
     return MoeConfig(T=T, d=d, E=E, k=k, h=h, n_shared=n_shared,
                      capacity_factor=float(capacity_factor),
                      act=ACT_CODES.get(act, act) if isinstance(act, str) else act,
                      dtype=DTYPE_CODES.get(dtype, dtype) if isinstance(dtype, str) else dtype,
                      ffn_bias=int(bool(ffn_bias)), router_bias=int(bool(router_bias)),
-                     router_noise=int(bool(router_noise)))
+                     router_noise=int(bool(router_noise)),
+                     routing=ROUTING_CODES.get(routing, routing) if isinstance(routing, str) else routing)
 
 
 def _p(t):
@@ -188,6 +195,19 @@ def moe_combine(cfg, y_rows, dest, topk_gate, y_shared, counts, prob_sum, y, sta
     _check("moe_combine", lib().moe_combine(ctypes.byref(cfg), _p(y_rows), _p(dest),
                                             _p(topk_gate), _p(y_shared), _p(counts),
                                             _p(prob_sum), _p(y), _p(stats), _stream(stream)))
+
+
+def moe_expert_choice(cfg, logits, scores, counts, offsets, row_token, slot, stream=None):
+    _check("moe_expert_choice", lib().moe_expert_choice(
+        ctypes.byref(cfg), _p(logits), _p(scores), _p(counts), _p(offsets), _p(row_token),
+        _p(slot), _stream(stream)))
+
+
+def moe_combine_expert_choice(cfg, y_rows, slot, scores, y_shared, counts, prob_sum, y, stats,
+                              stream=None):
+    _check("moe_combine_expert_choice", lib().moe_combine_expert_choice(
+        ctypes.byref(cfg), _p(y_rows), _p(slot), _p(scores), _p(y_shared), _p(counts),
+        _p(prob_sum), _p(y), _p(stats), _stream(stream)))
 
 
 def moe_layer_forward(cfg, weights: dict, x, eps, logits_in, y, aux: dict | None, ws,

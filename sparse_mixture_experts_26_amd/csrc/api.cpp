@@ -34,8 +34,9 @@ constexpr int64_t kMaxElems = (int64_t)1 << 30;
 struct Cfg {
   int64_t T, d, E, k, h, S;
   int act, bf16;
+  bool ec;        // expert-choice routing
   int64_t C;      // capacity, clamped to T (no expert can receive more)
-  int64_t R;      // routed rows bound min(T*k, E*C)
+  int64_t R;      // routed rows bound: min(T*k, E*C), or E*C for expert choice
   size_t esz;     // bytes per activation / weight element
 };
 
@@ -54,6 +55,8 @@ moe_status_t check_cfg(const moe_config_t* c, Cfg* o) {
   if (c->act < 0 || c->act > 2 || (c->dtype != MOE_F32 && c->dtype != MOE_BF16))
     return MOE_ERR_INVALID_ARGUMENT;
   if (isnan(c->capacity_factor)) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->routing != MOE_ROUTE_TOKEN_CHOICE && c->routing != MOE_ROUTE_EXPERT_CHOICE)
+    return MOE_ERR_INVALID_ARGUMENT;
   if (c->E > 256 || c->k > 8 || c->d % 8 || c->h % 8) return MOE_ERR_UNSUPPORTED;
   if (c->router_noise && c->E > 128) return MOE_ERR_UNSUPPORTED;
   if (c->n_shared > 64) return MOE_ERR_UNSUPPORTED;
@@ -61,8 +64,9 @@ moe_status_t check_cfg(const moe_config_t* c, Cfg* o) {
   o->act = c->act;
   o->bf16 = c->dtype == MOE_BF16;
   o->esz = o->bf16 ? 2 : 4;
+  o->ec = c->routing == MOE_ROUTE_EXPERT_CHOICE;
   o->C = std::min<int64_t>(capacity_of(c), c->T);
-  o->R = std::min<int64_t>(c->T * c->k, c->E * o->C);
+  o->R = o->ec ? c->E * o->C : std::min<int64_t>(c->T * c->k, c->E * o->C);
   const int64_t rows = o->R + o->S * o->T;
   if (o->T * o->k >= kMaxElems || o->T * o->d >= kMaxElems || o->T * o->E >= kMaxElems ||
       rows * std::max(o->d, o->h) >= kMaxElems || o->d * o->h >= kMaxElems)
@@ -113,6 +117,7 @@ moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ER
 struct LayerWs {
   float* logits; int32_t* idx; float* gate; float* prob_sum;
   int32_t* counts; int32_t* offsets; int32_t* dest; int32_t* row_token;
+  float* scores; int32_t* slot;  // expert choice only
   void* hidden; float* y_rows;
   RouteWs rw; DispatchWs dw; FfnWs fw;
 };
@@ -128,7 +133,14 @@ LayerWs carve_layer(Carve& cv, const Cfg& c, const moe_aux_t* aux) {
   w.counts = static_cast<int32_t*>(pick(aux ? aux->counts : nullptr, (size_t)c.E * 4));
   w.offsets = static_cast<int32_t*>(pick(aux ? aux->offsets : nullptr, (size_t)(c.E + 1) * 4));
   w.dest = static_cast<int32_t*>(pick(aux ? aux->dest : nullptr, tk * 4));
-  w.row_token = static_cast<int32_t*>(pick(aux ? aux->row_token : nullptr, tk * 4));
+  w.row_token = static_cast<int32_t*>(
+      pick(aux ? aux->row_token : nullptr, (size_t)std::max<int64_t>(c.R, (int64_t)tk) * 4));
+  w.scores = nullptr;
+  w.slot = nullptr;
+  if (c.ec) {
+    w.scores = static_cast<float*>(pick(aux ? aux->scores : nullptr, (size_t)c.T * c.E * 4));
+    w.slot = static_cast<int32_t*>(pick(aux ? aux->slot : nullptr, (size_t)c.T * c.E * 4));
+  }
   const int64_t rows = c.R + c.S * c.T;
   w.hidden = cv.take((size_t)rows * c.h * c.esz);
   w.y_rows = static_cast<float*>(cv.take((size_t)rows * c.d * 4));
@@ -273,6 +285,7 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx, cons
   moe_status_t st = check_cfg(cfg, &c);
   if (st != MOE_OK) return st;
   if (!topk_idx || !counts || !offsets || !dest || !row_token || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.ec) return MOE_ERR_INVALID_ARGUMENT;
   if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
   const void* ptrs[] = {topk_idx, x, counts, offsets, dest, row_token, x_perm, ws};
   for (const void* q : ptrs)
@@ -369,6 +382,7 @@ moe_status_t moe_combine(const moe_config_t* cfg, const float* y_rows, const int
   moe_status_t st = check_cfg(cfg, &c);
   if (st != MOE_OK) return st;
   if (!y_rows || !dest || !topk_gate || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.ec) return MOE_ERR_INVALID_ARGUMENT;
   if (c.S > 0 && !y_shared) return MOE_ERR_INVALID_ARGUMENT;
   if (stats && (!counts || !prob_sum)) return MOE_ERR_INVALID_ARGUMENT;
   const void* ptrs[] = {y_rows, dest, topk_gate, y_shared, counts, prob_sum, y, stats};
@@ -385,6 +399,50 @@ moe_status_t moe_combine(const moe_config_t* cfg, const float* y_rows, const int
   sp.counts = counts; sp.prob_sum = prob_sum; sp.stats = stats;
   sp.T = (int)c.T; sp.k = (int)c.k; sp.E = (int)c.E; sp.C = (int)c.C;
   return hip_status(launch_stats(sp, stream));
+}
+
+moe_status_t moe_expert_choice(const moe_config_t* cfg, const float* logits, float* scores,
+                               int32_t* counts, int32_t* offsets, int32_t* row_token,
+                               int32_t* slot, hipStream_t stream) {
+  Cfg c;
+  moe_status_t st = check_cfg(cfg, &c);
+  if (st != MOE_OK) return st;
+  if (!c.ec || !scores || !counts || !offsets || !row_token || !slot) return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {logits, scores, counts, offsets, row_token, slot};
+  for (const void* q : ptrs)
+    if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
+  if (c.T == 0) return MOE_OK;
+  EcParams p;
+  p.scores = scores; p.counts = counts; p.offsets = offsets; p.row_token = row_token;
+  p.slot = slot; p.T = (int)c.T; p.E = (int)c.E; p.Cp = (int)c.C;
+  return hip_status(launch_expert_choice(p, logits, stream));
+}
+
+moe_status_t moe_combine_expert_choice(const moe_config_t* cfg, const float* y_rows,
+                                       const int32_t* slot, const float* scores,
+                                       const float* y_shared, const int32_t* counts,
+                                       const float* prob_sum, void* y, float* stats,
+                                       hipStream_t stream) {
+  Cfg c;
+  moe_status_t st = check_cfg(cfg, &c);
+  if (st != MOE_OK) return st;
+  if (!c.ec || !y_rows || !slot || !scores || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.S > 0 && !y_shared) return MOE_ERR_INVALID_ARGUMENT;
+  if (stats && (!counts || !prob_sum)) return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {y_rows, slot, scores, y_shared, counts, prob_sum, y, stats};
+  for (const void* q : ptrs)
+    if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
+  if (c.T == 0) return MOE_OK;
+  EcCombineParams p;
+  p.y_rows = y_rows; p.slot = slot; p.scores = scores;
+  p.y_shared = c.S > 0 ? y_shared : nullptr;
+  p.y = y; p.T = (int)c.T; p.d = (int)c.d; p.E = (int)c.E; p.S = (int)c.S; p.out_bf16 = c.bf16;
+  st = hip_status(launch_combine_ec(p, stream));
+  if (st != MOE_OK || !stats) return st;
+  EcStatsParams sp;
+  sp.counts = counts; sp.prob_sum = prob_sum; sp.slot = slot; sp.stats = stats;
+  sp.T = (int)c.T; sp.E = (int)c.E;
+  return hip_status(launch_stats_ec(sp, stream));
 }
 
 moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
@@ -410,7 +468,8 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
     if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
   if (aux) {
     const void* ap[] = {aux->logits, aux->topk_idx, aux->topk_gate, aux->prob_sum, aux->counts,
-                        aux->offsets, aux->dest, aux->row_token, aux->stats};
+                        aux->offsets, aux->dest, aux->row_token, aux->stats, aux->scores,
+                        aux->slot};
     for (const void* q : ap)
       if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
   }
@@ -435,12 +494,21 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   rp.T = (int)c.T; rp.d = (int)c.d; rp.E = (int)c.E; rp.k = (int)c.k; rp.bf16 = c.bf16;
   if ((st = hip_status(launch_route(rp, stream))) != MOE_OK) return st;
 
-  // 3. counts, capacity, dispatch tables
-  DispatchParams dp;
-  dp.idx = L.idx; dp.counts = L.counts; dp.offsets = L.offsets; dp.dest = L.dest;
-  dp.row_token = L.row_token; dp.local_rank = L.dw.local_rank; dp.chunk_hist = L.dw.chunk_hist;
-  dp.n = (int)(c.T * c.k); dp.k = (int)c.k; dp.E = (int)c.E; dp.C = (int)c.C;
-  if ((st = hip_status(launch_dispatch(dp, stream))) != MOE_OK) return st;
+  // 3. counts, capacity, dispatch tables (expert choice: every expert takes
+  //    its best tokens)
+  if (c.ec) {
+    EcParams ep;
+    ep.scores = L.scores; ep.counts = L.counts; ep.offsets = L.offsets;
+    ep.row_token = L.row_token; ep.slot = L.slot;
+    ep.T = (int)c.T; ep.E = (int)c.E; ep.Cp = (int)c.C;
+    if ((st = hip_status(launch_expert_choice(ep, rp.logits, stream))) != MOE_OK) return st;
+  } else {
+    DispatchParams dp;
+    dp.idx = L.idx; dp.counts = L.counts; dp.offsets = L.offsets; dp.dest = L.dest;
+    dp.row_token = L.row_token; dp.local_rank = L.dw.local_rank; dp.chunk_hist = L.dw.chunk_hist;
+    dp.n = (int)(c.T * c.k); dp.k = (int)c.k; dp.E = (int)c.E; dp.C = (int)c.C;
+    if ((st = hip_status(launch_dispatch(dp, stream))) != MOE_OK) return st;
+  }
 
   // 4. grouped expert FFN: routed groups gathered through row_token, then the
   //    shared experts over all tokens, in one launch per projection
@@ -462,6 +530,21 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   if ((st = hip_status(launch_ffn(dn, stream))) != MOE_OK) return st;
 
   // 5. combine (+ statistics)
+  if (c.ec) {
+    EcCombineParams cp;
+    cp.y_rows = L.y_rows; cp.slot = L.slot; cp.scores = L.scores;
+    cp.y_shared = c.S > 0 ? L.y_rows + (size_t)c.R * c.d : nullptr;
+    cp.y = y; cp.T = (int)c.T; cp.d = (int)c.d; cp.E = (int)c.E; cp.S = (int)c.S;
+    cp.out_bf16 = c.bf16;
+    if ((st = hip_status(launch_combine_ec(cp, stream))) != MOE_OK) return st;
+    if (aux && aux->stats) {
+      EcStatsParams sp;
+      sp.counts = L.counts; sp.prob_sum = L.prob_sum; sp.slot = L.slot; sp.stats = aux->stats;
+      sp.T = (int)c.T; sp.E = (int)c.E;
+      if ((st = hip_status(launch_stats_ec(sp, stream))) != MOE_OK) return st;
+    }
+    return MOE_OK;
+  }
   CombineParams cp;
   cp.y_rows = L.y_rows; cp.dest = L.dest; cp.gate = L.gate;
   cp.y_shared = c.S > 0 ? L.y_rows + (size_t)c.R * c.d : nullptr;

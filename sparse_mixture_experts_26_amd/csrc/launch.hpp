@@ -79,6 +79,38 @@ struct FfnParams {
 int64_t ffn_max_entries(int64_t rows_bound, int G, int S, int T);
 hipError_t launch_ffn(const FfnParams& p, hipStream_t stream);
 
+// ---- expert-choice routing ---------------------------------------------------------
+struct EcParams {
+  float* scores;             // [T,E]: written from logits, or given (replay)
+  int32_t* counts;           // [E]   = Cp
+  int32_t* offsets;          // [E+1] = e * Cp
+  int32_t* row_token;        // [E*Cp]
+  int32_t* slot;             // [T,E] row of (t, e) or -1
+  int T, E, Cp;              // Cp = min(C, T)
+};
+// logits != null: scores = softmax(logits) first; then the selection.
+hipError_t launch_expert_choice(const EcParams& p, const float* logits, hipStream_t stream);
+
+struct EcCombineParams {
+  const float* y_rows;       // [E*Cp (+S*T), d]
+  const int32_t* slot;       // [T,E]
+  const float* scores;       // [T,E]
+  const float* y_shared;     // [S,T,d] or null
+  void* y;                   // [T,d]
+  int T, d, E, S;
+  int out_bf16;
+};
+hipError_t launch_combine_ec(const EcCombineParams& p, hipStream_t stream);
+
+struct EcStatsParams {
+  const int32_t* counts;     // [E]
+  const float* prob_sum;     // [E]
+  const int32_t* slot;       // [T,E]
+  float* stats;              // [2E+2]
+  int T, E;
+};
+hipError_t launch_stats_ec(const EcStatsParams& p, hipStream_t stream);
+
 // ---- combine -------------------------------------------------------------------
 struct CombineParams {
   const float* y_rows;       // [*, d]

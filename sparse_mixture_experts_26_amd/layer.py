@@ -15,11 +15,13 @@ WEIGHT_NAMES = ("w_g", "b_g", "w_noise", "w1", "w3", "w2", "b1", "b2", "ws1", "w
 
 def config_of(spec) -> L.MoeConfig:
     """MoeConfig from any object with the layer-shape attributes (T, d, E, k, h,
-    act, dtype, capacity_factor, n_shared, ffn_bias, router_bias, router_noise)."""
+    act, dtype, capacity_factor, n_shared, ffn_bias, router_bias, router_noise,
+    and optionally routing: "token" or "expert")."""
     return L.make_config(spec.T, spec.d, spec.E, spec.k, spec.h, act=spec.act, dtype=spec.dtype,
                          capacity_factor=spec.capacity_factor, n_shared=spec.n_shared,
                          ffn_bias=spec.ffn_bias, router_bias=spec.router_bias != "none",
-                         router_noise=spec.router_noise)
+                         router_noise=spec.router_noise,
+                         routing=getattr(spec, "routing", "token"))
 
 
 class MoeLayer:
@@ -33,6 +35,7 @@ class MoeLayer:
         self.capacity = L.moe_capacity(c)
         self.rows_bound = L.moe_routed_rows_bound(c)
         self.group_bound = min(T, self.capacity)
+        self.ec = c.routing == L.MOE_ROUTE_EXPERT_CHOICE
         dev = self.device
         self.ws = torch.empty(max(L.moe_workspace_bytes(c), 256), dtype=torch.uint8, device=dev)
         out_dtype = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
@@ -47,9 +50,12 @@ class MoeLayer:
             "counts": torch.empty((E,), **i32),
             "offsets": torch.empty((E + 1,), **i32),
             "dest": torch.empty((T, k), **i32),
-            "row_token": torch.empty((max(T * k, 1),), **i32),
+            "row_token": torch.empty((max(T * k, self.rows_bound, 1),), **i32),
             "stats": torch.empty((2 * E + 2,), **f32),
         }
+        if self.ec:
+            self.out["scores"] = torch.empty((T, E), **f32)
+            self.out["slot"] = torch.empty((T, E), **i32)
         rows = self.rows_bound + S * T
         self.hidden = torch.empty((max(rows, 1), h), dtype=out_dtype, device=dev)
         self.y_rows = torch.empty((max(rows, 1), d), **f32)
@@ -57,16 +63,18 @@ class MoeLayer:
     def forward(self, x, eps=None, logits_in=None, stream=None):
         """moe_layer_forward with every auxiliary output captured."""
         aux = {n: self.out[n] for n in ("logits", "topk_idx", "topk_gate", "prob_sum", "counts",
-                                        "offsets", "dest", "row_token", "stats")}
+                                        "offsets", "dest", "row_token", "stats", "scores", "slot")
+               if n in self.out}
         if logits_in is not None:
             aux.pop("logits")
         L.moe_layer_forward(self.cfg, self.w, x, eps, logits_in, self.out["y"], aux, self.ws,
                             stream)
         return self.out
 
-    def staged(self, x, eps=None, logits_in=None, stream=None, between=None):
+    def staged(self, x, eps=None, logits_in=None, stream=None, between=None, scores_in=None):
         """The same layer through the five stage entry points; ``between(name)``
-        is called after each stage is enqueued (for event timing)."""
+        is called after each stage is enqueued (for event timing).  With
+        expert-choice routing, ``scores_in`` replays float32 scores [T,E]."""
         c, o, w = self.cfg, self.out, self.w
         T, d, S = c.T, c.d, c.n_shared
         tick = between or (lambda name: None)
@@ -78,8 +86,14 @@ class MoeLayer:
             L.moe_route(c, x, w["w_g"], w["b_g"], w["w_noise"], eps, o["logits"], o["topk_idx"],
                         o["topk_gate"], o["prob_sum"], self.ws, stream)
         tick("route")
-        L.moe_dispatch(c, o["topk_idx"], None, o["counts"], o["offsets"], o["dest"],
-                       o["row_token"], None, self.ws, stream)
+        if self.ec:
+            if scores_in is not None:
+                o["scores"].copy_(scores_in)
+            L.moe_expert_choice(c, None if scores_in is not None else o["logits"], o["scores"],
+                                o["counts"], o["offsets"], o["row_token"], o["slot"], stream)
+        else:
+            L.moe_dispatch(c, o["topk_idx"], None, o["counts"], o["offsets"], o["dest"],
+                           o["row_token"], None, self.ws, stream)
         tick("dispatch")
         R = self.rows_bound
         L.moe_expert_up(c, c.E, x, o["row_token"], o["offsets"], R, self.group_bound, w["w1"],
@@ -98,8 +112,12 @@ class MoeLayer:
                 L.moe_expert_down(c, 1, self.hidden[R:], off, T, T, w["ws2"][s], None,
                                   y_shared[s * T:(s + 1) * T], 0, self.ws, stream)
             tick("shared")
-        L.moe_combine(c, self.y_rows, o["dest"], o["topk_gate"], y_shared, o["counts"],
-                      o["prob_sum"], o["y"], o["stats"], stream)
+        if self.ec:
+            L.moe_combine_expert_choice(c, self.y_rows, o["slot"], o["scores"], y_shared,
+                                        o["counts"], o["prob_sum"], o["y"], o["stats"], stream)
+        else:
+            L.moe_combine(c, self.y_rows, o["dest"], o["topk_gate"], y_shared, o["counts"],
+                          o["prob_sum"], o["y"], o["stats"], stream)
         tick("combine")
         return o
 

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     assert set(names) == set(M.EXPORTS)
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
@@ -71,6 +71,11 @@ def test_capacity_matches_formula_and_oracle():
     assert M.moe_capacity(M.make_config(10, 8, 4, 1, 8, capacity_factor=0.01)) == 0
     assert M.moe_routed_rows_bound(config_of(FULL["finegrained_shared"])) == 98304
     assert M.moe_routed_rows_bound(config_of(FULL["switch_top1"])) == 4096
+    # expert choice: exactly E * min(C, T) rows
+    assert M.moe_capacity(config_of(FULL["mixtral_prefill_ec"])) == 2048
+    assert M.moe_routed_rows_bound(config_of(FULL["mixtral_prefill_ec"])) == 8 * 2048
+    assert M.moe_routed_rows_bound(M.make_config(10, 8, 4, 1, 8, capacity_factor=9.0,
+                                                 routing="expert")) == 4 * 10
 
 
 def test_workspace_bytes():
@@ -110,6 +115,34 @@ def test_config_validation_statuses():
     assert _route(ok, ws_bytes=16) == M.MOE_ERR_WORKSPACE_TOO_SMALL
     assert _route(M.make_config(0, 64, 4, 2, 128)) == M.MOE_OK                      # empty batch
     assert _route(M.make_config(0, 64, 4, 2, 128), x=None, w_g=None) == M.MOE_OK      # replay form
+    assert _route(M.make_config(64, 64, 4, 2, 128, routing=2)) == M.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_expert_choice_validation_statuses():
+    L = _lib.lib()
+    tc = M.make_config(64, 64, 4, 2, 128, act="gelu")
+    ec = M.make_config(64, 64, 4, 2, 128, act="gelu", capacity_factor=1.0, routing="expert")
+    # the expert-choice calls need an expert-choice config, and the token-choice
+    # dispatch / combine refuse one
+    assert L.moe_expert_choice(ctypes.byref(tc), P[0], P[1], P[2], P[3], P[4], P[5], None) \
+        == M.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_choice(ctypes.byref(ec), P[0], None, P[2], P[3], P[4], P[5], None) \
+        == M.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_expert_choice(ctypes.byref(ec), P[0] + 4, P[1], P[2], P[3], P[4], P[5], None) \
+        == M.MOE_ERR_UNSUPPORTED
+    assert L.moe_dispatch(ctypes.byref(ec), P[0], None, P[2], P[3], P[4], P[5], None, P[6],
+                          1 << 30, None) == M.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_combine(ctypes.byref(ec), P[0], P[1], P[2], None, P[3], P[4], P[5], None,
+                         None) == M.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_combine_expert_choice(ctypes.byref(tc), P[0], P[1], P[2], None, P[3], P[4],
+                                       P[5], None, None) == M.MOE_ERR_INVALID_ARGUMENT
+    ec2 = M.make_config(64, 64, 4, 2, 128, n_shared=1, capacity_factor=1.0, routing="expert")
+    assert L.moe_combine_expert_choice(ctypes.byref(ec2), P[0], P[1], P[2], None, P[3], P[4],
+                                       P[5], None, None) == M.MOE_ERR_INVALID_ARGUMENT
+    # empty batch: nothing to do
+    e0 = M.make_config(0, 64, 4, 2, 128, capacity_factor=1.0, routing="expert")
+    assert L.moe_expert_choice(ctypes.byref(e0), None, P[1], P[2], P[3], P[4], P[5], None) \
+        == M.MOE_OK
 
 
 def test_stage_validation_statuses():

@@ -35,6 +35,7 @@ class LayerConfig:
     x_std: float = 1.0
     w_std: float = 0.02
     b_std: float = 0.02          # std of b1/b2 where ffn_bias is set
+    routing: str = "token"       # "token": top-k per token; "expert": top-C' per expert
 
     @property
     def dropless(self) -> bool:
@@ -68,7 +69,13 @@ FINEGRAINED = LayerConfig(
     name="finegrained_shared", cfg_id=5, T=16384, d=2048, E=64, k=6, h=1408, act="swiglu",
     capacity_factor=1.25, dtype="bf16", n_shared=2, router_bias="zipf", zipf_s=1.1)
 
-FULL = {c.name: c for c in (TOY, SWITCH, DECODE, PREFILL, FINEGRAINED)}
+# Expert-choice routing on the Mixtral prefill shape: capacity factor 1.0
+# gives every expert C = T*k/E = 2048 tokens (the same rows as top-2 on
+# average, now perfectly balanced).
+PREFILL_EC = PREFILL.with_(name="mixtral_prefill_ec", cfg_id=6, capacity_factor=1.0,
+                           routing="expert")
+
+FULL = {c.name: c for c in (TOY, SWITCH, DECODE, PREFILL, FINEGRAINED, PREFILL_EC)}
 
 # Reduced variants: same structure (act, k, noise, bias kind, shared experts,
 # capacity regime), sizes small enough for the CPU oracle to finish in seconds,
@@ -83,6 +90,11 @@ SMALL = {
                                    h=704),
     "finegrained_small": FINEGRAINED.with_(name="finegrained_small", cfg_id=105, T=1500,
                                            d=256, E=16, k=4, h=192, n_shared=2),
+    "prefill_ec_small": PREFILL_EC.with_(name="prefill_ec_small", cfg_id=106, T=777, d=384,
+                                         E=8, h=704),
+    "finegrained_ec_small": FINEGRAINED.with_(name="finegrained_ec_small", cfg_id=107, T=1500,
+                                              d=256, E=16, k=4, h=192, n_shared=2,
+                                              routing="expert"),
 }
 
 
