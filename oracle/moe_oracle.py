@@ -58,6 +58,15 @@ the tie rule; the readings:
   EC6 f_i = rows of expert i / all rows (1/E here), P and L_aux as in R5, and
       the drop rate is the fraction of tokens that no expert took.
 
+Router z-loss and routing diagnostics ([MoE&SMS] "Advanced Theory &
+Extensions": a z-loss keeps router logits from growing large; "Benchmark
+Datasets & Evaluation": utilisation histograms, routing entropy and the
+fraction of tokens dropped; [MoEM] Level 3: overflow, imbalance measure).
+The pages give no z-loss formula; the reading:
+  Z1 z-loss = mean over tokens of (log sum_e exp H[t,e])^2, alpha = 1, on the
+     float32 logits; routing entropy = mean over tokens of -sum_e p log p of
+     the full softmax, in nats.
+
 Layouts (row-major, every weight in out x in form, as an nn.Linear stores it):
   x [T,d]; w_g, w_noise [E,d]; b_g [E]; eps [T,E]; w1, w3 [E,h,d]; w2 [E,d,h];
   b1 [E,h]; b2 [E,d]; ws1, ws3 [S,h,d]; ws2 [S,d,h].
@@ -75,7 +84,7 @@ __all__ = [
     "full_softmax", "capacity", "dispatch_in_arrival_order", "dispatch",
     "activation", "expert_ffn", "combine", "balance_stats", "moe_forward",
     "overflow_record", "expert_choice_scores", "expert_choice_select",
-    "expert_choice_combine", "moe_forward_expert_choice",
+    "expert_choice_combine", "moe_forward_expert_choice", "routing_diagnostics",
 ]
 
 
@@ -455,3 +464,31 @@ def moe_forward_expert_choice(x, w_g, w1, w2, *, k: int, act: str, capacity_fact
             "l_aux": float(E * np.sum(f * P)), "drop_rate": float(1.0 - covered.mean()) if T else 0.0,
             "experts_per_token": (sel["slot"] >= 0).sum(axis=1), "y": y, "tokens": tokens,
             "shared": shared}
+
+
+def routing_diagnostics(H32, counts, kept, dest, C: int, T: int, k: int, E: int) -> dict:
+    """Router z-loss (Z1) and routing diagnostics of one token-choice batch:
+    routing entropy, imbalance (load CV, absolute deviation from the equal
+    share, peak-to-mean load), overflow per expert, utilisation kept / C, and
+    the fractions of tokens that lost all or some of their k assignments."""
+    H = np.asarray(H32, np.float64)
+    m = H.max(axis=1, keepdims=True)
+    lse = (m + np.log(np.exp(H - m).sum(axis=1, keepdims=True)))[:, 0]
+    p = full_softmax(H32)
+    ent = lse - (p * H).sum(axis=1)  # -sum p log p with log p = H - lse
+    counts = np.asarray(counts, np.float64)
+    kept = np.asarray(kept, np.float64)
+    lost = (np.asarray(dest) < 0).sum(axis=1)
+    mean = counts.mean()
+    return {
+        "z_loss": float(np.mean(lse ** 2)),
+        "entropy": float(np.mean(ent)),
+        "load_cv": float(counts.std() / mean) if mean > 0 else 0.0,
+        "deviation": float(np.abs(counts - T * k / E).sum()),
+        "peak_to_mean": float(counts.max() / mean) if mean > 0 else 0.0,
+        "overflow": counts - kept,
+        "overflow_total": float((counts - kept).sum()),
+        "utilisation": kept / C if C > 0 else np.zeros(E),
+        "tokens_fully_dropped": float(np.mean(lost == k)),
+        "tokens_partly_dropped": float(np.mean((lost > 0) & (lost < k))),
+    }

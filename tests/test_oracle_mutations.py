@@ -163,6 +163,27 @@ def _ec_rows_in_score_order(S32, C):
     return out
 
 
+def _diag_z_unsquared(H32, counts, kept, dest, C, T, k, E):
+    d = ORIG["routing_diagnostics"](H32, counts, kept, dest, C, T, k, E)
+    H = np.asarray(H32, np.float64)
+    m = H.max(axis=1, keepdims=True)
+    d["z_loss"] = float(np.mean(m[:, 0] + np.log(np.exp(H - m).sum(axis=1))))
+    return d
+
+
+def _diag_entropy_bits(H32, counts, kept, dest, C, T, k, E):
+    d = ORIG["routing_diagnostics"](H32, counts, kept, dest, C, T, k, E)
+    d["entropy"] = d["entropy"] / math.log(2.0)
+    return d
+
+
+def _diag_any_loss_is_full(H32, counts, kept, dest, C, T, k, E):
+    d = ORIG["routing_diagnostics"](H32, counts, kept, dest, C, T, k, E)
+    lost = (np.asarray(dest) < 0).sum(axis=1)
+    d["tokens_fully_dropped"] = float(np.mean(lost > 0))
+    return d
+
+
 MUTATIONS = {
     "router drops the bias": ("router_logits", _router_no_bias),
     "noise without softplus": ("router_logits", _router_linear_noise),
@@ -185,6 +206,9 @@ MUTATIONS = {
     "expert choice: gates renormalised": ("expert_choice_combine", _ec_combine_renormalised),
     "expert choice: capacity not clipped at T": ("expert_choice_select", _ec_no_clip),
     "expert choice: rows in score order": ("expert_choice_select", _ec_rows_in_score_order),
+    "z-loss not squared": ("routing_diagnostics", _diag_z_unsquared),
+    "entropy in bits": ("routing_diagnostics", _diag_entropy_bits),
+    "a partial drop counted as a full one": ("routing_diagnostics", _diag_any_loss_is_full),
 }
 
 PIN_TESTS = [
@@ -210,6 +234,9 @@ PIN_TESTS = [
     ecpins.test_ec_single_expert_is_exactly_dense,
     ecpins.test_ec_partial_coverage_gates_are_raw_scores,
     ecpins.test_ec_capacity_above_batch_and_zero,
+    pins.test_zloss_and_entropy_closed_forms,
+    pins.test_diagnostics_on_the_capacity_worked_example,
+    pins.test_diagnostics_partial_drops_with_two_slots,
 ]
 
 

@@ -421,3 +421,65 @@ def test_small_configs_route_as_designed():
             assert drops == 0, name
         elif name != "toy_fp32":
             assert drops > 0, name
+
+
+# --- router z-loss and routing diagnostics --------------------------------------
+
+def _diag(H, idx_or_assign, C, k):
+    H = np.asarray(H, np.float32)
+    T, E = H.shape
+    idx = np.asarray(idx_or_assign, np.int32).reshape(T, k)
+    disp = O.dispatch(idx, E, C)
+    return O.routing_diagnostics(H, disp["counts"], disp["kept"], disp["dest"], C, T, k, E)
+
+
+def test_zloss_and_entropy_closed_forms():
+    """Z1 on logits whose log-partition and entropy are known in closed form."""
+    T, E = 5, 8
+    d = _diag(np.zeros((T, E)), np.zeros((T, 1)), T, 1)
+    assert d["z_loss"] == pytest.approx(math.log(E) ** 2, rel=1e-12)
+    assert d["entropy"] == pytest.approx(math.log(E), rel=1e-12)   # uniform router
+    d = _diag(np.full((T, E), 3.0), np.zeros((T, 1)), T, 1)
+    assert d["z_loss"] == pytest.approx((3.0 + math.log(E)) ** 2, rel=1e-12)
+    # two experts: entropy of a Bernoulli(sigmoid(a - b)); log-partition log(e^a + e^b)
+    a, b = 1.5, -0.5
+    q = 1 / (1 + math.exp(-(a - b)))
+    d = _diag([[a, b]], [[0]], 1, 1)
+    assert d["entropy"] == pytest.approx(-(q * math.log(q) + (1 - q) * math.log(1 - q)), rel=1e-12)
+    assert d["z_loss"] == pytest.approx(math.log(math.exp(a) + math.exp(b)) ** 2, rel=1e-12)
+    # one expert: the log-partition is the logit itself
+    h = np.array([[0.5], [-2.0], [4.0]])
+    d = _diag(h, np.zeros((3, 1)), 3, 1)
+    assert d["z_loss"] == pytest.approx(np.mean(h ** 2), rel=1e-12)
+    assert d["entropy"] == 0.0
+    # a nearly one-hot router has almost no entropy
+    d = _diag([[40.0, 0.0, 0.0]], [[0]], 1, 1)
+    assert d["entropy"] < 1e-15
+
+
+def test_diagnostics_on_the_capacity_worked_example():
+    """'Mixture-of-experts Models', Level 2: assignments [0,0,0,1,1,2,3,3] with
+    capacity 2 overflow expert 0 by one (printed [1 0 0 0]); that token loses
+    its only assignment."""
+    g = golden("capacity_worked_example.json")
+    a = np.array(g["assignments"])
+    H = np.zeros((a.size, 4), np.float32)
+    d = _diag(H, a[:, None], g["capacity"], 1)
+    assert d["overflow"].tolist() == g["printed_overflow"]
+    assert d["overflow_total"] == 1
+    assert d["utilisation"].tolist() == [1.0, 1.0, 0.5, 1.0]
+    assert d["tokens_fully_dropped"] == 1 / 8 and d["tokens_partly_dropped"] == 0.0
+    assert d["peak_to_mean"] == 3 / 2
+    assert d["deviation"] == 1 + 0 + 1 + 0        # |3-2| + |2-2| + |1-2| + |2-2|
+
+
+def test_diagnostics_partial_drops_with_two_slots():
+    # k = 2, E = 2, C = 1: token 0 keeps both slots, token 1 loses both
+    H = np.array([[1.0, 0.0], [1.0, 0.0]], np.float32)
+    d = _diag(H, [[0, 1], [0, 1]], 1, 2)
+    assert d["tokens_fully_dropped"] == 0.5 and d["tokens_partly_dropped"] == 0.0
+    # C = 1, E = 3, k = 2 in arrival order: token 0 keeps experts 0 and 1,
+    # token 1 finds expert 1 full and keeps 2, token 2 finds 2 and 0 full
+    H = np.zeros((3, 3), np.float32)
+    d = _diag(H, [[0, 1], [1, 2], [2, 0]], 1, 2)
+    assert d["tokens_partly_dropped"] == 1 / 3 and d["tokens_fully_dropped"] == 1 / 3
