@@ -9,7 +9,8 @@ entry points on torch's current stream.  Prints ONE JSON line.
 
 Workloads: mixtral_prefill (default; the MFMA-bound Mixtral-shaped prefill,
 T=8192, d=4096, 8 experts top-2, SwiGLU h=14336), mixtral_decode, switch_top1,
-finegrained_shared, toy_fp32.
+finegrained_shared, toy_fp32, mixtral_prefill_ec (the prefill shape with
+expert-choice routing).
 """
 from __future__ import annotations
 
@@ -200,6 +201,12 @@ def main():
     out = layer.out
     counts = out["counts"].cpu().numpy()
     stats = out["stats"].cpu().numpy()
+    diag = None
+    if not layer.ec:  # router z-loss and entropy of the last step's routing (untimed)
+        from sparse_mixture_experts_26_amd import _lib as L
+        d = torch.empty((8 + 2 * cfg.E,), dtype=torch.float32, device="cuda")
+        L.moe_router_diagnostics(layer.cfg, out["logits"], out["counts"], out["dest"], d, layer.ws)
+        diag = d.cpu().numpy()
     work = algorithmic_work(cfg, counts, layer.capacity)
     kernel = "ffn_f32" if cfg.dtype == "f32" else (
         "ffn_skinny" if layer.group_bound <= 32 and (cfg.n_shared == 0 or cfg.T <= 32) else "ffn_tiled")
@@ -245,7 +252,10 @@ def main():
         "routing": {"kept_rows": work["kept_rows"], "active_experts": work["active_experts"],
                     "drop_rate": round(float(stats[2 * E + 1]), 5),
                     "l_aux": round(float(stats[2 * E]), 5),
-                    "load_cv": round(float(counts.std() / counts.mean()), 4)},
+                    "load_cv": round(float(counts.std() / counts.mean()), 4),
+                    **({} if diag is None else {"z_loss": round(float(diag[0]), 4),
+                                                "entropy_nats": round(float(diag[1]), 4),
+                                                "tokens_fully_dropped": round(float(diag[6]), 5)})},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

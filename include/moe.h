@@ -108,6 +108,7 @@ typedef struct moe_aux {
   float*   stats;       /* [2E+2]                                             */
   float*   scores;      /* [T,E]   expert choice only                         */
   int32_t* slot;        /* [T,E]   expert choice only                         */
+  float*   diag;        /* [8+2E]  token choice only: moe_router_diagnostics  */
 } moe_aux_t;
 
 /* (host) Human-readable name of a status code; never NULL. */
@@ -236,6 +237,32 @@ moe_status_t moe_combine(const moe_config_t* cfg, const float* y_rows,
                          hipStream_t stream);
 
 /*
+ * Router z-loss and routing diagnostics of a token-choice batch ([MoE&SMS]
+ * Advanced Theory & Extensions: a z-loss keeps router logits small; Benchmark
+ * Datasets & Evaluation: utilisation, routing entropy, fraction of tokens
+ * dropped; [MoEM] Level 3: overflow and an imbalance measure).  The pages give
+ * no z-loss formula; the one used is the mean squared log-partition.
+ *   logits [T,E] float32; counts [E] and dest [T,k] as moe_dispatch wrote them
+ *   diag   [8 + 2E] float32:
+ *     [0] z-loss  mean_t (log sum_e exp logits[t,e])^2   (alpha = 1)
+ *     [1] routing entropy  mean_t -sum_e p log p, p = softmax(logits[t]), nats
+ *     [2] load coefficient of variation  std(counts)/mean(counts), population
+ *     [3] absolute deviation from the equal share  sum_e |counts[e] - T*k/E|
+ *     [4] peak-to-mean load  max(counts)/mean(counts)
+ *     [5] assignments over capacity  sum_e max(counts[e] - C, 0)
+ *     [6] fraction of tokens all of whose k assignments were dropped
+ *     [7] fraction of tokens that lost some but not all of them
+ *     [8 .. 8+E)     assignments over capacity per expert
+ *     [8+E .. 8+2E)  utilisation min(counts[e], C) / C (0 when C = 0)
+ * Token choice only (expert choice reports its uncovered tokens in the
+ * statistics of moe_combine_expert_choice).  Deterministic.  Workspace: at
+ * least moe_workspace_bytes(cfg).
+ */
+moe_status_t moe_router_diagnostics(const moe_config_t* cfg, const float* logits,
+                                    const int32_t* counts, const int32_t* dest, float* diag,
+                                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Expert-choice routing ([MoE&SMS] Advanced Theory & Extensions: every expert
  * takes the tokens it scores highest, up to its capacity; a token may be
  * taken by no expert or by several).  cfg->routing must be
@@ -278,7 +305,8 @@ moe_status_t moe_combine_expert_choice(const moe_config_t* cfg, const float* y_r
  * `eps` is the [T,E] noise for noisy gating (required when router_noise).
  * With cfg->routing == MOE_ROUTE_EXPERT_CHOICE the dispatch and combine steps
  * are moe_expert_choice and moe_combine_expert_choice (aux->topk_idx,
- * topk_gate and dest are then not written).
+ * topk_gate, dest and diag are then not written).  With token choice,
+ * aux->diag != NULL also runs moe_router_diagnostics on the layer's routing.
  * Intermediates live in `ws` unless `aux` names a buffer for them.
  */
 moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w,

@@ -39,7 +39,7 @@ class MoeWeights(ctypes.Structure):
 class MoeAux(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("logits", "topk_idx", "topk_gate", "prob_sum", "counts",
                                         "offsets", "dest", "row_token", "stats", "scores",
-                                        "slot")]
+                                        "slot", "diag")]
 
 
 class MoeError(RuntimeError):
@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
             "moe_expert_down": (st, [cfgp, c_int64, vp, vp, c_int64, c_int64, vp, vp, vp, c_int,
                                      vp, c_size_t, vp]),
             "moe_combine": (st, [cfgp] + [vp] * 9),
+            "moe_router_diagnostics": (st, [cfgp] + [vp] * 5 + [c_size_t, vp]),
             "moe_expert_choice": (st, [cfgp] + [vp] * 7),
             "moe_combine_expert_choice": (st, [cfgp] + [vp] * 9),
             "moe_layer_forward": (st, [cfgp, POINTER(MoeWeights), vp, vp, vp, vp,
@@ -89,7 +90,8 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("moe_status_string", "moe_capacity", "moe_routed_rows_bound", "moe_workspace_bytes",
            "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
-           "moe_combine", "moe_expert_choice", "moe_combine_expert_choice", "moe_layer_forward")
+           "moe_combine", "moe_router_diagnostics", "moe_expert_choice", "moe_combine_expert_choice",
+           "moe_layer_forward")
 
 
 def make_config(T, d, E, k, h, *, act="swiglu", dtype="bf16", capacity_factor=0.0,
@@ -195,6 +197,12 @@ def moe_combine(cfg, y_rows, dest, topk_gate, y_shared, counts, prob_sum, y, sta
     _check("moe_combine", lib().moe_combine(ctypes.byref(cfg), _p(y_rows), _p(dest),
                                             _p(topk_gate), _p(y_shared), _p(counts),
                                             _p(prob_sum), _p(y), _p(stats), _stream(stream)))
+
+
+def moe_router_diagnostics(cfg, logits, counts, dest, diag, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check("moe_router_diagnostics", lib().moe_router_diagnostics(
+        ctypes.byref(cfg), _p(logits), _p(counts), _p(dest), _p(diag), wp, wn, _stream(stream)))
 
 
 def moe_expert_choice(cfg, logits, scores, counts, offsets, row_token, slot, stream=None):

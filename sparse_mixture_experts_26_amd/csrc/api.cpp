@@ -93,6 +93,7 @@ struct Carve {
 struct RouteWs { float* prob_partial; };
 struct DispatchWs { int32_t* local_rank; int32_t* chunk_hist; };
 struct FfnWs { TileEntry* entries; int32_t* n_entries; };
+struct DiagWs { double* partial_d; int32_t* partial_i; };
 
 RouteWs carve_route(Carve& cv, const Cfg& c) {
   return {static_cast<float*>(cv.take((size_t)route_blocks(c.T) * c.E * 4))};
@@ -101,6 +102,12 @@ DispatchWs carve_dispatch(Carve& cv, const Cfg& c) {
   DispatchWs w;
   w.local_rank = static_cast<int32_t*>(cv.take((size_t)c.T * c.k * 4));
   w.chunk_hist = static_cast<int32_t*>(cv.take((size_t)dispatch_chunks(c.T * c.k) * c.E * 4));
+  return w;
+}
+DiagWs carve_diag(Carve& cv, const Cfg& c) {
+  DiagWs w;
+  w.partial_d = static_cast<double*>(cv.take((size_t)diag_blocks(c.T) * 2 * sizeof(double)));
+  w.partial_i = static_cast<int32_t*>(cv.take((size_t)diag_blocks(c.T) * 2 * sizeof(int32_t)));
   return w;
 }
 FfnWs carve_ffn(Carve& cv, int64_t rows_bound, int64_t groups, int64_t S, int64_t T) {
@@ -119,7 +126,7 @@ struct LayerWs {
   int32_t* counts; int32_t* offsets; int32_t* dest; int32_t* row_token;
   float* scores; int32_t* slot;  // expert choice only
   void* hidden; float* y_rows;
-  RouteWs rw; DispatchWs dw; FfnWs fw;
+  RouteWs rw; DispatchWs dw; FfnWs fw; DiagWs gw;
 };
 
 LayerWs carve_layer(Carve& cv, const Cfg& c, const moe_aux_t* aux) {
@@ -147,6 +154,7 @@ LayerWs carve_layer(Carve& cv, const Cfg& c, const moe_aux_t* aux) {
   w.rw = carve_route(cv, c);
   w.dw = carve_dispatch(cv, c);
   w.fw = carve_ffn(cv, c.R, c.E, c.S, c.T);
+  w.gw = carve_diag(cv, c);
   return w;
 }
 
@@ -401,6 +409,29 @@ moe_status_t moe_combine(const moe_config_t* cfg, const float* y_rows, const int
   return hip_status(launch_stats(sp, stream));
 }
 
+moe_status_t moe_router_diagnostics(const moe_config_t* cfg, const float* logits,
+                                    const int32_t* counts, const int32_t* dest, float* diag,
+                                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  Cfg c;
+  moe_status_t st = check_cfg(cfg, &c);
+  if (st != MOE_OK) return st;
+  if (c.ec || !logits || !counts || !dest || !diag || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {logits, counts, dest, diag, ws};
+  for (const void* q : ptrs)
+    if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
+  Carve cv(nullptr);
+  carve_diag(cv, c);
+  if (ws_bytes < cv.off + 256) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (c.T == 0) return MOE_OK;
+  Carve wv(ws);
+  DiagWs gw = carve_diag(wv, c);
+  DiagParams p;
+  p.logits = logits; p.counts = counts; p.dest = dest; p.diag = diag;
+  p.partial_d = gw.partial_d; p.partial_i = gw.partial_i;
+  p.T = (int)c.T; p.E = (int)c.E; p.k = (int)c.k; p.C = (int)c.C;
+  return hip_status(launch_diagnostics(p, stream));
+}
+
 moe_status_t moe_expert_choice(const moe_config_t* cfg, const float* logits, float* scores,
                                int32_t* counts, int32_t* offsets, int32_t* row_token,
                                int32_t* slot, hipStream_t stream) {
@@ -469,7 +500,7 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   if (aux) {
     const void* ap[] = {aux->logits, aux->topk_idx, aux->topk_gate, aux->prob_sum, aux->counts,
                         aux->offsets, aux->dest, aux->row_token, aux->stats, aux->scores,
-                        aux->slot};
+                        aux->slot, aux->diag};
     for (const void* q : ap)
       if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
   }
@@ -508,6 +539,13 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
     dp.row_token = L.row_token; dp.local_rank = L.dw.local_rank; dp.chunk_hist = L.dw.chunk_hist;
     dp.n = (int)(c.T * c.k); dp.k = (int)c.k; dp.E = (int)c.E; dp.C = (int)c.C;
     if ((st = hip_status(launch_dispatch(dp, stream))) != MOE_OK) return st;
+    if (aux && aux->diag) {
+      DiagParams gp;
+      gp.logits = rp.logits; gp.counts = L.counts; gp.dest = L.dest; gp.diag = aux->diag;
+      gp.partial_d = L.gw.partial_d; gp.partial_i = L.gw.partial_i;
+      gp.T = (int)c.T; gp.E = (int)c.E; gp.k = (int)c.k; gp.C = (int)c.C;
+      if ((st = hip_status(launch_diagnostics(gp, stream))) != MOE_OK) return st;
+    }
   }
 
   // 4. grouped expert FFN: routed groups gathered through row_token, then the

@@ -111,6 +111,19 @@ struct EcStatsParams {
 };
 hipError_t launch_stats_ec(const EcStatsParams& p, hipStream_t stream);
 
+// ---- router z-loss and routing diagnostics ---------------------------------------
+struct DiagParams {
+  const float* logits;       // [T,E]
+  const int32_t* counts;     // [E]
+  const int32_t* dest;       // [T,k]
+  float* diag;               // [8 + 2E]
+  double* partial_d;         // [diag_blocks(T), 2] scratch
+  int32_t* partial_i;        // [diag_blocks(T), 2] scratch
+  int T, E, k, C;
+};
+int diag_blocks(int64_t T);
+hipError_t launch_diagnostics(const DiagParams& p, hipStream_t stream);
+
 // ---- combine -------------------------------------------------------------------
 struct CombineParams {
   const float* y_rows;       // [*, d]

@@ -56,6 +56,8 @@ class MoeLayer:
         if self.ec:
             self.out["scores"] = torch.empty((T, E), **f32)
             self.out["slot"] = torch.empty((T, E), **i32)
+        else:
+            self.out["diag"] = torch.empty((8 + 2 * E,), **f32)
         rows = self.rows_bound + S * T
         self.hidden = torch.empty((max(rows, 1), h), dtype=out_dtype, device=dev)
         self.y_rows = torch.empty((max(rows, 1), d), **f32)
@@ -63,7 +65,8 @@ class MoeLayer:
     def forward(self, x, eps=None, logits_in=None, stream=None):
         """moe_layer_forward with every auxiliary output captured."""
         aux = {n: self.out[n] for n in ("logits", "topk_idx", "topk_gate", "prob_sum", "counts",
-                                        "offsets", "dest", "row_token", "stats", "scores", "slot")
+                                        "offsets", "dest", "row_token", "stats", "scores", "slot",
+                                        "diag")
                if n in self.out}
         if logits_in is not None:
             aux.pop("logits")

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     assert set(names) == set(M.EXPORTS)
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
@@ -195,3 +195,17 @@ def test_binding_raises_on_error():
     with pytest.raises(M.MoeError) as e:
         M.moe_combine(c, P[0], P[1], P[2], None, None, None, P[3], None, stream=0)
     assert e.value.status == M.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_diagnostics_validation_statuses():
+    L = _lib.lib()
+    tc = M.make_config(64, 64, 4, 2, 128, act="gelu")
+    ec = M.make_config(64, 64, 4, 2, 128, act="gelu", capacity_factor=1.0, routing="expert")
+    assert L.moe_router_diagnostics(ctypes.byref(ec), P[0], P[1], P[2], P[3], P[4], 1 << 30,
+                                    None) == M.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_router_diagnostics(ctypes.byref(tc), P[0], P[1], None, P[3], P[4], 1 << 30,
+                                    None) == M.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_router_diagnostics(ctypes.byref(tc), P[0], P[1], P[2], P[3], P[4], 8,
+                                    None) == M.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert L.moe_router_diagnostics(ctypes.byref(tc), P[0], P[1], P[2], P[3] + 8, P[4], 1 << 30,
+                                    None) == M.MOE_ERR_UNSUPPORTED
