@@ -58,6 +58,24 @@ the tie rule; the readings:
   EC6 f_i = rows of expert i / all rows (1/E here), P and L_aux as in R5, and
       the drop rate is the fraction of tokens that no expert took.
 
+Overflow re-routing ([MoEM] Level 2 "Overflow handling defines an output
+contract": an assignment that finds its expert full may be dropped, sent to a
+lower-ranked expert, or kept on a residual path; [3D-lab] Capacity panel).
+The pages fix no re-routing policy; the reading:
+  RR1 A token's fallback experts are the ones ranked below its top k, in the
+      same float32-logit order and tie rule; each is tried at most once.
+  RR2 Rounds: every still-unplaced assignment proposes its token's next
+      untried fallback (a token's unplaced slots, in slot order, take
+      consecutive untried fallbacks); every expert accepts the proposals in
+      arrival order up to its spare capacity C - load; the rest retry in the
+      next round; an assignment whose token has no untried fallback left is
+      dropped.
+  RR3 A re-routed slot keeps its gate; only the expert that processes it
+      changes.
+  RR4 f_i still counts the router's (primary) assignments; the drop rate
+      counts assignments left unplaced; an expert's rows are its primary
+      kept assignments, then each round's accepted ones, in arrival order.
+
 Router z-loss and routing diagnostics ([MoE&SMS] "Advanced Theory &
 Extensions": a z-loss keeps router logits from growing large; "Benchmark
 Datasets & Evaluation": utilisation histograms, routing entropy and the
@@ -85,6 +103,7 @@ __all__ = [
     "activation", "expert_ffn", "combine", "balance_stats", "moe_forward",
     "overflow_record", "expert_choice_scores", "expert_choice_select",
     "expert_choice_combine", "moe_forward_expert_choice", "routing_diagnostics",
+    "fallback_order", "dispatch_reroute",
 ]
 
 
@@ -492,3 +511,62 @@ def routing_diagnostics(H32, counts, kept, dest, C: int, T: int, k: int, E: int)
         "tokens_fully_dropped": float(np.mean(lost == k)),
         "tokens_partly_dropped": float(np.mean((lost > 0) & (lost < k))),
     }
+
+
+def fallback_order(H32: np.ndarray, k: int) -> np.ndarray:
+    """[T, E-k]: each token's experts ranked k+1-th and below (RR1)."""
+    return np.argsort(-np.asarray(H32, np.float32), axis=1, kind="stable")[:, k:].astype(np.int32)
+
+
+def dispatch_reroute(idx: np.ndarray, H32: np.ndarray, E: int, C: int) -> dict:
+    """Capacity with overflow re-routing (RR1-RR4): the arrival-order pass of
+    ``dispatch`` first, then rounds of fallback proposals.  Returns the same
+    tables as ``dispatch`` (offsets, dest and row_token over the final
+    placement; counts are the primary ones) plus ``final_expert`` [T,k] (-1
+    when dropped), ``placed`` per expert and ``rounds``."""
+    idx = np.asarray(idx, np.int64)
+    T, k = idx.shape
+    prim = dispatch(idx, E, C)
+    load = np.asarray(prim["kept"], np.int64).copy()
+    flat_dest = prim["dest"].reshape(-1)
+    final_e = np.where(flat_dest >= 0, idx.reshape(-1), -1)
+    row_in_e = np.where(flat_dest >= 0, prim["rank"].reshape(-1), -1)
+    F = fallback_order(H32, k)
+    nf = E - k
+    ptr = np.zeros(T, np.int64)
+    unplaced = [i for i in range(T * k) if flat_dest[i] < 0]
+    rounds = 0
+    while unplaced:
+        rounds += 1
+        proposals = []
+        seen = {}
+        for i in unplaced:                     # consecutive untried fallbacks per token
+            t = i // k
+            j = seen.get(t, 0)
+            seen[t] = j + 1
+            q = ptr[t] + j
+            proposals.append(int(F[t, q]) if q < nf else -1)
+        for t, n in seen.items():
+            ptr[t] += n
+        taken = np.zeros(E, np.int64)
+        still = []
+        for i, e in zip(unplaced, proposals):  # arrival order
+            if e < 0:
+                continue                        # no fallback left: dropped
+            if load[e] + taken[e] < C:
+                final_e[i] = e
+                row_in_e[i] = load[e] + taken[e]
+                taken[e] += 1
+            else:
+                still.append(i)
+        load += taken
+        unplaced = still
+    offsets = np.zeros(E + 1, np.int64)
+    offsets[1:] = np.cumsum(load)
+    dest = np.where(final_e >= 0, offsets[np.maximum(final_e, 0)] + row_in_e, -1)
+    row_token = np.full(int(offsets[-1]), -1, np.int64)
+    ok = dest >= 0
+    row_token[dest[ok]] = np.arange(T * k)[ok] // k
+    return {"counts": prim["counts"], "kept": prim["kept"], "placed": load, "offsets": offsets,
+            "dest": dest.reshape(T, k), "row_token": row_token,
+            "final_expert": final_e.reshape(T, k), "rounds": rounds}

@@ -15,6 +15,7 @@ import oracle
 import oracle.moe_oracle as M
 import tests.test_oracle_expert_choice as ecpins
 import tests.test_oracle_pins as pins
+import tests.test_oracle_reroute as rrpins
 
 ORIG = {n: getattr(M, n) for n in M.__all__}
 
@@ -184,6 +185,69 @@ def _diag_any_loss_is_full(H32, counts, kept, dest, C, T, k, E):
     return d
 
 
+def _rr_fallback_reversed(H32, k):
+    return ORIG["fallback_order"](H32, k)[:, ::-1].copy()
+
+
+def _rr_variant(idx, H32, E, C, retry=True, reverse_arrival=False, reroute_first=False):
+    """The re-routing rounds with one planted change."""
+    idx = np.asarray(idx, np.int64)
+    T, k = idx.shape
+    prim = M.dispatch(idx, E, C)
+    load = np.asarray(prim["kept"], np.int64).copy()
+    fd = prim["dest"].reshape(-1)
+    fe = np.where(fd >= 0, idx.reshape(-1), -1)
+    rin = np.where(fd >= 0, prim["rank"].reshape(-1), -1)
+    F = M.fallback_order(H32, k)
+    ptr = np.zeros(T, np.int64)
+    un = [i for i in range(T * k) if fd[i] < 0]
+    rerouted = np.zeros(T * k, bool)
+    rounds = 0
+    while un:
+        rounds += 1
+        props, seen = [], {}
+        for i in un:
+            t = i // k
+            j = seen.get(t, 0)
+            seen[t] = j + 1
+            q = ptr[t] + j
+            props.append(int(F[t, q]) if q < E - k else -1)
+        for t, n in seen.items():
+            ptr[t] += n
+        taken = np.zeros(E, np.int64)
+        still = []
+        order = list(zip(un, props))
+        if reverse_arrival:
+            order = order[::-1]
+        for i, e in order:
+            if e < 0:
+                continue
+            if load[e] + taken[e] < C:
+                fe[i], rin[i] = e, load[e] + taken[e]
+                taken[e] += 1
+                rerouted[i] = True
+            elif retry:
+                still.append(i)
+        load += taken
+        un = sorted(still)
+    if reroute_first:  # re-routed rows before the primary ones
+        for e in range(E):
+            mine = np.nonzero(fe == e)[0]
+            rr = [i for i in mine if rerouted[i]]
+            pr = [i for i in mine if not rerouted[i]]
+            for pos, i in enumerate(rr + pr):
+                rin[i] = pos
+    off = np.zeros(E + 1, np.int64)
+    off[1:] = np.cumsum(load)
+    dest = np.where(fe >= 0, off[np.maximum(fe, 0)] + rin, -1)
+    rt = np.full(int(off[-1]), -1, np.int64)
+    ok = dest >= 0
+    rt[dest[ok]] = np.arange(T * k)[ok] // k
+    return {"counts": prim["counts"], "kept": prim["kept"], "placed": load, "offsets": off,
+            "dest": dest.reshape(T, k), "row_token": rt, "final_expert": fe.reshape(T, k),
+            "rounds": rounds}
+
+
 MUTATIONS = {
     "router drops the bias": ("router_logits", _router_no_bias),
     "noise without softplus": ("router_logits", _router_linear_noise),
@@ -209,6 +273,10 @@ MUTATIONS = {
     "z-loss not squared": ("routing_diagnostics", _diag_z_unsquared),
     "entropy in bits": ("routing_diagnostics", _diag_entropy_bits),
     "a partial drop counted as a full one": ("routing_diagnostics", _diag_any_loss_is_full),
+    "re-route: fallbacks from the lowest rank": ("fallback_order", _rr_fallback_reversed),
+    "re-route: no retry after a rejection": ("dispatch_reroute", lambda *a: _rr_variant(*a, retry=False)),
+    "re-route: later arrivals win": ("dispatch_reroute", lambda *a: _rr_variant(*a, reverse_arrival=True)),
+    "re-route: re-routed rows first": ("dispatch_reroute", lambda *a: _rr_variant(*a, reroute_first=True)),
 }
 
 PIN_TESTS = [
@@ -237,6 +305,11 @@ PIN_TESTS = [
     pins.test_zloss_and_entropy_closed_forms,
     pins.test_diagnostics_on_the_capacity_worked_example,
     pins.test_diagnostics_partial_drops_with_two_slots,
+    rrpins.test_reroute_hand_example,
+    rrpins.test_reroute_on_the_capacity_worked_example,
+    rrpins.test_reroute_multiple_slots_take_distinct_fallbacks,
+    rrpins.test_reroute_equals_drop_when_nothing_overflows,
+    lambda: [rrpins.test_reroute_invariants(s_) for s_ in range(3)],
 ]
 
 
