@@ -10,7 +10,8 @@ entry points on torch's current stream.  Prints ONE JSON line.
 Workloads: mixtral_prefill (default; the MFMA-bound Mixtral-shaped prefill,
 T=8192, d=4096, 8 experts top-2, SwiGLU h=14336), mixtral_decode, switch_top1,
 finegrained_shared, toy_fp32, mixtral_prefill_ec (the prefill shape with
-expert-choice routing).
+expert-choice routing), finegrained_reroute (the fine-grained layer with
+overflow re-routed to lower-ranked experts).
 """
 from __future__ import annotations
 
@@ -32,15 +33,16 @@ DOMINANT = {"ffn_tiled": "ffn_tiled_kernel", "ffn_skinny": "ffn_skinny_kernel",
             "ffn_f32": "ffn_f32_kernel"}
 
 
-def algorithmic_work(cfg, counts, C):
+def algorithmic_work(cfg, offsets):
     """Algorithmic FLOPs and bytes of the layer and of its first expert GEMM.
 
-    Only work the method must do counts: kept assignments (dropped ones and
-    padding excluded), weights of experts that received rows, each operand and
-    result once.  m = weight matrices per expert (3 SwiGLU, 2 otherwise)."""
+    Only work the method must do counts: the rows placed with experts (the
+    final offsets: dropped assignments and padding excluded), weights of
+    experts that received rows, each operand and result once.  m = weight
+    matrices per expert (3 SwiGLU, 2 otherwise)."""
     b = 2 if cfg.dtype == "bf16" else 4
     T, d, E, k, h, S = cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, cfg.n_shared
-    kept = np.minimum(np.asarray(counts, np.int64), C)
+    kept = np.diff(np.asarray(offsets, np.int64))
     rows = int(kept.sum())
     active = int((kept > 0).sum())
     m_up = 2 if cfg.act == "swiglu" else 1
@@ -207,7 +209,7 @@ def main():
         d = torch.empty((8 + 2 * cfg.E,), dtype=torch.float32, device="cuda")
         L.moe_router_diagnostics(layer.cfg, out["logits"], out["counts"], out["dest"], d, layer.ws)
         diag = d.cpu().numpy()
-    work = algorithmic_work(cfg, counts, layer.capacity)
+    work = algorithmic_work(cfg, out["offsets"].cpu().numpy())
     kernel = "ffn_f32" if cfg.dtype == "f32" else (
         "ffn_skinny" if layer.group_bound <= 32 and (cfg.n_shared == 0 or cfg.T <= 32) else "ffn_tiled")
     up_ms = stage_ms["up"]

@@ -69,6 +69,11 @@ typedef enum { MOE_ACT_GELU = 0, MOE_ACT_RELU = 1, MOE_ACT_SWIGLU = 2 } moe_act_
  * [MoE&SMS] Advanced Theory & Extensions). */
 typedef enum { MOE_ROUTE_TOKEN_CHOICE = 0, MOE_ROUTE_EXPERT_CHOICE = 1 } moe_routing_t;
 
+/* What a full expert does to a token-choice assignment ([MoEM] "Overflow
+ * handling defines an output contract"): drop it, or re-route it to the
+ * token's lower-ranked experts (moe_dispatch_reroute). */
+typedef enum { MOE_OVERFLOW_DROP = 0, MOE_OVERFLOW_REROUTE = 1 } moe_overflow_t;
+
 typedef struct moe_config {
   int64_t T;                /* tokens in the batch                               */
   int64_t d;                /* model width                                       */
@@ -83,6 +88,7 @@ typedef struct moe_config {
   int32_t router_bias;      /* nonzero: b_g [E] is given                         */
   int32_t router_noise;     /* nonzero: w_noise [E,d] and eps [T,E] are given    */
   int32_t routing;          /* moe_routing_t (0 = token choice)                  */
+  int32_t overflow;         /* moe_overflow_t (0 = drop); token choice only      */
 } moe_config_t;
 
 /* Device pointers to the layer's parameters (unused ones may be NULL). */
@@ -109,6 +115,7 @@ typedef struct moe_aux {
   float*   scores;      /* [T,E]   expert choice only                         */
   int32_t* slot;        /* [T,E]   expert choice only                         */
   float*   diag;        /* [8+2E]  token choice only: moe_router_diagnostics  */
+  int32_t* final_expert;/* [T,k]   re-routing only: expert of each slot, -1  */
 } moe_aux_t;
 
 /* (host) Human-readable name of a status code; never NULL. */
@@ -172,6 +179,32 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx,
                           void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Counts, capacity and dispatch with overflow re-routing ([MoEM] Level 2:
+ * "Overflow handling defines an output contract" -- an assignment that finds
+ * its expert full goes to a lower-ranked expert; [3D-lab] Capacity panel).
+ * cfg->overflow must be MOE_OVERFLOW_REROUTE.  First the arrival-order pass of
+ * moe_dispatch; then rounds: every unplaced assignment proposes its token's
+ * next untried fallback (the experts ranked below the token's top k by the
+ * float32 logits, ties to the lower index, each tried at most once; a token's
+ * unplaced slots, in slot order, take consecutive ones), and every expert
+ * accepts proposals in arrival order up to its spare capacity C - load; the
+ * rest retry in the next round; an assignment whose token has no untried
+ * fallback left is dropped.  A re-routed slot keeps its gate.
+ *   counts[e]        primary assignments routed to e (before capacity)
+ *   offsets[e]       exclusive prefix sum of the final loads; [E+1]
+ *   dest[t,s]        final row of slot s, or -1
+ *   row_token[r]     token of row r, r < offsets[E]: an expert's primary kept
+ *                    rows, then each round's accepted rows, in arrival order
+ *   final_expert[t,s] the expert that processes slot s, or -1
+ * logits are the float32 logits the top-k was taken on.  Exact and
+ * deterministic.  Workspace: at least moe_workspace_bytes(cfg).
+ */
+moe_status_t moe_dispatch_reroute(const moe_config_t* cfg, const int32_t* topk_idx,
+                                  const float* logits, int32_t* counts, int32_t* offsets,
+                                  int32_t* dest, int32_t* row_token, int32_t* final_expert,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Grouped expert FFN over expert-contiguous rows ([MoE&SMS] Core Concepts:
  * each expert is an FFN with its own weights; [SMoE-arch] each expert runs
  * once on its grouped tokens).  For every group g < n_groups and every row r in
@@ -229,6 +262,7 @@ moe_status_t moe_expert_down(const moe_config_t* cfg, int64_t n_groups,
  *   y_shared  [n_shared, T, d] float32, or NULL when n_shared == 0
  *   stats     optional [2E+2]: f[E] = counts/(T*k), P[E] = prob_sum/T,
  *             L_aux = E * sum f P (alpha = 1), drop_rate = 1 - sum min(counts,C)/(T*k)
+ *             (with re-routing: the fraction of slots whose dest is -1)
  */
 moe_status_t moe_combine(const moe_config_t* cfg, const float* y_rows,
                          const int32_t* dest, const float* topk_gate,
@@ -306,7 +340,8 @@ moe_status_t moe_combine_expert_choice(const moe_config_t* cfg, const float* y_r
  * With cfg->routing == MOE_ROUTE_EXPERT_CHOICE the dispatch and combine steps
  * are moe_expert_choice and moe_combine_expert_choice (aux->topk_idx,
  * topk_gate, dest and diag are then not written).  With token choice,
- * aux->diag != NULL also runs moe_router_diagnostics on the layer's routing.
+ * aux->diag != NULL also runs moe_router_diagnostics on the layer's routing,
+ * and cfg->overflow == MOE_OVERFLOW_REROUTE uses moe_dispatch_reroute.
  * Intermediates live in `ws` unless `aux` names a buffer for them.
  */
 moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w,

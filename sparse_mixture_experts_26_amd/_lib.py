@@ -19,8 +19,10 @@ MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMA
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_GELU, MOE_ACT_RELU, MOE_ACT_SWIGLU = 0, 1, 2
 MOE_ROUTE_TOKEN_CHOICE, MOE_ROUTE_EXPERT_CHOICE = 0, 1
+MOE_OVERFLOW_DROP, MOE_OVERFLOW_REROUTE = 0, 1
 ACT_CODES = {"gelu": MOE_ACT_GELU, "relu": MOE_ACT_RELU, "swiglu": MOE_ACT_SWIGLU}
 ROUTING_CODES = {"token": MOE_ROUTE_TOKEN_CHOICE, "expert": MOE_ROUTE_EXPERT_CHOICE}
+OVERFLOW_CODES = {"drop": MOE_OVERFLOW_DROP, "reroute": MOE_OVERFLOW_REROUTE}
 DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16}
 
 
@@ -28,7 +30,7 @@ class MoeConfig(ctypes.Structure):
     _fields_ = [("T", c_int64), ("d", c_int64), ("E", c_int64), ("k", c_int64), ("h", c_int64),
                 ("n_shared", c_int64), ("capacity_factor", c_double), ("act", c_int32),
                 ("dtype", c_int32), ("ffn_bias", c_int32), ("router_bias", c_int32),
-                ("router_noise", c_int32), ("routing", c_int32)]
+                ("router_noise", c_int32), ("routing", c_int32), ("overflow", c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -39,7 +41,7 @@ class MoeWeights(ctypes.Structure):
 class MoeAux(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("logits", "topk_idx", "topk_gate", "prob_sum", "counts",
                                         "offsets", "dest", "row_token", "stats", "scores",
-                                        "slot", "diag")]
+                                        "slot", "diag", "final_expert")]
 
 
 class MoeError(RuntimeError):
@@ -68,6 +70,7 @@ def lib() -> ctypes.CDLL:
             "moe_workspace_bytes": (c_size_t, [cfgp]),
             "moe_route": (st, [cfgp] + [vp] * 10 + [c_size_t, vp]),
             "moe_dispatch": (st, [cfgp] + [vp] * 8 + [c_size_t, vp]),
+            "moe_dispatch_reroute": (st, [cfgp] + [vp] * 8 + [c_size_t, vp]),
             "moe_expert_ffn": (st, [cfgp, c_int64, vp, vp, vp, c_int64, c_int64, vp, vp, vp, vp,
                                     vp, vp, c_int, vp, c_size_t, vp]),
             "moe_expert_up": (st, [cfgp, c_int64, vp, vp, vp, c_int64, c_int64, vp, vp, vp, vp,
@@ -89,21 +92,22 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ("moe_status_string", "moe_capacity", "moe_routed_rows_bound", "moe_workspace_bytes",
-           "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
+           "moe_route", "moe_dispatch", "moe_dispatch_reroute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
            "moe_combine", "moe_router_diagnostics", "moe_expert_choice", "moe_combine_expert_choice",
            "moe_layer_forward")
 
 
 def make_config(T, d, E, k, h, *, act="swiglu", dtype="bf16", capacity_factor=0.0,
                 n_shared=0, ffn_bias=False, router_bias=False, router_noise=False,
-                routing="token") -> MoeConfig:
+                routing="token", overflow="drop") -> MoeConfig:
     return MoeConfig(T=T, d=d, E=E, k=k, h=h, n_shared=n_shared,
                      capacity_factor=float(capacity_factor),
                      act=ACT_CODES.get(act, act) if isinstance(act, str) else act,
                      dtype=DTYPE_CODES.get(dtype, dtype) if isinstance(dtype, str) else dtype,
                      ffn_bias=int(bool(ffn_bias)), router_bias=int(bool(router_bias)),
                      router_noise=int(bool(router_noise)),
-                     routing=ROUTING_CODES.get(routing, routing) if isinstance(routing, str) else routing)
+                     routing=ROUTING_CODES.get(routing, routing) if isinstance(routing, str) else routing,
+                     overflow=OVERFLOW_CODES.get(overflow, overflow) if isinstance(overflow, str) else overflow)
 
 
 def _p(t):
@@ -166,6 +170,14 @@ def moe_dispatch(cfg, topk_idx, x, counts, offsets, dest, row_token, x_perm, ws,
     _check("moe_dispatch", lib().moe_dispatch(ctypes.byref(cfg), _p(topk_idx), _p(x), _p(counts),
                                               _p(offsets), _p(dest), _p(row_token), _p(x_perm),
                                               wp, wn, _stream(stream)))
+
+
+def moe_dispatch_reroute(cfg, topk_idx, logits, counts, offsets, dest, row_token, final_expert, ws,
+                         stream=None):
+    wp, wn = _ws(ws)
+    _check("moe_dispatch_reroute", lib().moe_dispatch_reroute(
+        ctypes.byref(cfg), _p(topk_idx), _p(logits), _p(counts), _p(offsets), _p(dest),
+        _p(row_token), _p(final_expert), wp, wn, _stream(stream)))
 
 
 def moe_expert_ffn(cfg, n_groups, x_rows, row_token, offsets, rows_bound, group_bound, w1, w3, w2,

@@ -35,6 +35,7 @@ struct Cfg {
   int64_t T, d, E, k, h, S;
   int act, bf16;
   bool ec;        // expert-choice routing
+  bool rr;        // token choice with overflow re-routing
   int64_t C;      // capacity, clamped to T (no expert can receive more)
   int64_t R;      // routed rows bound: min(T*k, E*C), or E*C for expert choice
   size_t esz;     // bytes per activation / weight element
@@ -57,6 +58,10 @@ moe_status_t check_cfg(const moe_config_t* c, Cfg* o) {
   if (isnan(c->capacity_factor)) return MOE_ERR_INVALID_ARGUMENT;
   if (c->routing != MOE_ROUTE_TOKEN_CHOICE && c->routing != MOE_ROUTE_EXPERT_CHOICE)
     return MOE_ERR_INVALID_ARGUMENT;
+  if (c->overflow != MOE_OVERFLOW_DROP && c->overflow != MOE_OVERFLOW_REROUTE)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (c->overflow == MOE_OVERFLOW_REROUTE && c->routing != MOE_ROUTE_TOKEN_CHOICE)
+    return MOE_ERR_INVALID_ARGUMENT;
   if (c->E > 256 || c->k > 8 || c->d % 8 || c->h % 8) return MOE_ERR_UNSUPPORTED;
   if (c->router_noise && c->E > 128) return MOE_ERR_UNSUPPORTED;
   if (c->n_shared > 64) return MOE_ERR_UNSUPPORTED;
@@ -65,6 +70,7 @@ moe_status_t check_cfg(const moe_config_t* c, Cfg* o) {
   o->bf16 = c->dtype == MOE_BF16;
   o->esz = o->bf16 ? 2 : 4;
   o->ec = c->routing == MOE_ROUTE_EXPERT_CHOICE;
+  o->rr = c->overflow == MOE_OVERFLOW_REROUTE;
   o->C = std::min<int64_t>(capacity_of(c), c->T);
   o->R = o->ec ? c->E * o->C : std::min<int64_t>(c->T * c->k, c->E * o->C);
   const int64_t rows = o->R + o->S * o->T;
@@ -94,6 +100,9 @@ struct RouteWs { float* prob_partial; };
 struct DispatchWs { int32_t* local_rank; int32_t* chunk_hist; };
 struct FfnWs { TileEntry* entries; int32_t* n_entries; };
 struct DiagWs { double* partial_d; int32_t* partial_i; };
+struct RerouteWs {
+  uint8_t* fallback; int32_t* list_a; int32_t* list_b; int32_t* fe; int32_t* rin; int32_t* ptr;
+};
 
 RouteWs carve_route(Carve& cv, const Cfg& c) {
   return {static_cast<float*>(cv.take((size_t)route_blocks(c.T) * c.E * 4))};
@@ -102,6 +111,17 @@ DispatchWs carve_dispatch(Carve& cv, const Cfg& c) {
   DispatchWs w;
   w.local_rank = static_cast<int32_t*>(cv.take((size_t)c.T * c.k * 4));
   w.chunk_hist = static_cast<int32_t*>(cv.take((size_t)dispatch_chunks(c.T * c.k) * c.E * 4));
+  return w;
+}
+RerouteWs carve_reroute(Carve& cv, const Cfg& c) {
+  RerouteWs w;
+  const size_t tk = (size_t)c.T * c.k;
+  w.fallback = static_cast<uint8_t*>(cv.take((size_t)c.T * (c.E - c.k)));
+  w.list_a = static_cast<int32_t*>(cv.take(tk * 4));
+  w.list_b = static_cast<int32_t*>(cv.take(tk * 4));
+  w.fe = static_cast<int32_t*>(cv.take(tk * 4));
+  w.rin = static_cast<int32_t*>(cv.take(tk * 4));
+  w.ptr = static_cast<int32_t*>(cv.take((size_t)c.T * 4));
   return w;
 }
 DiagWs carve_diag(Carve& cv, const Cfg& c) {
@@ -125,8 +145,9 @@ struct LayerWs {
   float* logits; int32_t* idx; float* gate; float* prob_sum;
   int32_t* counts; int32_t* offsets; int32_t* dest; int32_t* row_token;
   float* scores; int32_t* slot;  // expert choice only
+  int32_t* final_expert;         // re-routing only
   void* hidden; float* y_rows;
-  RouteWs rw; DispatchWs dw; FfnWs fw; DiagWs gw;
+  RouteWs rw; DispatchWs dw; FfnWs fw; DiagWs gw; RerouteWs rrw;
 };
 
 LayerWs carve_layer(Carve& cv, const Cfg& c, const moe_aux_t* aux) {
@@ -144,6 +165,9 @@ LayerWs carve_layer(Carve& cv, const Cfg& c, const moe_aux_t* aux) {
       pick(aux ? aux->row_token : nullptr, (size_t)std::max<int64_t>(c.R, (int64_t)tk) * 4));
   w.scores = nullptr;
   w.slot = nullptr;
+  w.final_expert = nullptr;
+  if (c.rr)
+    w.final_expert = static_cast<int32_t*>(pick(aux ? aux->final_expert : nullptr, tk * 4));
   if (c.ec) {
     w.scores = static_cast<float*>(pick(aux ? aux->scores : nullptr, (size_t)c.T * c.E * 4));
     w.slot = static_cast<int32_t*>(pick(aux ? aux->slot : nullptr, (size_t)c.T * c.E * 4));
@@ -155,6 +179,8 @@ LayerWs carve_layer(Carve& cv, const Cfg& c, const moe_aux_t* aux) {
   w.dw = carve_dispatch(cv, c);
   w.fw = carve_ffn(cv, c.R, c.E, c.S, c.T);
   w.gw = carve_diag(cv, c);
+  w.rrw = RerouteWs{};
+  if (c.rr) w.rrw = carve_reroute(cv, c);
   return w;
 }
 
@@ -293,7 +319,7 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx, cons
   moe_status_t st = check_cfg(cfg, &c);
   if (st != MOE_OK) return st;
   if (!topk_idx || !counts || !offsets || !dest || !row_token || !ws) return MOE_ERR_INVALID_ARGUMENT;
-  if (c.ec) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.ec || c.rr) return MOE_ERR_INVALID_ARGUMENT;
   if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
   const void* ptrs[] = {topk_idx, x, counts, offsets, dest, row_token, x_perm, ws};
   for (const void* q : ptrs)
@@ -312,6 +338,41 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx, cons
   if (st != MOE_OK || !x) return st;
   return hip_status(launch_permute(x, row_token, offsets + c.E, x_perm,
                                    (int64_t)c.d * (int64_t)c.esz, c.R, stream));
+}
+
+moe_status_t moe_dispatch_reroute(const moe_config_t* cfg, const int32_t* topk_idx,
+                                  const float* logits, int32_t* counts, int32_t* offsets,
+                                  int32_t* dest, int32_t* row_token, int32_t* final_expert,
+                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  Cfg c;
+  moe_status_t st = check_cfg(cfg, &c);
+  if (st != MOE_OK) return st;
+  if (!c.rr || !topk_idx || !logits || !counts || !offsets || !dest || !row_token ||
+      !final_expert || !ws)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {topk_idx, logits, counts, offsets, dest, row_token, final_expert, ws};
+  for (const void* q : ptrs)
+    if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
+  Carve cv(nullptr);
+  carve_dispatch(cv, c);
+  carve_reroute(cv, c);
+  if (ws_bytes < cv.off + 256) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (c.T == 0) return MOE_OK;
+  Carve wv(ws);
+  DispatchWs dw = carve_dispatch(wv, c);
+  RerouteWs rw = carve_reroute(wv, c);
+  DispatchParams p;
+  p.idx = topk_idx; p.counts = counts; p.offsets = offsets; p.dest = dest;
+  p.row_token = row_token; p.local_rank = dw.local_rank; p.chunk_hist = dw.chunk_hist;
+  p.n = (int)(c.T * c.k); p.k = (int)c.k; p.E = (int)c.E; p.C = (int)c.C;
+  if ((st = hip_status(launch_dispatch(p, stream))) != MOE_OK) return st;
+  RerouteParams r;
+  r.idx = topk_idx; r.logits = logits; r.counts = counts; r.offsets = offsets;
+  r.dest = dest; r.dest_out = dest; r.row_token = row_token; r.final_expert = final_expert;
+  r.fallback = rw.fallback; r.list_a = rw.list_a; r.list_b = rw.list_b; r.fe = rw.fe;
+  r.rin = rw.rin; r.ptr = rw.ptr;
+  r.T = (int)c.T; r.E = (int)c.E; r.k = (int)c.k; r.C = (int)c.C;
+  return hip_status(launch_reroute(r, stream));
 }
 
 moe_status_t moe_expert_up(const moe_config_t* cfg, int64_t n_groups, const void* x_rows,
@@ -405,6 +466,7 @@ moe_status_t moe_combine(const moe_config_t* cfg, const float* y_rows, const int
   if (st != MOE_OK || !stats) return st;
   StatsParams sp;
   sp.counts = counts; sp.prob_sum = prob_sum; sp.stats = stats;
+  sp.dest = c.rr ? dest : nullptr;
   sp.T = (int)c.T; sp.k = (int)c.k; sp.E = (int)c.E; sp.C = (int)c.C;
   return hip_status(launch_stats(sp, stream));
 }
@@ -500,7 +562,7 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   if (aux) {
     const void* ap[] = {aux->logits, aux->topk_idx, aux->topk_gate, aux->prob_sum, aux->counts,
                         aux->offsets, aux->dest, aux->row_token, aux->stats, aux->scores,
-                        aux->slot, aux->diag};
+                        aux->slot, aux->diag, aux->final_expert};
     for (const void* q : ap)
       if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
   }
@@ -539,6 +601,16 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
     dp.row_token = L.row_token; dp.local_rank = L.dw.local_rank; dp.chunk_hist = L.dw.chunk_hist;
     dp.n = (int)(c.T * c.k); dp.k = (int)c.k; dp.E = (int)c.E; dp.C = (int)c.C;
     if ((st = hip_status(launch_dispatch(dp, stream))) != MOE_OK) return st;
+    if (c.rr) {
+      RerouteParams r;
+      r.idx = L.idx; r.logits = rp.logits; r.counts = L.counts; r.offsets = L.offsets;
+      r.dest = L.dest; r.dest_out = L.dest; r.row_token = L.row_token;
+      r.final_expert = L.final_expert;
+      r.fallback = L.rrw.fallback; r.list_a = L.rrw.list_a; r.list_b = L.rrw.list_b;
+      r.fe = L.rrw.fe; r.rin = L.rrw.rin; r.ptr = L.rrw.ptr;
+      r.T = (int)c.T; r.E = (int)c.E; r.k = (int)c.k; r.C = (int)c.C;
+      if ((st = hip_status(launch_reroute(r, stream))) != MOE_OK) return st;
+    }
     if (aux && aux->diag) {
       DiagParams gp;
       gp.logits = rp.logits; gp.counts = L.counts; gp.dest = L.dest; gp.diag = aux->diag;
@@ -592,6 +664,7 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   if (aux && aux->stats) {
     StatsParams sp;
     sp.counts = L.counts; sp.prob_sum = L.prob_sum; sp.stats = aux->stats;
+    sp.dest = c.rr ? L.dest : nullptr;
     sp.T = (int)c.T; sp.k = (int)c.k; sp.E = (int)c.E; sp.C = (int)c.C;
     if ((st = hip_status(launch_stats(sp, stream))) != MOE_OK) return st;
   }

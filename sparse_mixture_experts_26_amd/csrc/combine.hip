@@ -64,15 +64,23 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsParams p) {
     kept[e] = c < p.C ? c : p.C;
   }
   __syncthreads();
+  // slots left unplaced (re-routing): counted over dest in a fixed order
+  __shared__ int lost[256];
+  int my_lost = 0;
+  if (p.dest)
+    for (int64_t i = e; i < (int64_t)p.T * p.k; i += 256) my_lost += p.dest[i] < 0;
+  lost[e] = my_lost;
+  __syncthreads();
   if (e == 0) {
     double s = 0.0;
-    long long ks = 0;
+    long long ks = 0, ls = 0;
     for (int i = 0; i < p.E; ++i) {
       s += prod[i];
       ks += kept[i];
     }
+    for (int i = 0; i < 256; ++i) ls += lost[i];
     p.stats[2 * p.E] = (float)((double)p.E * s);
-    p.stats[2 * p.E + 1] = (float)(1.0 - (double)ks / tk);
+    p.stats[2 * p.E + 1] = p.dest ? (float)((double)ls / tk) : (float)(1.0 - (double)ks / tk);
   }
 }
 

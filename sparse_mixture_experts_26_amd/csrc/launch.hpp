@@ -43,6 +43,27 @@ constexpr int kDispatchChunk = 1024;
 inline int dispatch_chunks(int64_t n) { return (int)((n + kDispatchChunk - 1) / kDispatchChunk); }
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t stream);
 
+// Overflow re-routing after the primary dispatch (which leaves counts,
+// offsets and dest of the arrival-order pass).
+struct RerouteParams {
+  const int32_t* idx;       // [T,k]
+  const float* logits;      // [T,E]
+  const int32_t* counts;    // [E] primary counts
+  int32_t* offsets;         // [E+1] in: primary, out: over the final placement
+  const int32_t* dest;      // [T,k] primary (may be dest_out itself)
+  int32_t* dest_out;        // [T,k] final
+  int32_t* row_token;       // [T*k]
+  int32_t* final_expert;    // [T,k]
+  uint8_t* fallback;        // [T, E-k] scratch
+  int32_t* list_a;          // [T*k] scratch
+  int32_t* list_b;          // [T*k] scratch
+  int32_t* fe;              // [T*k] scratch
+  int32_t* rin;             // [T*k] scratch
+  int32_t* ptr;             // [T] scratch
+  int T, E, k, C;
+};
+hipError_t launch_reroute(const RerouteParams& p, hipStream_t stream);
+
 // x_perm[r] = x[row_token[r]] for r < offsets[E]; row_bytes % 16 == 0.
 hipError_t launch_permute(const void* x, const int32_t* row_token, const int32_t* total,
                           void* x_perm, int64_t row_bytes, int64_t rows_bound,
@@ -140,6 +161,7 @@ struct StatsParams {
   const int32_t* counts;     // [E]
   const float* prob_sum;     // [E]
   float* stats;              // [2E+2]
+  const int32_t* dest;       // [T,k]: when set, the drop rate counts dest < 0
   int T, k, E, C;
 };
 hipError_t launch_stats(const StatsParams& p, hipStream_t stream);

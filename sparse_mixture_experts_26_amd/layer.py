@@ -21,7 +21,8 @@ def config_of(spec) -> L.MoeConfig:
                          capacity_factor=spec.capacity_factor, n_shared=spec.n_shared,
                          ffn_bias=spec.ffn_bias, router_bias=spec.router_bias != "none",
                          router_noise=spec.router_noise,
-                         routing=getattr(spec, "routing", "token"))
+                         routing=getattr(spec, "routing", "token"),
+                         overflow=getattr(spec, "overflow", "drop"))
 
 
 class MoeLayer:
@@ -36,6 +37,7 @@ class MoeLayer:
         self.rows_bound = L.moe_routed_rows_bound(c)
         self.group_bound = min(T, self.capacity)
         self.ec = c.routing == L.MOE_ROUTE_EXPERT_CHOICE
+        self.rr = c.overflow == L.MOE_OVERFLOW_REROUTE
         dev = self.device
         self.ws = torch.empty(max(L.moe_workspace_bytes(c), 256), dtype=torch.uint8, device=dev)
         out_dtype = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
@@ -58,6 +60,8 @@ class MoeLayer:
             self.out["slot"] = torch.empty((T, E), **i32)
         else:
             self.out["diag"] = torch.empty((8 + 2 * E,), **f32)
+        if self.rr:
+            self.out["final_expert"] = torch.empty((T, k), **i32)
         rows = self.rows_bound + S * T
         self.hidden = torch.empty((max(rows, 1), h), dtype=out_dtype, device=dev)
         self.y_rows = torch.empty((max(rows, 1), d), **f32)
@@ -66,7 +70,7 @@ class MoeLayer:
         """moe_layer_forward with every auxiliary output captured."""
         aux = {n: self.out[n] for n in ("logits", "topk_idx", "topk_gate", "prob_sum", "counts",
                                         "offsets", "dest", "row_token", "stats", "scores", "slot",
-                                        "diag")
+                                        "diag", "final_expert")
                if n in self.out}
         if logits_in is not None:
             aux.pop("logits")
@@ -94,6 +98,9 @@ class MoeLayer:
                 o["scores"].copy_(scores_in)
             L.moe_expert_choice(c, None if scores_in is not None else o["logits"], o["scores"],
                                 o["counts"], o["offsets"], o["row_token"], o["slot"], stream)
+        elif self.rr:
+            L.moe_dispatch_reroute(c, o["topk_idx"], o["logits"], o["counts"], o["offsets"],
+                                   o["dest"], o["row_token"], o["final_expert"], self.ws, stream)
         else:
             L.moe_dispatch(c, o["topk_idx"], None, o["counts"], o["offsets"], o["dest"],
                            o["row_token"], None, self.ws, stream)

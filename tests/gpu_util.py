@@ -25,7 +25,8 @@ def oracle_forward(inp, logits=None, tokens=None) -> dict:
     return O.moe_forward(inp.x, inp.w_g, inp.w1, inp.w2, k=c.k, act=c.act,
                          capacity_factor=c.capacity_factor, w3=inp.w3, b_g=inp.b_g,
                          w_noise=inp.w_noise, eps=inp.eps, b1=inp.b1, b2=inp.b2,
-                         ws1=inp.ws1, ws3=inp.ws3, ws2=inp.ws2, logits=logits, tokens=tokens)
+                         ws1=inp.ws1, ws3=inp.ws3, ws2=inp.ws2, logits=logits, tokens=tokens,
+                         overflow=c.overflow)
 
 
 def weights_of(dev: dict) -> dict:

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     assert set(names) == set(M.EXPORTS)
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
@@ -209,3 +209,21 @@ def test_diagnostics_validation_statuses():
                                     None) == M.MOE_ERR_WORKSPACE_TOO_SMALL
     assert L.moe_router_diagnostics(ctypes.byref(tc), P[0], P[1], P[2], P[3] + 8, P[4], 1 << 30,
                                     None) == M.MOE_ERR_UNSUPPORTED
+
+
+def test_reroute_validation_statuses():
+    L = _lib.lib()
+    rr = M.make_config(64, 64, 4, 2, 128, act="gelu", capacity_factor=1.0, overflow="reroute")
+    dr = M.make_config(64, 64, 4, 2, 128, act="gelu", capacity_factor=1.0)
+    args = (P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], 1 << 30, None)
+    assert L.moe_dispatch_reroute(ctypes.byref(dr), *args) == M.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_dispatch(ctypes.byref(rr), P[0], None, P[2], P[3], P[4], P[5], None, P[6],
+                          1 << 30, None) == M.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_dispatch_reroute(ctypes.byref(rr), P[0], None, *args[2:]) \
+        == M.MOE_ERR_INVALID_ARGUMENT                                    # logits needed
+    assert L.moe_dispatch_reroute(ctypes.byref(rr), *args[:8], 64, None) \
+        == M.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert _route(M.make_config(64, 64, 4, 2, 128, routing="expert", overflow="reroute")) \
+        == M.MOE_ERR_INVALID_ARGUMENT
+    assert _route(M.make_config(64, 64, 4, 2, 128, overflow=3)) == M.MOE_ERR_INVALID_ARGUMENT
+    assert M.moe_workspace_bytes(rr) > M.moe_workspace_bytes(dr)

@@ -20,7 +20,7 @@ from workloads import FULL, make_inputs
 pytestmark = pytest.mark.gpu
 
 SAMPLE = {"toy_fp32": None, "switch_top1": None, "mixtral_decode": None,
-          "mixtral_prefill": 24, "finegrained_shared": 40}
+          "mixtral_prefill": 24, "finegrained_shared": 40, "finegrained_reroute": 40}
 
 
 def _tokens(cfg):
@@ -56,6 +56,8 @@ def test_full_size_parity(name):
     assert np.array_equal(host(got["dest"]), want["dest"])
     total = int(want["offsets"][-1])
     assert np.array_equal(host(got["row_token"])[:total], want["row_token"])
+    if cfg.overflow == "reroute":
+        assert np.array_equal(host(got["final_expert"]), want["final_expert"])
     E = cfg.E
     st = host(got["stats"]).astype(np.float64)
     assert rel_l2(st[:E], want["f"]) <= 1e-6

@@ -46,6 +46,8 @@ def _check_routing_exact(cfg, want, got):
     assert np.array_equal(host(got["dest"]), want["dest"])
     total = int(want["offsets"][-1])
     assert np.array_equal(host(got["row_token"])[:total], want["row_token"])
+    if cfg.overflow == "reroute":
+        assert np.array_equal(host(got["final_expert"]), want["final_expert"])
 
 
 def _check_stats(cfg, want, got):

@@ -178,7 +178,8 @@ def test_capacity_formula_values():
     """'3D mixture-of-experts routing lab', Capacity: C = factor*tokens*k/experts,
     floored; at k = 1 it is 'LLM part 09' s.3's factor * T / E."""
     expect = {"toy_fp32": 40, "switch_top1": 32, "mixtral_decode": 32,
-              "mixtral_prefill": 8192, "finegrained_shared": 1920, "mixtral_prefill_ec": 2048}
+              "mixtral_prefill": 8192, "finegrained_shared": 1920, "mixtral_prefill_ec": 2048,
+              "finegrained_reroute": 1920}
     for name, c in FULL.items():
         assert O.capacity(c.capacity_factor, c.T, c.k, c.E) == expect[name]
     assert O.capacity(1.25, 100, 1, 4) == 31       # floor, not round

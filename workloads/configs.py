@@ -36,6 +36,7 @@ class LayerConfig:
     w_std: float = 0.02
     b_std: float = 0.02          # std of b1/b2 where ffn_bias is set
     routing: str = "token"       # "token": top-k per token; "expert": top-C' per expert
+    overflow: str = "drop"       # "drop" | "reroute": what a full expert does to an assignment
 
     @property
     def dropless(self) -> bool:
@@ -75,7 +76,13 @@ FINEGRAINED = LayerConfig(
 PREFILL_EC = PREFILL.with_(name="mixtral_prefill_ec", cfg_id=6, capacity_factor=1.0,
                            routing="expert")
 
-FULL = {c.name: c for c in (TOY, SWITCH, DECODE, PREFILL, FINEGRAINED, PREFILL_EC)}
+# The fine-grained layer again, with overflow re-routed to lower-ranked
+# experts instead of dropped (its Zipf-biased router overflows 62% of the
+# assignments when they are dropped).
+FINEGRAINED_RR = FINEGRAINED.with_(name="finegrained_reroute", cfg_id=7, overflow="reroute")
+
+FULL = {c.name: c for c in (TOY, SWITCH, DECODE, PREFILL, FINEGRAINED, PREFILL_EC,
+                            FINEGRAINED_RR)}
 
 # Reduced variants: same structure (act, k, noise, bias kind, shared experts,
 # capacity regime), sizes small enough for the CPU oracle to finish in seconds,
@@ -95,6 +102,10 @@ SMALL = {
     "finegrained_ec_small": FINEGRAINED.with_(name="finegrained_ec_small", cfg_id=107, T=1500,
                                               d=256, E=16, k=4, h=192, n_shared=2,
                                               routing="expert"),
+    "finegrained_rr_small": FINEGRAINED_RR.with_(name="finegrained_rr_small", cfg_id=108,
+                                                 T=1500, d=256, E=16, k=4, h=192, n_shared=2),
+    "switch_rr_small": SWITCH.with_(name="switch_rr_small", cfg_id=109, T=1000, d=256, E=16,
+                                    h=384, overflow="reroute"),
 }
 
 
