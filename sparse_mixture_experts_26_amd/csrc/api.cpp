@@ -101,7 +101,8 @@ struct DispatchWs { int32_t* local_rank; int32_t* chunk_hist; };
 struct FfnWs { TileEntry* entries; int32_t* n_entries; };
 struct DiagWs { double* partial_d; int32_t* partial_i; };
 struct RerouteWs {
-  uint8_t* fallback; int32_t* list_a; int32_t* list_b; int32_t* fe; int32_t* rin; int32_t* ptr;
+  uint8_t* fallback; int32_t* list_a; int32_t* list_b; int32_t* fe; int32_t* rin;
+  int32_t* off_prim;
 };
 
 RouteWs carve_route(Carve& cv, const Cfg& c) {
@@ -117,11 +118,11 @@ RerouteWs carve_reroute(Carve& cv, const Cfg& c) {
   RerouteWs w;
   const size_t tk = (size_t)c.T * c.k;
   w.fallback = static_cast<uint8_t*>(cv.take((size_t)c.T * (c.E - c.k)));
-  w.list_a = static_cast<int32_t*>(cv.take(tk * 4));
-  w.list_b = static_cast<int32_t*>(cv.take(tk * 4));
+  w.list_a = static_cast<int32_t*>(cv.take(2 * tk * 4));
+  w.list_b = static_cast<int32_t*>(cv.take(2 * tk * 4));
   w.fe = static_cast<int32_t*>(cv.take(tk * 4));
   w.rin = static_cast<int32_t*>(cv.take(tk * 4));
-  w.ptr = static_cast<int32_t*>(cv.take((size_t)c.T * 4));
+  w.off_prim = static_cast<int32_t*>(cv.take((size_t)(c.E + 1) * 4));
   return w;
 }
 DiagWs carve_diag(Carve& cv, const Cfg& c) {
@@ -370,7 +371,7 @@ moe_status_t moe_dispatch_reroute(const moe_config_t* cfg, const int32_t* topk_i
   r.idx = topk_idx; r.logits = logits; r.counts = counts; r.offsets = offsets;
   r.dest = dest; r.dest_out = dest; r.row_token = row_token; r.final_expert = final_expert;
   r.fallback = rw.fallback; r.list_a = rw.list_a; r.list_b = rw.list_b; r.fe = rw.fe;
-  r.rin = rw.rin; r.ptr = rw.ptr;
+  r.rin = rw.rin; r.off_prim = rw.off_prim;
   r.T = (int)c.T; r.E = (int)c.E; r.k = (int)c.k; r.C = (int)c.C;
   return hip_status(launch_reroute(r, stream));
 }
@@ -607,7 +608,7 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
       r.dest = L.dest; r.dest_out = L.dest; r.row_token = L.row_token;
       r.final_expert = L.final_expert;
       r.fallback = L.rrw.fallback; r.list_a = L.rrw.list_a; r.list_b = L.rrw.list_b;
-      r.fe = L.rrw.fe; r.rin = L.rrw.rin; r.ptr = L.rrw.ptr;
+      r.fe = L.rrw.fe; r.rin = L.rrw.rin; r.off_prim = L.rrw.off_prim;
       r.T = (int)c.T; r.E = (int)c.E; r.k = (int)c.k; r.C = (int)c.C;
       if ((st = hip_status(launch_reroute(r, stream))) != MOE_OK) return st;
     }

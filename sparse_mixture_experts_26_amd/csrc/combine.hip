@@ -67,8 +67,22 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsParams p) {
   // slots left unplaced (re-routing): counted over dest in a fixed order
   __shared__ int lost[256];
   int my_lost = 0;
-  if (p.dest)
-    for (int64_t i = e; i < (int64_t)p.T * p.k; i += 256) my_lost += p.dest[i] < 0;
+  if (p.dest) {
+    const int64_t n = (int64_t)p.T * p.k, n4 = n >> 2;
+    const int4* d4 = reinterpret_cast<const int4*>(p.dest);  // 16-byte aligned
+    int64_t i = e;
+    for (; i + 3 * 256 < n4; i += 4 * 256) {  // four loads in flight
+      const int4 a = d4[i], b = d4[i + 256], c = d4[i + 512], d = d4[i + 768];
+      my_lost += (a.x < 0) + (a.y < 0) + (a.z < 0) + (a.w < 0) + (b.x < 0) + (b.y < 0) +
+                 (b.z < 0) + (b.w < 0) + (c.x < 0) + (c.y < 0) + (c.z < 0) + (c.w < 0) +
+                 (d.x < 0) + (d.y < 0) + (d.z < 0) + (d.w < 0);
+    }
+    for (; i < n4; i += 256) {
+      const int4 v = d4[i];
+      my_lost += (v.x < 0) + (v.y < 0) + (v.z < 0) + (v.w < 0);
+    }
+    for (int64_t i = 4 * n4 + e; i < n; i += 256) my_lost += p.dest[i] < 0;
+  }
   lost[e] = my_lost;
   __syncthreads();
   if (e == 0) {

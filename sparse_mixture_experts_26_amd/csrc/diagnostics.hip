@@ -9,8 +9,9 @@
 //
 // Per-token terms: one wave per token (lane owns experts lane + 64 j), 16
 // tokens per block, partial sums per block in double in a fixed order; a
-// one-block kernel reduces the partials in block order and adds the
-// count-based metrics.  No atomics: results are deterministic.
+// one-block kernel reduces the partials in a fixed order (strided per thread,
+// then over the threads) and adds the count-based metrics.  No atomics:
+// results are deterministic.
 #include "launch.hpp"
 
 namespace moe {
@@ -96,15 +97,33 @@ __global__ __launch_bounds__(256) void diag_final_kernel(DiagParams p, int nbloc
     p.diag[8 + p.E + e] = p.C > 0 ? (float)((double)kept / (double)p.C) : 0.f;
     s_ov[e] = (double)(c - kept);
   }
-  __syncthreads();
-  if (e == 0) {
-    double zs = 0.0, hs = 0.0, var = 0.0, dev = 0.0, ov = 0.0;
+  // partials: thread e sums blocks e, e+256, ... (fixed order), then thread 0
+  // sums the 256 thread sums in order
+  __shared__ double s_zs[256], s_hs[256];
+  __shared__ long long s_full[256], s_part[256];
+  {
+    double zs = 0.0, hs = 0.0;
     long long full = 0, part = 0;
-    for (int b = 0; b < nblocks; ++b) {
+    for (int b = e; b < nblocks; b += 256) {
       zs += p.partial_d[2 * b];
       hs += p.partial_d[2 * b + 1];
       full += p.partial_i[2 * b];
       part += p.partial_i[2 * b + 1];
+    }
+    s_zs[e] = zs;
+    s_hs[e] = hs;
+    s_full[e] = full;
+    s_part[e] = part;
+  }
+  __syncthreads();
+  if (e == 0) {
+    double zs = 0.0, hs = 0.0, var = 0.0, dev = 0.0, ov = 0.0;
+    long long full = 0, part = 0;
+    for (int b = 0; b < 256; ++b) {
+      zs += s_zs[b];
+      hs += s_hs[b];
+      full += s_full[b];
+      part += s_part[b];
     }
     for (int i = 0; i < p.E; ++i) {
       const double c = (double)p.counts[i];

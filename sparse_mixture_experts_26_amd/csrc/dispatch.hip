@@ -143,21 +143,37 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(DispatchParams p) {
 
 __global__ __launch_bounds__(256) void dispatch_scan_kernel(DispatchParams p, int nchunks) {
   __shared__ int skept[256];
-  const int e = threadIdx.x;
-  int kept = 0;
-  if (e < p.E) {
-    int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      int* cell = p.chunk_hist + (int64_t)c * p.E + e;
-      const int v = *cell;
-      *cell = run;  // becomes the chunk's base rank for expert e
-      run += v;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // per expert (one wave each, lanes over 64 chunks at a time): the chunk
+  // histograms become per-chunk base ranks in chunk order, and the total is
+  // the expert's count
+  for (int e = w; e < 256; e += 4) {
+    if (e >= p.E) {
+      if (lane == 0) skept[e] = 0;
+      continue;
     }
-    p.counts[e] = run;
-    kept = run < p.C ? run : p.C;
+    int carry = 0;
+    for (int c0 = 0; c0 < nchunks; c0 += 64) {
+      const int c = c0 + lane;
+      int* cell = p.chunk_hist + (int64_t)c * p.E + e;
+      const int v = c < nchunks ? *cell : 0;
+      int incl = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += u;
+      }
+      if (c < nchunks) *cell = carry + incl - v;
+      carry += __shfl(incl, 63, kWave);
+    }
+    if (lane == 0) {
+      p.counts[e] = carry;
+      skept[e] = carry < p.C ? carry : p.C;
+    }
   }
-  skept[e] = kept;
   __syncthreads();
+  const int e = tid;
+  const int kept = skept[e];
   // Hillis-Steele inclusive scan over 256 experts.
   for (int o = 1; o < 256; o <<= 1) {
     const int v = e >= o ? skept[e - o] : 0;

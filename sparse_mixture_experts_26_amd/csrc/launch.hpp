@@ -55,11 +55,11 @@ struct RerouteParams {
   int32_t* row_token;       // [T*k]
   int32_t* final_expert;    // [T,k]
   uint8_t* fallback;        // [T, E-k] scratch
-  int32_t* list_a;          // [T*k] scratch
-  int32_t* list_b;          // [T*k] scratch
+  int32_t* list_a;          // [2*T*k] scratch: (assignment, pointer) pairs
+  int32_t* list_b;          // [2*T*k] scratch
   int32_t* fe;              // [T*k] scratch
   int32_t* rin;             // [T*k] scratch
-  int32_t* ptr;             // [T] scratch
+  int32_t* off_prim;        // [E+1] scratch: the primary offsets
   int T, E, k, C;
 };
 hipError_t launch_reroute(const RerouteParams& p, hipStream_t stream);

@@ -21,7 +21,8 @@
 //      histograms, a running count per expert across chunks, acceptance
 //      against the expert's load at the start of the round, and an ordered
 //      compaction of the assignments still unplaced;
-//   3. offsets over the final loads, dest, row_token and final_expert.
+//   3. offsets over the final loads (same block), then dest, row_token and
+//      final_expert in a kernel of one thread per assignment.
 // Every step is ordered, so the integer results are exact and deterministic.
 #include "launch.hpp"
 
@@ -82,99 +83,235 @@ __device__ __forceinline__ int rr_excl_count(bool flag, int* wtot, int& total) {
   return before + __popcll(b & ((1ull << lane) - 1ull));
 }
 
+// The rounds, in one block of 1024 threads.  The unplaced list holds pairs
+// (assignment i, its token's fallback pointer at the start of the round) in
+// arrival order.  Chunks of proposals go through a three-stage software
+// pipeline, so no step waits on a dependent global load; a step takes 4096
+// proposals (four per thread, 64 slices of 64 lanes in arrival order):
+//   step s loads the pairs of chunk s+3 into registers,
+//          writes the tokens of chunk s+2 (loaded a step ago) into an LDS ring
+//          of three chunks,
+//          lets each slot of chunk s+1 find, in the ring, its position j among
+//          its token's unplaced slots and how many follow it, and loads its
+//          proposal F[t, ptr + j],
+//          and settles chunk s: ranks per expert (9 ballots per slice, slice
+//          histograms tagged with the chunk number so they need no zeroing),
+//          acceptance against the expert's load at the start of the round,
+//          and the ordered compaction of the rejected pairs, whose token
+//          pointer moves past all of the token's proposals of the round.
+struct Pair { int i, ptr; };
+constexpr int kSub = 4;                        // 1024-proposal sub-chunks per step
+constexpr int kStep = kSub * kRrThreads;       // proposals per step
+constexpr int kSlices = kSub * kRrWaves;       // 64-lane slices per step
+constexpr int kRing = 3 * kStep;
+static_assert(kSlices == 64, "one lane per slice in the scans");
+
 __global__ __launch_bounds__(kRrThreads) void reroute_kernel(RerouteParams p) {
-  __shared__ int hist[kRrWaves][256];   // per-slice counts, then slice bases
-  __shared__ int load[256], run[256], ctot[256], off_prim[257];
-  __shared__ int wtot[kRrWaves];
+  // (tag << 16) | count, then | base; rows padded to 257 words so the scan's
+  // column reads (lane = slice) fall in 64 distinct banks
+  __shared__ uint32_t hist[kSlices][257];
+  __shared__ int load[256], run[256], ctot[256];
+  __shared__ int wtot[kSlices];
+  __shared__ int ring[kRing];              // token of list position pos % kRing
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int E = p.E, k = p.k, C = p.C, nf = p.E - p.k;
   const int n_all = p.T * k;
-  for (int e = tid; e < E; e += kRrThreads) {
-    const int c = p.counts[e];
+  for (int e = tid; e < 256; e += kRrThreads) {
+    const int c = e < E ? p.counts[e] : 0;
     load[e] = c < C ? c : C;
   }
-  for (int e = tid; e <= E; e += kRrThreads) off_prim[e] = p.offsets[e];
-  for (int t = tid; t < p.T; t += kRrThreads) p.ptr[t] = 0;
-  // the unplaced list, in arrival order
+  for (int e = tid; e <= E; e += kRrThreads) p.off_prim[e] = p.offsets[e];
+  for (int x = tid; x < kSlices * 257; x += kRrThreads) (&hist[0][0])[x] = 0u;
+  // the unplaced list, in arrival order, with pointer 0; four slots a thread
   int n = 0;
-  for (int i0 = 0; i0 < n_all; i0 += kRrThreads) {
-    const int i = i0 + tid;
-    const bool un = i < n_all && p.dest[i] < 0;
-    int tot;
-    const int pos = n + rr_excl_count(un, wtot, tot);
-    if (un) {
-      p.list_a[pos] = i;
-      p.fe[i] = -1;
+  for (int i0 = 0; i0 < n_all; i0 += 4 * kRrThreads) {
+    int cnt = 0, fl[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + 4 * tid + u;
+      fl[u] = i < n_all && p.dest[i] < 0;
+      cnt += fl[u];
     }
-    n += tot;
+    int incl = cnt;  // inclusive prefix over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) wtot[w] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int x = 0; x < kRrWaves; ++x) {
+      before += x < w ? wtot[x] : 0;
+      all += wtot[x];
+    }
+    __syncthreads();
+    int pos = n + before + incl - cnt;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (fl[u]) {
+        const int i = i0 + 4 * tid + u;
+        p.list_a[2 * pos] = i;
+        p.list_a[2 * pos + 1] = 0;
+        p.fe[i] = -1;
+        ++pos;
+      }
+    }
+    n += all;
   }
   int* cur = p.list_a;
   int* nxt = p.list_b;
+  uint32_t tag = 0;
   __syncthreads();
+
   for (int round = 0; round <= nf && n > 0; ++round) {
     for (int e = tid; e < 256; e += kRrThreads) run[e] = 0;
-    __syncthreads();
     int m = 0;
-    for (int c0 = 0; c0 < n; c0 += kRrThreads) {
-      const int pos = c0 + tid;
-      const bool valid = pos < n;
-      const int i = valid ? cur[pos] : 0;
-      const int t = i / k;
-      // j = earlier unplaced slots of the same token (contiguous in the list)
-      int j = 0;
-      bool last = true;
-      if (valid) {
-        for (int b = 1; b < k && pos - b >= 0 && cur[pos - b] / k == t; ++b) ++j;
-        last = !(pos + 1 < n && cur[pos + 1] / k == t);
+    // position of this thread's proposal u in step-chunk c
+    auto at = [&](int c, int u) { return c * kStep + u * kRrThreads + tid; };
+    auto load_pair = [&](int pos) -> Pair {
+      Pair r{-1, 0};
+      if (pos < n) {
+        r.i = cur[2 * pos];
+        r.ptr = cur[2 * pos + 1];
       }
-      const int q = valid ? p.ptr[t] + j : 0;
-      const int e = (valid && q < nf) ? (int)p.fallback[(int64_t)t * nf + q] : kNoExpert;
-      // rank among this chunk's proposals to the same expert (slice = wave)
-      for (int x = tid; x < kRrWaves * 256; x += kRrThreads) (&hist[0][0])[x] = 0;
-      __syncthreads();
-      uint64_t peers = ~0ull;
+      return r;
+    };
+    Pair pa[kSub], p1[kSub], pc[kSub];
+    int ec[kSub], cntc[kSub];
 #pragma unroll
-      for (int bit = 0; bit < 9; ++bit) {
-        const bool on = (e >> bit) & 1;
-        const uint64_t bal = __ballot(on);
-        peers &= on ? bal : ~bal;
-      }
-      const int r_slice = __popcll(peers & ((1ull << lane) - 1ull));
-      if (e != kNoExpert && r_slice == 0) hist[w][e] = __popcll(peers);
-      __syncthreads();
-      // slice bases within the chunk, and this chunk's total per expert
-      for (int x = tid; x < E; x += kRrThreads) {
-        int acc = 0;
-        for (int sl = 0; sl < kRrWaves; ++sl) {
-          const int c = hist[sl][x];
-          hist[sl][x] = acc;
-          acc += c;
-        }
-        ctot[x] = acc;
-      }
-      __syncthreads();
-      bool accepted = false, still = false;
-      if (e != kNoExpert) {
-        const int rank = run[e] + hist[w][e] + r_slice;
-        accepted = load[e] + rank < C;
-        still = !accepted;
-        if (accepted) {
-          p.fe[i] = e;
-          p.rin[i] = load[e] + rank;
-        }
-      }
-      // token pointers advance past every proposal of this round (after the
-      // reads above); the last slot of a token in the list writes it
-      __syncthreads();
-      if (valid && last) p.ptr[t] = p.ptr[t] + j + 1;
-      int tot;
-      const int spos = m + rr_excl_count(still, wtot, tot);
-      if (still) nxt[spos] = i;
-      m += tot;
-      for (int x = tid; x < E; x += kRrThreads) run[x] += ctot[x];
-      __syncthreads();
+    for (int u = 0; u < kSub; ++u) {
+      pa[u] = load_pair(at(0, u));
+      p1[u] = Pair{-1, 0};
+      pc[u] = Pair{-1, 0};
+      ec[u] = kNoExpert;
+      cntc[u] = 0;
     }
-    // accepted this round per expert: the proposals ranked below the spare capacity
+    // sub-chunks of step-chunk c that hold proposals (uniform)
+    auto live = [&](int c) {
+      const int left = n - c * kStep;
+      return left <= 0 ? 0 : (left >= kStep ? kSub : (left + kRrThreads - 1) / kRrThreads);
+    };
+    for (int s_ = -2; s_ * kStep < n; ++s_) {
+      Pair pb[kSub];
+      const int live_cur = live(s_), live_2 = live(s_ + 2), live_3 = live(s_ + 3);
+#pragma unroll
+      for (int u = 0; u < kSub; ++u) {
+        pb[u] = u < live_3 ? load_pair(at(s_ + 3, u)) : Pair{-1, 0};  // chunk s+3
+        if (u < live_2) {                  // chunk s+2's tokens into the ring
+          const int pos = at(s_ + 2, u);
+          ring[pos % kRing] = pa[u].i >= 0 ? pa[u].i / k : -1 - pos;
+        }
+      }
+      const bool cur_ok = s_ >= 0;
+      // ---- current chunk s: ballots and slice counts
+      int r_slice[kSub];
+      if (cur_ok) {
+        ++tag;
+#pragma unroll
+        for (int u = 0; u < kSub; ++u) {
+          r_slice[u] = 0;
+          if (u >= live_cur) continue;   // no proposals there: slices stay empty
+          const int e = ec[u];
+          uint64_t peers = ~0ull;
+#pragma unroll
+          for (int bit = 0; bit < 9; ++bit) {
+            const bool on = (e >> bit) & 1;
+            const uint64_t bal = __ballot(on);
+            peers &= on ? bal : ~bal;
+          }
+          r_slice[u] = __popcll(peers & ((1ull << lane) - 1ull));
+          if (e != kNoExpert && r_slice[u] == 0)
+            hist[u * kRrWaves + w][e] = (tag << 16) | (uint32_t)__popcll(peers);
+        }
+      }
+      __syncthreads();  // A: ring and slice counts are in
+      // ---- chunk s+1: position among its token's slots, proposal
+      int en[kSub], cntn[kSub];
+#pragma unroll
+      for (int u = 0; u < kSub; ++u) {
+        en[u] = kNoExpert;
+        cntn[u] = 0;
+        if (p1[u].i >= 0) {
+          const int pos = at(s_ + 1, u);
+          const int t = p1[u].i / k;
+          int jn = 0, after = 0;
+          for (int b = 1; b < k && pos - b >= 0 && ring[(pos - b) % kRing] == t; ++b) ++jn;
+          for (int b = 1; b < k && pos + b < n && ring[(pos + b) % kRing] == t; ++b) ++after;
+          cntn[u] = jn + 1 + after;
+          const int q = p1[u].ptr + jn;
+          if (q < nf) en[u] = p.fallback[(int64_t)t * nf + q];
+        }
+      }
+      if (cur_ok) {
+        // per expert, an exclusive scan over the 64 slices: one wave per
+        // expert, lane = slice
+        for (int x = w; x < E; x += kRrWaves) {
+          const uint32_t h = hist[lane][x];
+          const int c = (h >> 16) == tag ? (int)(h & 0xffffu) : 0;
+          int incl = c;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o, kWave);
+            if (lane >= o) incl += v;
+          }
+          hist[lane][x] = (tag << 16) | (uint32_t)(incl - c);
+          if (lane == 63) ctot[x] = incl;
+        }
+      }
+      __syncthreads();  // B: slice bases and chunk totals are in
+      if (cur_ok) {
+        uint64_t sb[kSub];
+        bool still[kSub];
+#pragma unroll
+        for (int u = 0; u < kSub; ++u) {
+          const int e = ec[u];
+          still[u] = false;
+          if (e != kNoExpert) {
+            const int rank = run[e] + (int)(hist[u * kRrWaves + w][e] & 0xffffu) + r_slice[u];
+            if (load[e] + rank < C) {
+              p.fe[pc[u].i] = e;
+              p.rin[pc[u].i] = load[e] + rank;
+            } else {
+              still[u] = true;
+            }
+          }
+          sb[u] = __ballot(still[u]);
+          if (lane == 0) wtot[u * kRrWaves + w] = __popcll(sb[u]);
+        }
+        __syncthreads();  // C: every slice's count of rejected pairs is in
+        // exclusive scan of the slice counts, lane = slice, in every wave
+        const int wc = wtot[lane];
+        int wincl = wc;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int v = __shfl_up(wincl, o, kWave);
+          if (lane >= o) wincl += v;
+        }
+        const int all = __shfl(wincl, 63, kWave);
+#pragma unroll
+        for (int u = 0; u < kSub; ++u) {
+          const int before = __shfl(wincl - wc, u * kRrWaves + w, kWave);
+          if (still[u]) {
+            const int o = m + before + __popcll(sb[u] & ((1ull << lane) - 1ull));
+            nxt[2 * o] = pc[u].i;
+            nxt[2 * o + 1] = pc[u].ptr + cntc[u];  // past all of the token's proposals
+          }
+        }
+        m += all;
+        for (int x = tid; x < E; x += kRrThreads) run[x] += ctot[x];
+      }
+      // next step: chunk s+1 is current, s+2 becomes s+1, s+3 becomes s+2
+#pragma unroll
+      for (int u = 0; u < kSub; ++u) {
+        pc[u] = p1[u];
+        ec[u] = en[u];
+        cntc[u] = cntn[u];
+        p1[u] = pa[u];
+        pa[u] = pb[u];
+      }
+    }
+    __syncthreads();
     for (int x = tid; x < E; x += kRrThreads) {
       const int spare = C - load[x];
       load[x] += run[x] < spare ? run[x] : spare;
@@ -185,7 +322,6 @@ __global__ __launch_bounds__(kRrThreads) void reroute_kernel(RerouteParams p) {
     n = m;
     __syncthreads();
   }
-  // offsets over the final loads
   if (tid == 0) {
     int acc = 0;
     for (int x = 0; x < E; ++x) {
@@ -194,23 +330,26 @@ __global__ __launch_bounds__(kRrThreads) void reroute_kernel(RerouteParams p) {
     }
     p.offsets[E] = acc;
   }
-  __syncthreads();
-  // final placement of every assignment
-  for (int i = tid; i < n_all; i += kRrThreads) {
-    const int dp = p.dest[i];
-    int e, r;
-    if (dp >= 0) {
-      e = p.idx[i];
-      r = dp - off_prim[e];
-    } else {
-      e = p.fe[i];
-      r = e >= 0 ? p.rin[i] : 0;
-    }
-    const int d = e >= 0 ? p.offsets[e] + r : -1;
-    p.final_expert[i] = e;
-    p.dest_out[i] = d;
-    if (d >= 0) p.row_token[d] = i / k;
+}
+
+// Final placement of every assignment: primary kept rows keep their rank,
+// re-routed ones take theirs from the rounds.
+__global__ __launch_bounds__(256) void reroute_place_kernel(RerouteParams p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)p.T * p.k) return;
+  const int dp = p.dest[i];
+  int e, r;
+  if (dp >= 0) {
+    e = p.idx[i];
+    r = dp - p.off_prim[e];
+  } else {
+    e = p.fe[i];
+    r = e >= 0 ? p.rin[i] : 0;
   }
+  const int d = e >= 0 ? p.offsets[e] + r : -1;
+  p.final_expert[i] = e;
+  p.dest_out[i] = d;
+  if (d >= 0) p.row_token[d] = (int)(i / p.k);
 }
 
 }  // namespace
@@ -219,6 +358,10 @@ hipError_t launch_reroute(const RerouteParams& p, hipStream_t stream) {
   if (p.T > 0 && p.E > p.k)
     hipLaunchKernelGGL(fallback_kernel, dim3((p.T + 3) / 4), dim3(256), 0, stream, p);
   hipLaunchKernelGGL(reroute_kernel, dim3(1), dim3(kRrThreads), 0, stream, p);
+  const int64_t n = (int64_t)p.T * p.k;
+  if (n > 0)
+    hipLaunchKernelGGL(reroute_place_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       stream, p);
   return hipGetLastError();
 }
 
