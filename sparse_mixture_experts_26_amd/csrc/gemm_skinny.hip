@@ -47,6 +47,16 @@ struct UnitDesc {
   const void* A;
 };
 
+// The unit's base pointers are the same for the whole wave; say so, or the
+// buffer resources built from them are taken as per-lane and every load
+// becomes a waterfall loop (which also makes the wait counts conservative).
+__device__ __forceinline__ void* uniform_ptr(const void* q) {
+  const uint64_t v = reinterpret_cast<uint64_t>(q);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+}
+
 template <int ACT>
 __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n_slabs,
                                                               int n_units) {
@@ -68,8 +78,11 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
   const int kl = (lane >> 4) * 8;
   const int total = (u_end - u_begin) * per;
 
-  // Unit descriptor.  The expert's row range and gathered rows are re-read only
-  // when the expert changes (consecutive units are slabs of one expert).
+  // Unit descriptor.  The expert's row range and gathered rows are re-read
+  // only when the expert changes (consecutive units are slabs of one expert):
+  // those loads are needed at once, and waiting for them would also wait for
+  // the stage in flight.  The stage loads themselves are unconditional, so the
+  // compiler's wait counts stay exact.
   int cached_g = -1, cached_rows = 0, cached_r0 = 0;
   uint32_t cached_a[2] = {kOOB, kOOB};
   auto describe = [&](int u, UnitDesc& d) __attribute__((always_inline)) {
@@ -125,27 +138,38 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
         for (int s = 0; s < NB; ++s) acc[mf][nf][s] = f32x4{};
   };
 
+  // `red` is the only memory the waves share: a barrier needs this wave's LDS
+  // operations done, not its loads in flight (which __syncthreads would drain)
+  auto lds_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+  };
+
   struct Stage { u32x4 a[UNR][2], b[UNR][NF][NB]; };
-  // loads of step `st` (0..per-1) of the unit described by d
-  auto load = [&](Stage& sg, const UnitDesc& d, int st) __attribute__((always_inline)) {
+  // loads of step `st` (0..per-1) of the unit described by d; `past` (past the
+  // block's last step) turns every offset out of range: the loads read zeros
+  // and move no data, and the code stays branch-free
+  auto load = [&](Stage& sg, const UnitDesc& d, int st, uint32_t past) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(d.A), (short)0, 0x7fffffff, 0x00020000);
+        uniform_ptr(d.A), (short)0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(d.W), (short)0, (int)(wstride * 2), 0x00020000);
+        uniform_ptr(d.W), (short)0, (int)(wstride * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t u_rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(d.U), (short)0, (int)(wstride * 2), 0x00020000);
+        uniform_ptr(d.U), (short)0, (int)(wstride * 2), 0x00020000);
     const int k0 = kb + st * kStep;
 #pragma unroll
     for (int v = 0; v < UNR; ++v) {
       const int kk = k0 + v * 32 + kl;
-      const uint32_t kadd = kk < ke ? (uint32_t)(k0 + v * 32) * 2u : kOOB;
+      const uint32_t kadd = (kk < ke ? (uint32_t)(k0 + v * 32) * 2u : kOOB) | past;
 #pragma unroll
       for (int mf = 0; mf < 2; ++mf)
-        sg.a[v][mf] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, d.a_off[mf] + kadd, 0, 0);
+        sg.a[v][mf] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, (d.a_off[mf] + kadd) | past, 0, 0);
 #pragma unroll
       for (int nf = 0; nf < NF; ++nf) {
-        sg.b[v][nf][0] = __builtin_amdgcn_raw_buffer_load_b128(w_rs, d.b_off[nf] + kadd, 0, 0);
-        if (GATED) sg.b[v][nf][NB - 1] = __builtin_amdgcn_raw_buffer_load_b128(u_rs, d.b_off[nf] + kadd, 0, 0);
+        sg.b[v][nf][0] = __builtin_amdgcn_raw_buffer_load_b128(w_rs, (d.b_off[nf] + kadd) | past, 0, 0);
+        if (GATED)
+          sg.b[v][nf][NB - 1] =
+              __builtin_amdgcn_raw_buffer_load_b128(u_rs, (d.b_off[nf] + kadd) | past, 0, 0);
       }
     }
   };
@@ -176,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
         for (int s = 0; s < NB; ++s)
 #pragma unroll
           for (int i = 0; i < 4; ++i) red[w][(mf * NF + nf) * NB + s][i][lane] = acc[mf][nf][s][i];
-    __syncthreads();
+    lds_barrier();
     const bool routed = d.g < p.G;
     const int gw = routed ? d.g : d.g - p.G;
     const int slab = u - d.g * n_slabs;
@@ -210,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
         *dst = p.accumulate ? *dst + out : out;
       }
     }
-    __syncthreads();  // red is reused by the next unit
+    lds_barrier();  // red is reused by the next unit
   };
 
   // One continuous pipeline over the block's units: the loads of step i+1 (of
@@ -222,26 +246,29 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
   cd = ld;
   zero_acc();
   Stage s0, s1;
-  load(s0, ld, 0);
-#define MOE_SKINNY_STEP(Scur, Snext, i)                             \
-  {                                                                 \
-    const int nl = (i) + 1;                                         \
-    if (nl < total) {                                               \
-      if (nl % per == 0) describe(u_begin + nl / per, ld);          \
-      load(Snext, ld, nl % per);                                    \
-    }                                                               \
-    compute(Scur);                                                  \
-    if ((i) % per == per - 1) {                                     \
-      finish(cd, u_begin + (i) / per);                              \
-      zero_acc();                                                   \
-      cd = ld;                                                      \
-    }                                                               \
+  load(s0, ld, 0, 0u);
+#define MOE_SKINNY_STEP(Scur, Snext, i)                                    \
+  {                                                                        \
+    const int nl = (i) + 1;                                                \
+    const int nq = nl < total ? nl : total - 1;                            \
+    describe(u_begin + nq / per, ld);                                      \
+    load(Snext, ld, nq % per, nl < total ? 0u : kOOB);                     \
+    compute(Scur);                                                         \
+    if ((i) % per == per - 1) {                                            \
+      finish(cd, u_begin + (i) / per);                                     \
+      zero_acc();                                                          \
+      cd = ld;                                                             \
+    }                                                                      \
   }
-  for (int i = 0; i < total; i += 2) {
+  // the loop body has no exit of its own: an exit between the two steps
+  // would join the loop's back edge with loads still in flight, and the
+  // compiler would then wait for all of them at the top of every iteration
+  int i = 0;
+  for (; i + 1 < total; i += 2) {
     MOE_SKINNY_STEP(s0, s1, i)
-    if (i + 1 >= total) break;
     MOE_SKINNY_STEP(s1, s0, i + 1)
   }
+  if (i < total) MOE_SKINNY_STEP(s0, s1, i)
 #undef MOE_SKINNY_STEP
 }
 
