@@ -120,7 +120,7 @@ def softplus(z: np.ndarray) -> np.ndarray:
     return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
 
 
-def router_logits(x, w_g, b_g=None, w_noise=None, eps=None) -> np.ndarray:
+def router_logits(x, w_g, b_g=None, w_noise=None, eps=None, rounded: bool = True) -> np.ndarray:
     """Router logits H [T,E], returned as float32.
 
     [MoE&SMS] "Mathematical Formulation": one logit per expert from a linear map
@@ -128,7 +128,8 @@ def router_logits(x, w_g, b_g=None, w_noise=None, eps=None) -> np.ndarray:
     with eps ~ N(0,1) supplied by the caller (R6).  An optional per-expert bias
     is added to the linear term ([SMoE-arch] router uses a biased linear layer).
     Computed in float64 and rounded once to float32: these float32 logits are
-    what routing decides on (R2).
+    what routing decides on (R2).  ``rounded=False`` returns the float64 value
+    unrounded (derivative checks of the backward need a smooth map).
     """
     x64 = to_f64(x)
     H = x64 @ to_f64(w_g).T
@@ -141,7 +142,7 @@ def router_logits(x, w_g, b_g=None, w_noise=None, eps=None) -> np.ndarray:
     H32 = H.astype(np.float32)
     if not np.all(np.isfinite(H32)):
         raise FloatingPointError("non-finite router logits")
-    return H32
+    return H32 if rounded else H
 
 
 def select_top_k(H32: np.ndarray, k: int) -> np.ndarray:
@@ -328,7 +329,8 @@ def balance_stats(counts, kept, P, T: int, k: int, E: int) -> dict:
 
 def moe_forward(x, w_g, w1, w2, *, k: int, act: str, capacity_factor: float,
                 w3=None, b_g=None, w_noise=None, eps=None, b1=None, b2=None,
-                ws1=None, ws3=None, ws2=None, logits=None, tokens=None) -> dict:
+                ws1=None, ws3=None, ws2=None, logits=None, tokens=None,
+                overflow: str = "drop", exact_logits: bool = False) -> dict:
     """The whole layer forward, step by step.
 
     1. router logits H (or the supplied float32 ``logits``);
@@ -340,19 +342,23 @@ def moe_forward(x, w_g, w1, w2, *, k: int, act: str, capacity_factor: float,
     ``tokens`` (default all) selects which output rows to compute; steps 1-3
     and the statistics always cover the whole batch, since capacity couples
     tokens through their arrival order ([MoEM] "Routing is conditional on a
-    token and its batch context").
+    token and its batch context").  ``overflow="reroute"`` sends assignments
+    that find their expert full to lower-ranked experts (RR1-RR4) instead of
+    dropping them.  ``exact_logits`` keeps the logits in float64 instead of
+    rounding them to float32 (for derivative checks; the top-k order is still
+    decided in float32).
     """
     T, d = np.asarray(x).shape
     E = np.asarray(w_g).shape[0]
     if logits is None:
-        H = router_logits(x, w_g, b_g, w_noise, eps)
+        H = router_logits(x, w_g, b_g, w_noise, eps, rounded=not exact_logits)
     else:
-        H = np.asarray(logits, np.float32)
+        H = np.asarray(logits, np.float64 if exact_logits else np.float32)
     idx = select_top_k(H, k)
     g = selected_gates(H, idx)
     P = full_softmax(H).mean(axis=0)
     C = capacity(capacity_factor, T, k, E)
-    disp = dispatch(idx, E, C)
+    disp = dispatch_reroute(idx, H, E, min(C, T)) if overflow == "reroute" else dispatch(idx, E, C)
     tokens = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
     want = np.zeros(T, bool)
     want[tokens] = True
@@ -378,6 +384,8 @@ def moe_forward(x, w_g, w1, w2, *, k: int, act: str, capacity_factor: float,
                                  None if ws3 is None else ws3[s])
     y = combine(T, d, idx, g, disp["dest"], rows_out, tokens, shared)
     stats = balance_stats(disp["counts"], disp["kept"], P, T, k, E)
+    if overflow == "reroute":  # RR4: what is left unplaced after re-routing
+        stats["drop_rate"] = float(np.mean(np.asarray(disp["dest"]) < 0)) if T else 0.0
     return {"logits": H, "idx": idx, "gates": g, "prob_mean": P, "capacity": C,
             **disp, **stats, "y": y, "tokens": tokens, "shared": shared}
 
