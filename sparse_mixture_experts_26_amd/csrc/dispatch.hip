@@ -143,34 +143,27 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(DispatchParams p) {
 
 __global__ __launch_bounds__(256) void dispatch_scan_kernel(DispatchParams p, int nchunks) {
   __shared__ int skept[256];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  // per expert (one wave each, lanes over 64 chunks at a time): the chunk
-  // histograms become per-chunk base ranks in chunk order, and the total is
-  // the expert's count
-  for (int e = w; e < 256; e += 4) {
-    if (e >= p.E) {
-      if (lane == 0) skept[e] = 0;
-      continue;
-    }
-    int carry = 0;
-    for (int c0 = 0; c0 < nchunks; c0 += 64) {
-      const int c = c0 + lane;
-      int* cell = p.chunk_hist + (int64_t)c * p.E + e;
-      const int v = c < nchunks ? *cell : 0;
-      int incl = v;
+  const int tid = threadIdx.x;
+  // per expert (one thread each): the chunk histograms become per-chunk base
+  // ranks in chunk order, and the total is the expert's count; the column is
+  // read 16 chunks at a time so that its loads are in flight together
+  constexpr int kBatch = 16;
+  int run = 0;
+  if (tid < p.E) {
+    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+      int* col = p.chunk_hist + (int64_t)c0 * p.E + tid;
+      int v[kBatch];
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += u;
+      for (int j = 0; j < kBatch; ++j) v[j] = c0 + j < nchunks ? col[(int64_t)j * p.E] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (c0 + j < nchunks) col[(int64_t)j * p.E] = run;
+        run += v[j];
       }
-      if (c < nchunks) *cell = carry + incl - v;
-      carry += __shfl(incl, 63, kWave);
     }
-    if (lane == 0) {
-      p.counts[e] = carry;
-      skept[e] = carry < p.C ? carry : p.C;
-    }
+    p.counts[tid] = run;
   }
+  skept[tid] = tid < p.E ? (run < p.C ? run : p.C) : 0;
   __syncthreads();
   const int e = tid;
   const int kept = skept[e];
