@@ -1,5 +1,6 @@
 /*
- * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts layer forward.
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts layer: the
+ * forward pass, and its backward for training.
  *
  * One sparse MoE layer in five steps, each a HIP kernel on the caller's stream:
  *   router logits -> top-k + gates -> counts/capacity/dispatch -> grouped expert
@@ -116,6 +117,13 @@ typedef struct moe_aux {
   int32_t* slot;        /* [T,E]   expert choice only                         */
   float*   diag;        /* [8+2E]  token choice only: moe_router_diagnostics  */
   int32_t* final_expert;/* [T,k]   re-routing only: expert of each slot, -1  */
+  /* Saved for moe_layer_backward.  Rows: the R = moe_routed_rows_bound(cfg)
+   * routed rows, then n_shared blocks of T rows (shared expert s, token t at
+   * row R + s*T + t). */
+  void*    hidden;      /* [R + n_shared*T, h]  config dtype: act(...)       */
+  void*    pre;         /* [R + n_shared*T, h, or 2h for SwiGLU] config dtype:
+                           u = x w1^T (+ b1) in [0,h), then v = x w3^T       */
+  float*   y_rows;      /* [R + n_shared*T, d]  expert outputs before gates  */
 } moe_aux_t;
 
 /* (host) Human-readable name of a status code; never NULL. */
@@ -348,6 +356,69 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w,
                                const void* x, const float* eps, const float* logits_in,
                                void* y, const moe_aux_t* aux, void* ws, size_t ws_bytes,
                                hipStream_t stream);
+
+/*
+ * ---- Backward pass (token choice) ----------------------------------------------
+ *
+ * The pages train these layers but print no backward ([MoE&SMS] Mathematical
+ * Formulation: the router learns through the gate values and L_aux through
+ * P_i, f_i being a hard count; [MoEM] Level 2: routing decisions are
+ * discrete).  The objective differentiated is
+ *     L = <dy, y> + g_aux * L_aux + g_z * L_z
+ * with dy [T,d] float32 the upstream gradient of the layer output, L_aux the
+ * load-balancing loss of moe_combine's statistics and L_z the z-loss of
+ * moe_router_diagnostics.  Held fixed (no gradient): the top-k set, capacity
+ * drops, re-routing and the counts f_i.  The float32 rounding of the logits
+ * is taken as the identity.  Gradients flow through
+ *   - the gates (softmax over the selected logits; a dropped slot's own gate
+ *     gradient is 0, and its logit still receives gradient through the other
+ *     gates, which were not renormalised),
+ *   - P_i:   dL_aux/dH[t,j] = (E/T) p_tj (f_j - sum_i f_i p_ti),
+ *   - L_z:   dL_z/dH[t,j]   = (2/T) lse_t p_tj,
+ *   - softplus of the noise: d/d(x W_noise^T) = dH * eps * sigmoid(x W_noise^T),
+ *   - the expert FFNs (shared experts with weight 1) and the router weights.
+ * Every gradient is float32; dW = sum over rows in float32 from config-dtype
+ * operands (bf16 layers: bf16 MFMA products of bf16-rounded dy, gated rows
+ * and activations).  Deterministic (no atomics).
+ */
+typedef struct moe_grads {
+  float* dx;        /* [T,d]    required                                        */
+  float* dw_g;      /* [E,d]    required                                        */
+  float* db_g;      /* [E]      required when router_bias                       */
+  float* dw_noise;  /* [E,d]    required when router_noise                      */
+  float* dw1;       /* [E,h,d]  required                                        */
+  float* dw3;       /* [E,h,d]  required for SwiGLU                             */
+  float* dw2;       /* [E,d,h]  required                                        */
+  float* db1;       /* [E,h]    required when ffn_bias                          */
+  float* db2;       /* [E,d]    required when ffn_bias                          */
+  float* dws1;      /* [S,h,d]  required when n_shared > 0                      */
+  float* dws3;      /* [S,h,d]  required when n_shared > 0 and SwiGLU           */
+  float* dws2;      /* [S,d,h]  required when n_shared > 0                      */
+} moe_grads_t;
+
+/* (host) Workspace bytes for moe_layer_backward; 0 for an invalid config or
+ * one the backward does not cover (expert choice). */
+size_t moe_backward_workspace_bytes(const moe_config_t* cfg);
+
+/*
+ * Backward of moe_layer_forward for token-choice routing (drop or re-route).
+ *   x, eps       the forward's inputs (eps: [T,E] when router_noise)
+ *   dy           [T,d] float32 upstream gradient of y
+ *   g_aux, g_z   weights of L_aux and of the z-loss in L (0 disables each)
+ *   saved        what moe_layer_forward wrote for this batch; required members:
+ *                logits, topk_idx, topk_gate, counts, offsets, dest, row_token,
+ *                hidden, pre, y_rows (the offsets and dest are the final ones
+ *                when re-routing; counts are the router's)
+ *   grads        outputs, every member float32, overwritten (not accumulated)
+ * The weights must be the ones the forward used.  Workspace: at least
+ * moe_backward_workspace_bytes(cfg).  MOE_ERR_UNSUPPORTED for expert choice
+ * or when a bf16 intermediate would exceed 2^30 elements.
+ */
+moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
+                                const void* x, const float* eps, const float* dy,
+                                float g_aux, float g_z, const moe_aux_t* saved,
+                                const moe_grads_t* grads, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -10,7 +10,8 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, c_char_p, c_double, c_int, c_int32, c_int64, c_size_t, c_void_p
+from ctypes import (POINTER, c_char_p, c_double, c_float, c_int, c_int32, c_int64, c_size_t,
+                    c_void_p)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
@@ -41,7 +42,13 @@ class MoeWeights(ctypes.Structure):
 class MoeAux(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("logits", "topk_idx", "topk_gate", "prob_sum", "counts",
                                         "offsets", "dest", "row_token", "stats", "scores",
-                                        "slot", "diag", "final_expert")]
+                                        "slot", "diag", "final_expert", "hidden", "pre",
+                                        "y_rows")]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("dx", "dw_g", "db_g", "dw_noise", "dw1", "dw3", "dw2",
+                                        "db1", "db2", "dws1", "dws3", "dws2")]
 
 
 class MoeError(RuntimeError):
@@ -83,6 +90,9 @@ def lib() -> ctypes.CDLL:
             "moe_combine_expert_choice": (st, [cfgp] + [vp] * 9),
             "moe_layer_forward": (st, [cfgp, POINTER(MoeWeights), vp, vp, vp, vp,
                                        POINTER(MoeAux), vp, c_size_t, vp]),
+            "moe_backward_workspace_bytes": (c_size_t, [cfgp]),
+            "moe_layer_backward": (st, [cfgp, POINTER(MoeWeights), vp, vp, vp, c_float, c_float,
+                                        POINTER(MoeAux), POINTER(MoeGrads), vp, c_size_t, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -94,7 +104,7 @@ def lib() -> ctypes.CDLL:
 EXPORTS = ("moe_status_string", "moe_capacity", "moe_routed_rows_bound", "moe_workspace_bytes",
            "moe_route", "moe_dispatch", "moe_dispatch_reroute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
            "moe_combine", "moe_router_diagnostics", "moe_expert_choice", "moe_combine_expert_choice",
-           "moe_layer_forward")
+           "moe_layer_forward", "moe_backward_workspace_bytes", "moe_layer_backward")
 
 
 def make_config(T, d, E, k, h, *, act="swiglu", dtype="bf16", capacity_factor=0.0,
@@ -239,3 +249,20 @@ def moe_layer_forward(cfg, weights: dict, x, eps, logits_in, y, aux: dict | None
     _check("moe_layer_forward", lib().moe_layer_forward(
         ctypes.byref(cfg), ctypes.byref(w), _p(x), _p(eps), _p(logits_in), _p(y),
         ctypes.byref(a), wp, wn, _stream(stream)))
+
+
+def moe_backward_workspace_bytes(cfg: MoeConfig) -> int:
+    return lib().moe_backward_workspace_bytes(ctypes.byref(cfg))
+
+
+def moe_layer_backward(cfg, weights: dict, x, eps, dy, g_aux, g_z, saved: dict, grads: dict, ws,
+                       stream=None):
+    """``saved`` maps MoeAux field names to the forward's tensors, ``grads``
+    MoeGrads field names to output tensors."""
+    w = MoeWeights(**{k: _p(v) for k, v in weights.items() if v is not None})
+    a = MoeAux(**{k: _p(v) for k, v in saved.items() if v is not None})
+    g = MoeGrads(**{k: _p(v) for k, v in grads.items() if v is not None})
+    wp, wn = _ws(ws)
+    _check("moe_layer_backward", lib().moe_layer_backward(
+        ctypes.byref(cfg), ctypes.byref(w), _p(x), _p(eps), _p(dy), float(g_aux), float(g_z),
+        ctypes.byref(a), ctypes.byref(g), wp, wn, _stream(stream)))

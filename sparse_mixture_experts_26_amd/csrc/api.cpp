@@ -174,8 +174,8 @@ LayerWs carve_layer(Carve& cv, const Cfg& c, const moe_aux_t* aux) {
     w.slot = static_cast<int32_t*>(pick(aux ? aux->slot : nullptr, (size_t)c.T * c.E * 4));
   }
   const int64_t rows = c.R + c.S * c.T;
-  w.hidden = cv.take((size_t)rows * c.h * c.esz);
-  w.y_rows = static_cast<float*>(cv.take((size_t)rows * c.d * 4));
+  w.hidden = pick(aux ? aux->hidden : nullptr, (size_t)rows * c.h * c.esz);
+  w.y_rows = static_cast<float*>(pick(aux ? aux->y_rows : nullptr, (size_t)rows * c.d * 4));
   w.rw = carve_route(cv, c);
   w.dw = carve_dispatch(cv, c);
   w.fw = carve_ffn(cv, c.R, c.E, c.S, c.T);
@@ -244,6 +244,74 @@ moe_status_t run_down(const Cfg& c, FfnParams p, const void* hidden, const void*
   return hip_status(launch_ffn(p, s));
 }
 
+// ---- backward workspace ----------------------------------------------------------
+struct BwdWs {
+  float* row_gate; float* dg; float* dH; float* dHn; float* noise_pre;
+  float* r_logits; int32_t* r_idx; float* r_gate; float* r_prob_sum; RouteWs rw;
+  float* rpartial;
+  void* dy_lp;                   // dy in the config dtype (bf16 layers)
+  void* w2t; void* w13t;         // transposed weights, routed then shared groups
+  void* duv; float* dxr;         // [rows, Kup] and [rows, d]
+  GroupDesc* desc; int32_t* total;
+  void* dyT; void* xT; void* hidT; void* duT; void* dvT;
+  FfnWs fw;
+};
+
+int64_t padded_rows_bound(const Cfg& c) {
+  return c.R + 63 * c.E + c.S * ((c.T + 63) / 64 * 64);
+}
+
+BwdWs carve_backward(Carve& cv, const Cfg& c, bool noise) {
+  BwdWs w;
+  memset(&w, 0, sizeof(w));
+  const bool swi = c.act == MOE_ACT_SWIGLU;
+  const int64_t kup = swi ? 2 * c.h : c.h;
+  const int64_t rows = c.R + c.S * c.T;
+  const int64_t rp = padded_rows_bound(c);
+  const int64_t groups = c.E + c.S;
+  const size_t te = (size_t)c.T * c.E * 4, tk = (size_t)c.T * c.k * 4;
+  w.row_gate = static_cast<float*>(cv.take((size_t)std::max<int64_t>(c.R, 1) * 4));
+  w.dg = static_cast<float*>(cv.take(tk));
+  w.dH = static_cast<float*>(cv.take(te));
+  if (noise) {
+    w.dHn = static_cast<float*>(cv.take(te));
+    w.noise_pre = static_cast<float*>(cv.take(te));
+    w.r_logits = static_cast<float*>(cv.take(te));
+    w.r_idx = static_cast<int32_t*>(cv.take(tk));
+    w.r_gate = static_cast<float*>(cv.take(tk));
+    w.r_prob_sum = static_cast<float*>(cv.take((size_t)c.E * 4));
+    w.rw = carve_route(cv, c);
+  }
+  w.rpartial = static_cast<float*>(
+      cv.take((size_t)router_wgrad_splits(c.T, c.E, c.d) * c.E * c.d * 4));
+  if (c.bf16) w.dy_lp = cv.take((size_t)c.T * c.d * 2);
+  w.w2t = cv.take((size_t)groups * c.h * c.d * c.esz);
+  w.w13t = cv.take((size_t)groups * c.d * kup * c.esz);
+  w.duv = cv.take((size_t)rows * kup * c.esz);
+  w.dxr = static_cast<float*>(cv.take((size_t)rows * c.d * 4));
+  w.desc = static_cast<GroupDesc*>(cv.take((size_t)groups * sizeof(GroupDesc)));
+  w.total = static_cast<int32_t*>(cv.take(4));
+  w.dyT = cv.take((size_t)c.d * rp * c.esz);
+  w.xT = cv.take((size_t)c.d * rp * c.esz);
+  w.hidT = cv.take((size_t)c.h * rp * c.esz);
+  w.duT = cv.take((size_t)c.h * rp * c.esz);
+  if (swi) w.dvT = cv.take((size_t)c.h * rp * c.esz);
+  const int64_t ent = std::max<int64_t>(ffn_max_entries(c.R, (int)c.E, (int)c.S, (int)c.T),
+                                        wgrad_entries((int)groups, (int)std::max(c.d, c.h)));
+  w.fw.entries = static_cast<TileEntry*>(cv.take((size_t)ent * sizeof(TileEntry)));
+  w.fw.n_entries = static_cast<int32_t*>(cv.take(4));
+  return w;
+}
+
+// the bf16 intermediates the kernels address with 31-bit byte offsets
+bool backward_fits(const Cfg& c) {
+  const int64_t kup = c.act == MOE_ACT_SWIGLU ? 2 * c.h : c.h;
+  const int64_t rows = c.R + c.S * c.T;
+  const int64_t rp = padded_rows_bound(c);
+  return rows * kup < kMaxElems && rows * c.d < kMaxElems && std::max(c.d, c.h) * rp < kMaxElems &&
+         c.T * c.d < kMaxElems && c.d * kup < kMaxElems;
+}
+
 }  // namespace
 
 extern "C" {
@@ -309,6 +377,7 @@ moe_status_t moe_route(const moe_config_t* cfg, const void* x, const void* w_g,
   p.logits = logits; p.idx = topk_idx; p.gate = topk_gate;
   p.prob_partial = carve_route(wv, c).prob_partial;
   p.prob_sum = prob_sum;
+  p.noise_pre = nullptr;
   p.T = (int)c.T; p.d = (int)c.d; p.E = (int)c.E; p.k = (int)c.k; p.bf16 = c.bf16;
   return hip_status(launch_route(p, stream));
 }
@@ -563,7 +632,8 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   if (aux) {
     const void* ap[] = {aux->logits, aux->topk_idx, aux->topk_gate, aux->prob_sum, aux->counts,
                         aux->offsets, aux->dest, aux->row_token, aux->stats, aux->scores,
-                        aux->slot, aux->diag, aux->final_expert};
+                        aux->slot, aux->diag, aux->final_expert, aux->hidden, aux->pre,
+                        aux->y_rows};
     for (const void* q : ap)
       if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
   }
@@ -585,6 +655,7 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   rp.eps = cfg->router_noise ? eps : nullptr;
   rp.logits = logits_in ? const_cast<float*>(logits_in) : L.logits;
   rp.idx = L.idx; rp.gate = L.gate; rp.prob_partial = L.rw.prob_partial; rp.prob_sum = L.prob_sum;
+  rp.noise_pre = nullptr;
   rp.T = (int)c.T; rp.d = (int)c.d; rp.E = (int)c.E; rp.k = (int)c.k; rp.bf16 = c.bf16;
   if ((st = hip_status(launch_route(rp, stream))) != MOE_OK) return st;
 
@@ -631,6 +702,7 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
   up.bias_main = cfg->ffn_bias ? w->b1 : nullptr; up.bias_shared = nullptr;
   up.out = L.hidden; up.out_bf16 = c.bf16; up.accumulate = 0;
   up.N = (int)c.h; up.K = (int)c.d; up.act = c.act;
+  up.pre = aux ? aux->pre : nullptr;
   if ((st = hip_status(launch_ffn(up, stream))) != MOE_OK) return st;
   FfnParams dn = fp;
   dn.a_main = L.hidden; dn.a_shared = L.hidden; dn.gather = nullptr; dn.a_from_c = 1;
@@ -669,6 +741,174 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
     sp.T = (int)c.T; sp.k = (int)c.k; sp.E = (int)c.E; sp.C = (int)c.C;
     if ((st = hip_status(launch_stats(sp, stream))) != MOE_OK) return st;
   }
+  return MOE_OK;
+}
+
+size_t moe_backward_workspace_bytes(const moe_config_t* cfg) {
+  Cfg c;
+  if (check_cfg(cfg, &c) != MOE_OK || c.ec) return 0;
+  Carve cv(nullptr);
+  carve_backward(cv, c, cfg->router_noise != 0);
+  return cv.off + 256;
+}
+
+moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                                const float* eps, const float* dy, float g_aux, float g_z,
+                                const moe_aux_t* sv, const moe_grads_t* gr, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  Cfg c;
+  moe_status_t st = check_cfg(cfg, &c);
+  if (st != MOE_OK) return st;
+  if (c.ec) return MOE_ERR_UNSUPPORTED;
+  const bool swi = c.act == MOE_ACT_SWIGLU, noise = cfg->router_noise != 0;
+  if (!w || !x || !dy || !sv || !gr || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (!w->w_g || !w->w1 || !w->w2 || (swi && !w->w3)) return MOE_ERR_INVALID_ARGUMENT;
+  if (noise && (!w->w_noise || !eps || !gr->dw_noise)) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.S > 0 && (!w->ws1 || !w->ws2 || (swi && !w->ws3))) return MOE_ERR_INVALID_ARGUMENT;
+  if (!sv->logits || !sv->topk_idx || !sv->topk_gate || !sv->counts || !sv->offsets ||
+      !sv->dest || !sv->row_token || !sv->hidden || !sv->pre || !sv->y_rows)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!gr->dx || !gr->dw_g || !gr->dw1 || !gr->dw2 || (swi && !gr->dw3))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (cfg->router_bias && !gr->db_g) return MOE_ERR_INVALID_ARGUMENT;
+  if (cfg->ffn_bias && (!gr->db1 || !gr->db2)) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.S > 0 && (!gr->dws1 || !gr->dws2 || (swi && !gr->dws3))) return MOE_ERR_INVALID_ARGUMENT;
+  if (!isfinite(g_aux) || !isfinite(g_z)) return MOE_ERR_INVALID_ARGUMENT;
+  if (c.d % 8 || c.h % 8) return MOE_ERR_UNSUPPORTED;
+  if (!backward_fits(c)) return MOE_ERR_UNSUPPORTED;
+  const void* ptrs[] = {x, eps, dy, ws, w->w_g, w->w_noise, w->w1, w->w3, w->w2, w->ws1, w->ws3,
+                        w->ws2, sv->logits, sv->topk_idx, sv->topk_gate, sv->counts,
+                        sv->offsets, sv->dest, sv->row_token, sv->hidden, sv->pre, sv->y_rows,
+                        gr->dx, gr->dw_g, gr->db_g, gr->dw_noise, gr->dw1, gr->dw3, gr->dw2,
+                        gr->db1, gr->db2, gr->dws1, gr->dws3, gr->dws2};
+  for (const void* q : ptrs)
+    if (!aligned(q)) return MOE_ERR_UNSUPPORTED;
+  {
+    Carve cv(nullptr);
+    carve_backward(cv, c, noise);
+    if (ws_bytes < cv.off + 256) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  }
+  Carve wv(ws);
+  BwdWs B = carve_backward(wv, c, noise);
+  const int64_t kup = swi ? 2 * c.h : c.h;
+  const int64_t rp = padded_rows_bound(c);
+  const int G = (int)c.E, S = (int)c.S;
+  hipError_t e;
+#define MOE_TRY(call) \
+  if ((e = (call)) != hipSuccess) return MOE_ERR_HIP;
+
+  // 1. gates of the routed rows, gate gradients, logit gradients
+  MOE_TRY(launch_row_gate(sv->dest, sv->topk_gate, c.T * c.k, B.row_gate, stream));
+  if (noise) {
+    RouteParams rp0;
+    rp0.x = x; rp0.w_g = w->w_g; rp0.b_g = cfg->router_bias ? w->b_g : nullptr;
+    rp0.w_noise = w->w_noise; rp0.eps = eps; rp0.logits = B.r_logits; rp0.idx = B.r_idx;
+    rp0.gate = B.r_gate; rp0.prob_partial = B.rw.prob_partial; rp0.prob_sum = B.r_prob_sum;
+    rp0.noise_pre = B.noise_pre;
+    rp0.T = (int)c.T; rp0.d = (int)c.d; rp0.E = (int)c.E; rp0.k = (int)c.k; rp0.bf16 = c.bf16;
+    if (c.T > 0) MOE_TRY(launch_route(rp0, stream));
+  }
+  BwdParams bp;
+  bp.dy = dy; bp.y_rows = sv->y_rows; bp.dest = sv->dest; bp.idx = sv->topk_idx;
+  bp.gate = sv->topk_gate; bp.logits = sv->logits; bp.counts = sv->counts;
+  bp.eps = noise ? eps : nullptr; bp.noise_pre = B.noise_pre;
+  bp.dg = B.dg; bp.dH = B.dH; bp.dHn = noise ? B.dHn : nullptr;
+  bp.dx_rows = B.dxr; bp.dx = gr->dx; bp.g_aux = g_aux; bp.g_z = g_z;
+  bp.rows_bound = c.R; bp.T = (int)c.T; bp.d = (int)c.d; bp.E = (int)c.E; bp.k = (int)c.k;
+  bp.S = S;
+  MOE_TRY(launch_router_backward(bp, stream));
+
+  // 2. router weights
+  MOE_TRY(launch_router_wgrad(B.dH, x, c.bf16, (int)c.T, G, (int)c.d, B.rpartial, gr->dw_g, stream));
+  if (noise)
+    MOE_TRY(launch_router_wgrad(B.dHn, x, c.bf16, (int)c.T, G, (int)c.d, B.rpartial,
+                                gr->dw_noise, stream));
+  if (cfg->router_bias) MOE_TRY(launch_column_sum(B.dH, (int)c.T, G, gr->db_g, stream));
+
+  // 3. transposed weights: w2t[g] = w2[g]^T [h,d]; w13t[g] = [w1[g]^T | w3[g]^T] [d, Kup]
+  const int esz = (int)c.esz;
+  const size_t gsz2 = (size_t)c.h * c.d * c.esz, gsz13 = (size_t)c.d * kup * c.esz;
+  char* w2t = static_cast<char*>(B.w2t);
+  char* w13t = static_cast<char*>(B.w13t);
+  MOE_TRY(launch_transpose(w->w2, G, (int)c.d, (int)c.h, w2t, (int)c.d, 0, esz, stream));
+  MOE_TRY(launch_transpose(w->w1, G, (int)c.h, (int)c.d, w13t, (int)kup, 0, esz, stream));
+  if (swi) MOE_TRY(launch_transpose(w->w3, G, (int)c.h, (int)c.d, w13t, (int)kup, (int)c.h, esz, stream));
+  if (S > 0) {
+    MOE_TRY(launch_transpose(w->ws2, S, (int)c.d, (int)c.h, w2t + G * gsz2, (int)c.d, 0, esz, stream));
+    MOE_TRY(launch_transpose(w->ws1, S, (int)c.h, (int)c.d, w13t + G * gsz13, (int)kup, 0, esz, stream));
+    if (swi)
+      MOE_TRY(launch_transpose(w->ws3, S, (int)c.h, (int)c.d, w13t + G * gsz13, (int)kup, (int)c.h,
+                               esz, stream));
+  }
+
+  // 4. input gradient of the down projection with the activation backward:
+  //    duv[r] = act'(pre[r]) * gate_r * (dy[token(r)] w2)   (config dtype)
+  const void* dy_op = dy;
+  if (c.bf16) {
+    MOE_TRY(launch_to_bf16(dy, c.T * c.d, static_cast<uint16_t*>(B.dy_lp), stream));
+    dy_op = B.dy_lp;
+  }
+  FfnParams fp = ffn_params(c, c.E, sv->offsets, c.R, c.C, B.fw);
+  fp.S = S;
+  FfnParams dd = fp;
+  dd.a_main = dy_op; dd.a_shared = dy_op; dd.gather = sv->row_token; dd.a_from_c = 0;
+  dd.w_main = w2t; dd.w_shared = w2t + G * gsz2; dd.u_main = nullptr; dd.u_shared = nullptr;
+  dd.bias_main = nullptr; dd.bias_shared = nullptr;
+  dd.out = B.duv; dd.out_bf16 = c.bf16; dd.accumulate = 0;
+  dd.N = (int)c.h; dd.K = (int)c.d; dd.act = kActBwd + c.act;
+  dd.pre = sv->pre; dd.row_gate = B.row_gate;
+  MOE_TRY(c.bf16 ? launch_ffn_tiled(dd, stream) : launch_ffn_f32(dd, stream));
+
+  // 5. input gradient of the up projection(s): dx_rows = duv [w1 | w3]
+  FfnParams du = fp;
+  du.a_main = B.duv; du.a_shared = B.duv; du.gather = nullptr; du.a_from_c = 1;
+  du.w_main = w13t; du.w_shared = w13t + G * gsz13; du.u_main = nullptr; du.u_shared = nullptr;
+  du.bias_main = nullptr; du.bias_shared = nullptr;
+  du.out = B.dxr; du.out_bf16 = 0; du.accumulate = 0;
+  du.N = (int)c.d; du.K = (int)kup; du.act = -1;
+  MOE_TRY(launch_ffn(du, stream));
+
+  // 6. dx = expert rows of the token + shared rows + router share
+  MOE_TRY(launch_dx(bp, w->w_g, noise ? w->w_noise : nullptr, c.bf16, stream));
+
+  // 7. weight gradients over each group's rows (transposed, zero-padded blocks)
+  MOE_TRY(launch_group_desc(sv->offsets, G, S, (int)c.T, c.R, B.desc, B.total, stream));
+  PackParams pk;
+  pk.desc = B.desc; pk.total = B.total; pk.row_token = sv->row_token; pk.G = G; pk.S = S;
+  auto pack = [&](const void* src, int src_esz, int64_t ld, int coff, int C, bool gathered,
+                  const float* scale, void* dst) {
+    PackParams q = pk;
+    q.C = C; q.ld = ld; q.coff = coff; q.gathered = gathered; q.row_gate = scale;
+    return launch_pack_t(q, src, src_esz, dst, esz, rp, stream);
+  };
+  MOE_TRY(pack(dy, 4, c.d, 0, (int)c.d, true, B.row_gate, B.dyT));       // (gate * dy)^T
+  MOE_TRY(pack(x, esz, c.d, 0, (int)c.d, true, nullptr, B.xT));          // x^T
+  MOE_TRY(pack(sv->hidden, esz, c.h, 0, (int)c.h, false, nullptr, B.hidT));
+  MOE_TRY(pack(B.duv, esz, kup, 0, (int)c.h, false, nullptr, B.duT));
+  if (swi) MOE_TRY(pack(B.duv, esz, kup, (int)c.h, (int)c.h, false, nullptr, B.dvT));
+  auto wgrad = [&](const void* At, const void* Bt, int M, int N, float* out, float* out_s) {
+    if (!c.bf16)
+      return launch_wgrad_f32(static_cast<const float*>(At), static_cast<const float*>(Bt),
+                              B.desc, G, S, M, N, out, out_s, stream);
+    FfnParams q = fp;
+    q.a_main = At; q.a_shared = At; q.gather = nullptr; q.a_from_c = 0;
+    q.w_main = Bt; q.w_shared = Bt; q.u_main = nullptr; q.u_shared = nullptr;
+    q.bias_main = nullptr; q.bias_shared = nullptr;
+    q.out = out; q.out_shared = out_s; q.out_bf16 = 0; q.accumulate = 0;
+    q.M = M; q.N = N; q.K = 0; q.act = kActWgrad; q.gdesc = B.desc;
+    return launch_ffn_tiled(q, stream);
+  };
+  MOE_TRY(wgrad(B.dyT, B.hidT, (int)c.d, (int)c.h, gr->dw2, gr->dws2));
+  MOE_TRY(wgrad(B.duT, B.xT, (int)c.h, (int)c.d, gr->dw1, gr->dws1));
+  if (swi) MOE_TRY(wgrad(B.dvT, B.xT, (int)c.h, (int)c.d, gr->dw3, gr->dws3));
+  if (cfg->ffn_bias) {
+    PackParams q = pk;
+    q.C = (int)c.h; q.ld = kup; q.coff = 0; q.gathered = 0; q.row_gate = nullptr;
+    MOE_TRY(launch_bias_grad(q, B.duv, esz, gr->db1, stream));
+    q.C = (int)c.d; q.ld = c.d; q.gathered = 1; q.row_gate = B.row_gate;
+    MOE_TRY(launch_bias_grad(q, dy, 4, gr->db2, stream));
+  }
+#undef MOE_TRY
   return MOE_OK;
 }
 

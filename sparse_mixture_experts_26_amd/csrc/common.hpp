@@ -14,6 +14,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // Native 16-byte vector (HIP's uint4 is a wrapper struct the optimiser cannot
 // always keep in registers).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -46,6 +47,27 @@ __device__ __forceinline__ float apply_act(int act, float a, float u) {
   return gelu_f32(a);
 }
 
+// Backward of the activation: from dh (gradient of the hidden value) and the
+// pre-activations u (v: the SwiGLU up projection), the gradients du and dv.
+//   GELU   d/du u Phi(u) = Phi(u) + u phi(u)
+//   ReLU   [u > 0]
+//   SwiGLU d/du silu(u) v = v s (1 + u (1 - s)), d/dv = silu(u), s = 1/(1+e^-u)
+__device__ __forceinline__ void act_backward(int act, float dh, float u, float v, float& du,
+                                             float& dv) {
+  dv = 0.0f;
+  if (act == 2) {
+    const float s = 1.0f / (1.0f + expf(-u));
+    du = dh * v * s * (1.0f + u * (1.0f - s));
+    dv = dh * u * s;
+  } else if (act == 1) {
+    du = u > 0.0f ? dh : 0.0f;
+  } else {
+    const float cdf = 0.5f * (1.0f + erff(u * 0.70710678118654752440f));
+    const float pdf = 0.39894228040143267794f * expf(-0.5f * u * u);
+    du = dh * (cdf + u * pdf);
+  }
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
@@ -66,6 +88,17 @@ struct TileEntry {
   int32_t a_row0;
   int32_t rows;
   int32_t c_row0;
+};
+
+// Reduction layout of one group for the weight gradients: its rows are
+// rows [row0, row0 + rows) of the row-major operands, and in the transposed
+// operands (feature-major, one block per group) its block starts at column
+// poff of a feature row and holds kp = rows rounded up to 64 (zero padded).
+struct GroupDesc {
+  int32_t poff;
+  int32_t kp;
+  int32_t row0;
+  int32_t rows;
 };
 
 }  // namespace moe

@@ -43,12 +43,32 @@ __global__ __launch_bounds__(64) void ffn_f32_kernel(FfnParams p, int col_blocks
   const float* a = A + arow * p.K;
   float acc = 0.f, accu = 0.f;
   for (int c = 0; c < p.K; ++c) acc = fmaf(a[c], W[c], acc);
-  if (p.act == 2) {
+  if (p.act == 2) {  // (the SwiGLU backward form has no second weight set)
     const float* Uw = static_cast<const float*>(routed ? p.u_main : p.u_shared) + wrow;
     for (int c = 0; c < p.K; ++c) accu = fmaf(a[c], Uw[c], accu);
   }
   const float* bias = routed ? p.bias_main : p.bias_shared;
   if (bias) acc += bias[(int64_t)gw * p.N + n];
+  if (p.act >= kActBwd) {
+    // input gradient of the down projection, scaled by the row's gate, through
+    // the activation's backward: du (and dv) from the saved pre-activations
+    const bool swi = p.act == kActBwd + 2;
+    const int64_t ld = swi ? 2 * (int64_t)p.N : p.N;
+    const float g = routed ? p.row_gate[r] : 1.0f;
+    const float* pre = static_cast<const float*>(p.pre) + r * ld;
+    float du, dv;
+    act_backward(p.act - kActBwd, acc * g, pre[n], swi ? pre[p.N + n] : 0.0f, du, dv);
+    float* o = static_cast<float*>(p.out) + r * ld;
+    o[n] = du;
+    if (swi) o[p.N + n] = dv;
+    return;
+  }
+  if (p.act >= 0 && p.pre) {  // pre-activations for the backward
+    const int64_t ld = p.act == 2 ? 2 * (int64_t)p.N : p.N;
+    float* pre = static_cast<float*>(p.pre) + r * ld;
+    pre[n] = acc;
+    if (p.act == 2) pre[p.N + n] = accu;
+  }
   const float o = p.act >= 0 ? apply_act(p.act, acc, accu) : acc;
   float* dst = static_cast<float*>(p.out) + r * p.N + n;
   *dst = p.accumulate ? *dst + o : o;

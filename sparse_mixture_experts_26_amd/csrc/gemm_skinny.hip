@@ -214,10 +214,17 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
       const int f0 = (mf * NF + nf) * NB;
       float a = ((red[0][f0][i][l] + red[1][f0][i][l]) + red[2][f0][i][l]) + red[3][f0][i][l];
       if (bias) a += bias[(int64_t)gw * N + col];
-      float out;
+      float out, up = 0.f;
+      if (GATED)
+        up = ((red[0][f0 + 1][i][l] + red[1][f0 + 1][i][l]) + red[2][f0 + 1][i][l]) +
+             red[3][f0 + 1][i][l];
+      if (ACT >= 0 && p.pre) {  // pre-activations for the backward
+        uint16_t* pre = static_cast<uint16_t*>(p.pre) +
+                        (int64_t)(d.c_row0 + row) * (GATED ? 2 * N : N) + col;
+        pre[0] = f32_to_bf16(a);
+        if (GATED) pre[N] = f32_to_bf16(up);
+      }
       if (GATED) {
-        const float up = ((red[0][f0 + 1][i][l] + red[1][f0 + 1][i][l]) + red[2][f0 + 1][i][l]) +
-                         red[3][f0 + 1][i][l];
         out = silu_f32(a) * up;
       } else if (ACT == 0) {
         out = gelu_f32(a);

@@ -117,7 +117,10 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* offsets
   if (tid == 0) *n_entries = min(base, max_entries);
 }
 
-// ACT: moe_act_t for the up projection (2 = gated SwiGLU), -1 for none.
+// ACT: moe_act_t for the up projection (2 = gated SwiGLU), -1 for none
+// (float32 output); kActBwd + a: the down projection's input gradient with
+// the backward of activation a applied in the epilogue; kActWgrad: the
+// per-group weight gradient, whose reduction runs over the group's rows.
 //
 // Persistent: one block per CU walks tiles.  XCD x (the hardware hands block
 // P to XCD P % 8) owns the contiguous tile range [x*per, (x+1)*per) with
@@ -126,6 +129,7 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* offsets
 template <int ACT>
 __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int n_tiles_n) {
   constexpr bool GATED = ACT == 2;
+  constexpr bool WGRAD = ACT == kActWgrad;
   __shared__ __attribute__((aligned(16))) char L[kSlots * kQuarter];
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform per wave; say so, or LDS-destination and buffer
@@ -138,9 +142,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
   const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3, nq = (gridDim.x + 7 - xcd) >> 3;
   const int per = (tiles + 7) >> 3;
   const int t_end = min(tiles, (xcd + 1) * per);
-  const int K = p.K, N = p.N;
-  const int64_t wstride = (int64_t)N * K;
-  const int nk = (K + BK - 1) / BK;
+  const int N = p.N;
   constexpr uint32_t kOOB = 0x80000000u;
 
   // Operand reads.  Quarter layout: rows of 128 bytes, chunk c of row r at
@@ -172,10 +174,27 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     const TileEntry te = p.entries[e_idx];
     const bool routed = te.group < p.G;
     const int gw = routed ? te.group : te.group - p.G;
-    const uint16_t* W = static_cast<const uint16_t*>(routed ? p.w_main : p.w_shared) + gw * wstride;
-    const uint16_t* U = W;
-    if (GATED) U = static_cast<const uint16_t*>(routed ? p.u_main : p.u_shared) + gw * wstride;
-    const uint16_t* A = static_cast<const uint16_t*>(routed ? p.a_main : p.a_shared);
+    int K = p.K;  // reduction depth of this tile
+    int64_t wstride = (int64_t)N * K;
+    const uint16_t* W;
+    const uint16_t* U;
+    const uint16_t* A;
+    if constexpr (WGRAD) {
+      // the group's blocks of the transposed operands: M (resp. N) feature
+      // rows of kp elements each
+      const GroupDesc gd = p.gdesc[te.group];
+      K = gd.kp;
+      wstride = (int64_t)N * K;
+      A = static_cast<const uint16_t*>(p.a_main) + (int64_t)p.M * gd.poff;
+      W = static_cast<const uint16_t*>(p.w_main) + (int64_t)N * gd.poff;
+      U = W;
+    } else {
+      W = static_cast<const uint16_t*>(routed ? p.w_main : p.w_shared) + gw * wstride;
+      U = W;
+      if (GATED) U = static_cast<const uint16_t*>(routed ? p.u_main : p.u_shared) + gw * wstride;
+      A = static_cast<const uint16_t*>(routed ? p.a_main : p.a_shared);
+    }
+    const int nk = (K + BK - 1) / BK;
     const int n_out0 = n_idx * (GATED ? BR / 2 : BR);
 
     // ---- direct-to-LDS loads.  A quarter is 16 loads of 1 KiB (8 rows x 128
@@ -327,9 +346,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     // needed.
     barrier();
     const float* bias = routed ? p.bias_main : p.bias_shared;
-    // Up projections (ACT >= 0) write the bf16 hidden layer; the down projection
-    // writes float32 (the host only selects this kernel for bf16 layers).
-    constexpr bool OUT_BF16 = ACT >= 0;
+    // Up projections write the bf16 hidden layer (and the bf16 pre-activations
+    // when asked); every other form stages float32 (the host only selects this
+    // kernel for bf16 layers).
+    constexpr bool FWD_ACT = ACT >= 0 && ACT <= 2;
+    constexpr bool BWD_ACT = ACT >= kActBwd && ACT <= kActBwd + 2;
+    constexpr bool OUT_BF16 = FWD_ACT;
     constexpr int NJ = GATED ? 1 : 2;            // 32-column blocks per wave
     constexpr int COLS = NJ * 32;                // columns per wave
     constexpr int esz = OUT_BF16 ? 2 : 4;
@@ -344,52 +366,130 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
       const int c = col0 + nj * 32 + lr;
       bcol[nj] = (bias && c < N) ? bias[(int64_t)gw * N + c] : 0.f;
     }
+    // value(mi, nj, v) of every accumulator -> LDS, then store(row, col, chunk)
+    // for every 16-byte row chunk inside the tile
+    auto emit = [&](auto value, auto store) __attribute__((always_inline)) {
 #pragma unroll
-    for (int pass = 0; pass < 128 / rows_pass; ++pass) {
-      // 1. activation, then registers -> LDS
+      for (int pass = 0; pass < 128 / rows_pass; ++pass) {
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        if ((mi * 32) / rows_pass != pass) continue;
+        for (int mi = 0; mi < 4; ++mi) {
+          if ((mi * 32) / rows_pass != pass) continue;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = (mi * 32 + (v >> 2) * 8 + lh * 4 + (v & 3)) % rows_pass;
+          for (int v = 0; v < 16; ++v) {
+            const int r = (mi * 32 + (v >> 2) * 8 + lh * 4 + (v & 3)) % rows_pass;
 #pragma unroll
-          for (int nj = 0; nj < NJ; ++nj) {
-            float o;
-            if (GATED) {
-              o = silu_f32(acc[mi][0][v] + bcol[0]) * acc[mi][1][v];
-            } else {
-              o = acc[mi][nj][v] + bcol[nj];
-              if (ACT == 0) o = gelu_outlined(o);
-              if (ACT == 1) o = fmaxf(o, 0.f);
+            for (int nj = 0; nj < NJ; ++nj) {
+              const float o = value(mi, nj, v);
+              char* dst = region + r * row_bytes + (nj * 32 + lr) * esz;
+              if (OUT_BF16) *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16(o);
+              else *reinterpret_cast<float*>(dst) = o;
             }
-            char* dst = region + r * row_bytes + (nj * 32 + lr) * esz;
-            if (OUT_BF16) *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16(o);
-            else *reinterpret_cast<float*>(dst) = o;
           }
         }
-      }
-      // 2. LDS -> global in 16-byte chunks (row-contiguous across lanes)
-      constexpr int chunks_row = COLS * esz / 16;
-      constexpr int chunks = rows_pass * chunks_row;
-      for (int c = lane; c < chunks; c += 64) {
-        const int r = c / chunks_row, ch = c - r * chunks_row;
-        const int row = wm * 128 + pass * rows_pass + r;
-        const int colc = col0 + ch * (16 / esz);
-        if (row >= te.rows || colc >= N) continue;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(region + r * row_bytes + ch * 16);
-        const int64_t off = (int64_t)(te.c_row0 + row) * N + colc;
-        if (OUT_BF16) {
-          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + off) = v;
-        } else {
-          f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + off);
-          f32x4 val = __builtin_bit_cast(f32x4, v);
-          if (p.accumulate) val += *dst;
-          *dst = val;
+        // LDS -> global in 16-byte chunks (row-contiguous across lanes)
+        constexpr int chunks_row = COLS * esz / 16;
+        constexpr int chunks = rows_pass * chunks_row;
+        for (int c = lane; c < chunks; c += 64) {
+          const int r = c / chunks_row, ch = c - r * chunks_row;
+          const int row = wm * 128 + pass * rows_pass + r;
+          const int colc = col0 + ch * (16 / esz);
+          if (row >= te.rows || colc >= N) continue;
+          store(row, colc, *reinterpret_cast<const u32x4*>(region + r * row_bytes + ch * 16));
         }
       }
+    };
+    const int64_t crow0 = te.c_row0;
+    if constexpr (FWD_ACT) {
+      uint16_t* out = static_cast<uint16_t*>(p.out);
+      emit(
+          [&](int mi, int nj, int v) __attribute__((always_inline)) {
+            if (GATED) return silu_f32(acc[mi][0][v] + bcol[0]) * acc[mi][1][v];
+            float o = acc[mi][nj][v] + bcol[nj];
+            if (ACT == 0) o = gelu_outlined(o);
+            if (ACT == 1) o = fmaxf(o, 0.f);
+            return o;
+          },
+          [&](int row, int colc, const u32x4& ch) __attribute__((always_inline)) {
+            *reinterpret_cast<u32x4*>(out + (crow0 + row) * N + colc) = ch;
+          });
+      if (p.pre) {
+        // pre-activations for the backward: u (+ bias), then v when gated
+        uint16_t* pre = static_cast<uint16_t*>(p.pre);
+        const int64_t ld = GATED ? 2 * (int64_t)N : N;
+        emit([&](int mi, int nj, int v) __attribute__((always_inline)) { return acc[mi][nj][v] + bcol[nj]; },
+             [&](int row, int colc, const u32x4& ch) __attribute__((always_inline)) {
+               *reinterpret_cast<u32x4*>(pre + (crow0 + row) * ld + colc) = ch;
+             });
+        if (GATED)
+          emit([&](int mi, int, int v) __attribute__((always_inline)) { return acc[mi][1][v]; },
+               [&](int row, int colc, const u32x4& ch) __attribute__((always_inline)) {
+                 *reinterpret_cast<u32x4*>(pre + (crow0 + row) * ld + N + colc) = ch;
+               });
+      }
+    } else if constexpr (BWD_ACT) {
+      // da = gate * (dy W2) per row; du (and dv) from the saved pre-activations
+      constexpr bool SWI = ACT == kActBwd + 2;
+      const int64_t ld = SWI ? 2 * (int64_t)N : N;
+      const uint16_t* pre = static_cast<const uint16_t*>(p.pre);
+      uint16_t* out = static_cast<uint16_t*>(p.out);
+      emit([&](int mi, int nj, int v) __attribute__((always_inline)) { return acc[mi][nj][v]; },
+           [&](int row, int colc, const u32x4& ch) __attribute__((always_inline)) {
+             const int64_t r = crow0 + row;
+             const float g = routed ? p.row_gate[r] : 1.f;
+             const f32x4 da = __builtin_bit_cast(f32x4, ch);
+             const u32x2 uu = *reinterpret_cast<const u32x2*>(pre + r * ld + colc);
+             u32x2 vv = {0u, 0u};
+             if (SWI) vv = *reinterpret_cast<const u32x2*>(pre + r * ld + N + colc);
+             float du[4], dv[4];
+#pragma unroll
+             for (int j = 0; j < 4; ++j) {
+               const uint32_t wu = uu[j >> 1], wv = vv[j >> 1];
+               const float u = bf16_to_f32((uint16_t)(j & 1 ? wu >> 16 : wu & 0xffffu));
+               const float v = bf16_to_f32((uint16_t)(j & 1 ? wv >> 16 : wv & 0xffffu));
+               act_backward(ACT - kActBwd, da[j] * g, u, v, du[j], dv[j]);
+             }
+             u32x2 o;
+             o[0] = f32_to_bf16(du[0]) | ((uint32_t)f32_to_bf16(du[1]) << 16);
+             o[1] = f32_to_bf16(du[2]) | ((uint32_t)f32_to_bf16(du[3]) << 16);
+             *reinterpret_cast<u32x2*>(out + r * ld + colc) = o;
+             if (SWI) {
+               o[0] = f32_to_bf16(dv[0]) | ((uint32_t)f32_to_bf16(dv[1]) << 16);
+               o[1] = f32_to_bf16(dv[2]) | ((uint32_t)f32_to_bf16(dv[3]) << 16);
+               *reinterpret_cast<u32x2*>(out + r * ld + N + colc) = o;
+             }
+           });
+    } else {
+      // float32 rows (down projection, input gradients) or weight gradients
+      float* out = static_cast<float*>(WGRAD && !routed ? p.out_shared : p.out);
+      emit([&](int mi, int nj, int v) __attribute__((always_inline)) { return acc[mi][nj][v] + bcol[nj]; },
+           [&](int row, int colc, const u32x4& ch) __attribute__((always_inline)) {
+             f32x4* dst = reinterpret_cast<f32x4*>(out + (crow0 + row) * N + colc);
+             f32x4 val = __builtin_bit_cast(f32x4, ch);
+             if (p.accumulate) val += *dst;
+             *dst = val;
+           });
     }
   }
+}
+
+// Weight-gradient schedule: every group (routed, then shared) gets the row
+// tiles of its M x N output, whatever its number of rows (a group without
+// rows gets zeros).
+__global__ __launch_bounds__(256) void build_wgrad_tiles_kernel(int groups, int G, int M,
+                                                                TileEntry* entries,
+                                                                int32_t* n_entries) {
+  const int mt = (M + BM - 1) / BM;
+  const int n = groups * mt;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const int g = i / mt, m0 = (i - g * mt) * BM;
+    TileEntry e;
+    e.group = g;
+    e.a_row0 = m0;
+    e.rows = min(BM, M - m0);
+    e.c_row0 = (g < G ? g : g - G) * M + m0;
+    entries[i] = e;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *n_entries = n;
 }
 
 }  // namespace
@@ -397,6 +497,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
 int64_t ffn_max_entries(int64_t rows_bound, int G, int S, int T) {
   return (rows_bound + BM - 1) / BM + G + (int64_t)S * ((T + BM - 1) / BM);
 }
+
+int64_t wgrad_entries(int groups, int M) { return (int64_t)groups * ((M + BM - 1) / BM); }
 
 int device_cus() {
   static int cus = 0;  // CUs of the current device, asked once
@@ -412,17 +514,37 @@ int device_cus() {
 }
 
 hipError_t launch_ffn_tiled(const FfnParams& p, hipStream_t stream) {
-  const int64_t max_entries = ffn_max_entries(p.rows_bound, p.G, p.S, p.T);
+  const bool wgrad = p.act == kActWgrad;
+  const int64_t max_entries =
+      wgrad ? wgrad_entries(p.G + p.S, p.M) : ffn_max_entries(p.rows_bound, p.G, p.S, p.T);
   const bool gated = p.act == 2;
   const int cols = gated ? BR / 2 : BR;
   const int n_tiles_n = (p.N + cols - 1) / cols;
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, stream, p.offsets, p.G, p.S,
-                     p.T, p.rows_bound, (int)max_entries, p.entries, p.n_entries);
+  if (wgrad) {
+    const int blocks = (int)std::min<int64_t>(64, (max_entries + 255) / 256);
+    hipLaunchKernelGGL(build_wgrad_tiles_kernel, dim3(std::max(blocks, 1)), dim3(256), 0, stream,
+                       p.G + p.S, p.G, p.M, p.entries, p.n_entries);
+  } else {
+    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, stream, p.offsets, p.G, p.S,
+                       p.T, p.rows_bound, (int)max_entries, p.entries, p.n_entries);
+  }
   // one resident block per CU (128 KiB of LDS each), never more blocks than tiles
   const int64_t grid = std::min<int64_t>(device_cus(), max_entries * n_tiles_n);
   if (grid > 0) {
     const dim3 g((unsigned)grid), block(kThreads);
     switch (p.act) {
+      case kActWgrad:
+        hipLaunchKernelGGL(ffn_tiled_kernel<kActWgrad>, g, block, 0, stream, p, n_tiles_n);
+        break;
+      case kActBwd + 2:
+        hipLaunchKernelGGL(ffn_tiled_kernel<kActBwd + 2>, g, block, 0, stream, p, n_tiles_n);
+        break;
+      case kActBwd + 1:
+        hipLaunchKernelGGL(ffn_tiled_kernel<kActBwd + 1>, g, block, 0, stream, p, n_tiles_n);
+        break;
+      case kActBwd:
+        hipLaunchKernelGGL(ffn_tiled_kernel<kActBwd>, g, block, 0, stream, p, n_tiles_n);
+        break;
       case 2: hipLaunchKernelGGL(ffn_tiled_kernel<2>, g, block, 0, stream, p, n_tiles_n); break;
       case 1: hipLaunchKernelGGL(ffn_tiled_kernel<1>, g, block, 0, stream, p, n_tiles_n); break;
       case 0: hipLaunchKernelGGL(ffn_tiled_kernel<0>, g, block, 0, stream, p, n_tiles_n); break;

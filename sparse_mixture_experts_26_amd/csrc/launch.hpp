@@ -21,6 +21,7 @@ struct RouteParams {
   float* gate;              // [T,k]
   float* prob_partial;      // [route_blocks(T), E]
   float* prob_sum;          // [E]
+  float* noise_pre;         // [T,E] out: x W_noise^T before softplus, or null
   int T, d, E, k;
   int bf16;
 };
@@ -92,11 +93,26 @@ struct FfnParams {
   int64_t rows_bound;
   int64_t group_bound;
   int N, K;
-  int act;                   // moe_act_t, or -1 for none (down projection)
+  int act;                   // moe_act_t, or -1 for none (down projection); see below
   int bf16;                  // operand dtype
   TileEntry* entries;        // scratch for the tiled path
   int32_t* n_entries;        // scratch
+  // forward (act 0..2): when set, the pre-activations are stored too: row r
+  // holds u = a W^T (+ bias) in [0, N) and, gated, v = a U^T in [N, 2N)
+  void* pre;
+  // act = kActBwd + a: backward of activation a fused into the epilogue
+  // (operand dtype out [rows, 2N when gated else N]: du, then dv), reading
+  // `pre` and scaling every routed row by its gate
+  const float* row_gate;     // [rows_bound] gate of each routed row
+  // act = kActWgrad: per-group weight gradient C_g[M, N] = A_g B_g^T over the
+  // group's transposed, zero-padded row block (gdesc); a_main and w_main are
+  // the transposed operands, out / out_shared the routed / shared outputs
+  int M;
+  const GroupDesc* gdesc;    // [G + S]
+  void* out_shared;
 };
+constexpr int kActBwd = 4;   // act codes 4, 5, 6: GELU, ReLU, SwiGLU backward
+constexpr int kActWgrad = 8;
 int64_t ffn_max_entries(int64_t rows_bound, int G, int S, int T);
 hipError_t launch_ffn(const FfnParams& p, hipStream_t stream);
 
@@ -165,5 +181,63 @@ struct StatsParams {
   int T, k, E, C;
 };
 hipError_t launch_stats(const StatsParams& p, hipStream_t stream);
+
+// ---- backward --------------------------------------------------------------------
+struct BwdParams {
+  const float* dy;           // [T,d] upstream gradient of the layer output
+  const float* y_rows;       // [rows_bound, d] routed expert outputs (forward)
+  const int32_t* dest;       // [T,k]
+  const int32_t* idx;        // [T,k]
+  const float* gate;         // [T,k]
+  const float* logits;       // [T,E]
+  const int32_t* counts;     // [E] routed (primary) counts
+  const float* eps;          // [T,E] noise, or null
+  const float* noise_pre;    // [T,E] x W_noise^T, or null
+  float* dg;                 // [T,k] out: gate gradients
+  float* dH;                 // [T,E] out: logit gradients
+  float* dHn;                // [T,E] out: gradients of x W_noise^T, or null
+  const float* dx_rows;      // [rows_bound + S*T, d] expert input gradients
+  float* dx;                 // [T,d] out
+  float g_aux, g_z;          // weights of L_aux and the z-loss
+  int64_t rows_bound;
+  int T, d, E, k, S;
+};
+hipError_t launch_row_gate(const int32_t* dest, const float* gate, int64_t n, float* row_gate,
+                           hipStream_t stream);
+// gate gradients, then the logit gradients
+hipError_t launch_router_backward(const BwdParams& p, hipStream_t stream);
+int router_wgrad_splits(int64_t T, int64_t E, int64_t d);
+// out[E,d] = G^T x with G [T,E] float32; partial: [splits, E, d] scratch
+hipError_t launch_router_wgrad(const float* G, const void* x, int bf16, int T, int E, int d,
+                               float* partial, float* out, hipStream_t stream);
+hipError_t launch_column_sum(const float* G, int T, int E, float* out, hipStream_t stream);
+hipError_t launch_to_bf16(const float* src, int64_t n, uint16_t* dst, hipStream_t stream);
+// dst[g][c][coff + r] = src[g][r][c], elements of esz bytes
+hipError_t launch_transpose(const void* src, int groups, int R, int C, void* dst, int ld,
+                            int coff, int esz, hipStream_t stream);
+hipError_t launch_group_desc(const int32_t* offsets, int G, int S, int T, int64_t rows_bound,
+                             GroupDesc* desc, int32_t* total, hipStream_t stream);
+// Source addressing of the transposed weight-gradient operands (see GroupDesc).
+struct PackParams {
+  const GroupDesc* desc;     // [G+S]
+  const int32_t* total;      // padded columns in use
+  const int32_t* row_token;  // gathered sources: token of each routed row
+  const float* row_gate;     // scale of each routed row, or null
+  int G, S;
+  int C;                     // features (rows of the transposed block)
+  int64_t ld;                // source elements per row
+  int coff;                  // first source column
+  int gathered;              // source rows are tokens (x, dy), else row-space rows
+};
+hipError_t launch_pack_t(const PackParams& p, const void* src, int src_esz, void* dst,
+                         int dst_esz, int64_t padded_bound, hipStream_t stream);
+hipError_t launch_bias_grad(const PackParams& p, const void* src, int src_esz, float* db,
+                            hipStream_t stream);
+hipError_t launch_wgrad_f32(const float* At, const float* Bt, const GroupDesc* desc, int G,
+                            int S, int M, int N, float* out, float* out_shared,
+                            hipStream_t stream);
+hipError_t launch_dx(const BwdParams& p, const void* w_g, const void* w_noise, int bf16,
+                     hipStream_t stream);
+int64_t wgrad_entries(int groups, int M);
 
 }  // namespace moe

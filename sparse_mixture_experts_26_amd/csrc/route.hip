@@ -131,7 +131,11 @@ __global__ __launch_bounds__(kMaxThreads) void route_kernel(RouteParams p) {
       if (t >= p.T) continue;
       float v = sH[m * ldh + e];
       if (p.b_g) v += p.b_g[e];
-      if (noise) v += p.eps[(int64_t)t * p.E + e] * softplus_f32(sH[m * ldh + p.E + e]);
+      if (noise) {
+        const float n = sH[m * ldh + p.E + e];
+        v += p.eps[(int64_t)t * p.E + e] * softplus_f32(n);
+        if (p.noise_pre) p.noise_pre[(int64_t)t * p.E + e] = n;
+      }
       sH[m * ldh + e] = v;
       p.logits[(int64_t)t * p.E + e] = v;
     }

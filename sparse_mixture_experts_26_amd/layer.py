@@ -131,6 +131,59 @@ class MoeLayer:
         tick("combine")
         return o
 
+    # ---- training ------------------------------------------------------------------
+    def forward_train(self, x, eps=None, logits_in=None, stream=None):
+        """moe_layer_forward that also keeps what moe_layer_backward needs (the
+        pre-activations, hidden layer and expert rows) in this object."""
+        c = self.cfg
+        if not hasattr(self, "pre"):
+            rows = self.rows_bound + c.n_shared * c.T
+            width = (2 if c.act == L.MOE_ACT_SWIGLU else 1) * c.h
+            self.pre = torch.empty((max(rows, 1), width), dtype=self.hidden.dtype,
+                                   device=self.device)
+        aux = {n: self.out[n] for n in ("logits", "topk_idx", "topk_gate", "prob_sum", "counts",
+                                        "offsets", "dest", "row_token", "stats", "scores", "slot",
+                                        "diag", "final_expert")
+               if n in self.out}
+        aux.update(hidden=self.hidden, pre=self.pre, y_rows=self.y_rows)
+        if logits_in is not None:
+            aux.pop("logits")
+        L.moe_layer_forward(c, self.w, x, eps, logits_in, self.out["y"], aux, self.ws, stream)
+        self._saved = dict(aux, logits=logits_in if logits_in is not None else self.out["logits"])
+        return self.out
+
+    def backward(self, x, dy, eps=None, g_aux=0.0, g_z=0.0, stream=None) -> dict:
+        """moe_layer_backward after ``forward_train`` on the same batch: float32
+        gradients of <dy, y> + g_aux L_aux + g_z L_z."""
+        c = self.cfg
+        T, d, E, h, S = c.T, c.d, c.E, c.h, c.n_shared
+        dev = self.device
+        if not hasattr(self, "grads"):
+            f32 = dict(dtype=torch.float32, device=dev)
+            swi = c.act == L.MOE_ACT_SWIGLU
+            g = {"dx": torch.empty((T, d), **f32), "dw_g": torch.empty((E, d), **f32),
+                 "dw1": torch.empty((E, h, d), **f32), "dw2": torch.empty((E, d, h), **f32)}
+            if swi:
+                g["dw3"] = torch.empty((E, h, d), **f32)
+            if c.router_bias:
+                g["db_g"] = torch.empty((E,), **f32)
+            if c.router_noise:
+                g["dw_noise"] = torch.empty((E, d), **f32)
+            if c.ffn_bias:
+                g["db1"] = torch.empty((E, h), **f32)
+                g["db2"] = torch.empty((E, d), **f32)
+            if S:
+                g["dws1"] = torch.empty((S, h, d), **f32)
+                g["dws2"] = torch.empty((S, d, h), **f32)
+                if swi:
+                    g["dws3"] = torch.empty((S, h, d), **f32)
+            self.grads = g
+            self.bws = torch.empty(max(L.moe_backward_workspace_bytes(c), 256), dtype=torch.uint8,
+                                   device=dev)
+        L.moe_layer_backward(c, self.w, x, eps, dy, g_aux, g_z, self._saved, self.grads, self.bws,
+                             stream)
+        return self.grads
+
     def _shared_offsets(self):
         if not hasattr(self, "_soff"):
             self._soff = torch.tensor([0, self.cfg.T], dtype=torch.int32, device=self.device)

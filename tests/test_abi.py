@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     assert set(names) == set(M.EXPORTS)
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
@@ -227,3 +227,48 @@ def test_reroute_validation_statuses():
         == M.MOE_ERR_INVALID_ARGUMENT
     assert _route(M.make_config(64, 64, 4, 2, 128, overflow=3)) == M.MOE_ERR_INVALID_ARGUMENT
     assert M.moe_workspace_bytes(rr) > M.moe_workspace_bytes(dr)
+
+
+def _backward_args(cfg, **over):
+    """Valid-looking (fake, aligned) arguments of moe_layer_backward."""
+    w = _lib.MoeWeights(w_g=P[0], w_noise=P[1], w1=P[2], w3=P[3], w2=P[4], ws1=P[5], ws3=P[6],
+                        ws2=P[7], b_g=P[8])
+    sv = _lib.MoeAux(logits=P[0], topk_idx=P[1], topk_gate=P[2], counts=P[3], offsets=P[4],
+                     dest=P[5], row_token=P[6], hidden=P[7], pre=P[8], y_rows=P[9])
+    g = _lib.MoeGrads(dx=P[0], dw_g=P[1], dw1=P[2], dw3=P[3], dw2=P[4], dws1=P[5], dws3=P[6],
+                      dws2=P[7], dw_noise=P[8], db_g=P[9], db1=P[10], db2=P[11])
+    for k, v in over.items():
+        for st in (w, sv, g):
+            if hasattr(st, k):
+                setattr(st, k, v)
+    return w, sv, g
+
+
+def _bwd(cfg, ws_bytes=1 << 40, g_aux=0.0, **over):
+    w, sv, g = _backward_args(cfg, **over)
+    L = _lib.lib()
+    return L.moe_layer_backward(ctypes.byref(cfg), ctypes.byref(w), P[10], P[11], P[12], g_aux,
+                                0.0, ctypes.byref(sv), ctypes.byref(g), P[13], ws_bytes, None)
+
+
+def test_backward_validation_statuses():
+    """moe_layer_backward rejects missing saved tensors, missing gradient
+    outputs, expert-choice routing, a short workspace and misaligned pointers
+    before any HIP call."""
+    tc = M.make_config(64, 64, 4, 2, 128, act="swiglu", capacity_factor=1.0)
+    noisy = M.make_config(64, 64, 4, 2, 128, act="gelu", router_noise=True)
+    ec = M.make_config(64, 64, 4, 2, 128, act="gelu", capacity_factor=1.0, routing="expert")
+    need = M.moe_backward_workspace_bytes(tc)
+    assert need > M.moe_workspace_bytes(tc)
+    assert M.moe_backward_workspace_bytes(ec) == 0
+    assert M.moe_backward_workspace_bytes(noisy) > M.moe_backward_workspace_bytes(
+        M.make_config(64, 64, 4, 2, 128, act="gelu"))
+    assert _bwd(ec) == M.MOE_ERR_UNSUPPORTED
+    assert _bwd(tc, ws_bytes=need - 1) == M.MOE_ERR_WORKSPACE_TOO_SMALL
+    for missing in ("pre", "hidden", "y_rows", "dest", "logits", "dx", "dw1", "dw3", "w3"):
+        assert _bwd(tc, **{missing: None}) == M.MOE_ERR_INVALID_ARGUMENT, missing
+    assert _bwd(noisy, dw_noise=None) == M.MOE_ERR_INVALID_ARGUMENT
+    assert _bwd(tc, g_aux=float("nan")) == M.MOE_ERR_INVALID_ARGUMENT
+    assert _bwd(tc, pre=P[8] + 8) == M.MOE_ERR_UNSUPPORTED
+    biased = M.make_config(64, 64, 4, 2, 128, act="gelu", ffn_bias=True)
+    assert _bwd(biased, db1=None) == M.MOE_ERR_INVALID_ARGUMENT

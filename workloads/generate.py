@@ -18,6 +18,7 @@ Recipe per tensor (std values come from the config):
   w2       [E, d, h]   N(0, w_std^2)
   b1 [E, h], b2 [E, d] fp32 N(0, b_std^2)                   (ffn_bias only)
   ws1, ws3 [S, h, d], ws2 [S, d, h]   shared experts, N(0, w_std^2)
+  dy       [T, d] fp32 N(0, 1)   upstream gradient of the layer output (backward)
 
 No step of the layer is computed here.
 """
@@ -34,7 +35,7 @@ from .configs import LayerConfig
 TENSOR_IDS = {
     "x": 0, "w_g": 1, "b_g": 2, "w_noise": 3, "eps": 4,
     "w1": 5, "w3": 6, "w2": 7, "b1": 8, "b2": 9,
-    "ws1": 10, "ws3": 11, "ws2": 12,
+    "ws1": 10, "ws3": 11, "ws2": 12, "dy": 13,
 }
 
 
@@ -149,3 +150,9 @@ def to_torch(a: np.ndarray, device="cpu"):
     else:
         t = torch.from_numpy(a)
     return t.to(device) if str(device) != "cpu" else t
+
+
+def make_upstream_grad(cfg: LayerConfig, seed: int = 0) -> np.ndarray:
+    """dy [T, d] float32 ~ N(0, 1): the gradient a training step hands the
+    layer output (the backward's input)."""
+    return _normal(_rng(seed, cfg.cfg_id, "dy"), (cfg.T, cfg.d), 1.0)
