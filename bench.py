@@ -5,7 +5,11 @@ grouped expert GEMMs, shared experts, combine + statistics) over one batch of
 seeded synthetic input already resident in HBM, through the C ABI's stage
 entry points on torch's current stream.  Prints ONE JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--train]
+
+--train times a training step instead: the forward that keeps what the
+backward needs, then moe_layer_backward (gradients of x and of every weight
+for the output gradient, the load-balancing loss and the z-loss).
 
 Workloads: mixtral_prefill (default; the MFMA-bound Mixtral-shaped prefill,
 T=8192, d=4096, 8 experts top-2, SwiGLU h=14336), mixtral_decode, switch_top1,
@@ -117,6 +121,74 @@ def cpu_baseline(cfg, inp, target_s):
                       f"statistics over all {cfg.T}); float64 NumPy; {dt:.1f} s"}
 
 
+def backward_work(cfg, offsets):
+    """Algorithmic FLOPs of the backward: each expert GEMM of the forward
+    twice (input gradient and weight gradient), the router's twice (dW_g and
+    its share of dx, again for the noise weights)."""
+    w = algorithmic_work(cfg, offsets)
+    router = 2.0 * cfg.T * cfg.d * cfg.E * (2 if cfg.router_noise else 1)
+    expert = 2.0 * (w["layer_flops"] - router)
+    return {"expert_flops": expert, "flops": expert + 2.0 * router}
+
+
+def train_step(args, cfg, layer, x, eps):
+    import torch
+    from workloads import make_upstream_grad, to_torch
+
+    dy = to_torch(make_upstream_grad(cfg, args.seed), "cuda")
+    g_aux, g_z = 0.01, 0.001
+    for _ in range(args.warmup):
+        layer.forward_train(x, eps)
+        layer.backward(x, dy, eps, g_aux, g_z)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(args.steps + 1):
+        ev.append(torch.cuda.Event(enable_timing=True))
+        ev.append(torch.cuda.Event(enable_timing=True))
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(args.steps):
+        layer.forward_train(x, eps)
+        ev[2 * i + 1].record()
+        layer.backward(x, dy, eps, g_aux, g_z)
+        ev[2 * i + 2].record()
+    torch.cuda.synchronize()
+    total_ms = ev[0].elapsed_time(ev[2 * args.steps])
+    fwd = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]
+    bwd = [ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(args.steps)]
+    ms_per_step = total_ms / args.steps
+    bwd_ms = float(np.mean(bwd))
+    offsets = layer.out["offsets"].cpu().numpy()
+    work = algorithmic_work(cfg, offsets)
+    bw = backward_work(cfg, offsets)
+    achieved = bw["expert_flops"] / (bwd_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "MoE-layer training tokens/sec at 1 GPU (forward + backward)",
+        "value": round(cfg.T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
+                   "h": cfg.h, "act": cfg.act, "n_shared": cfg.n_shared,
+                   "capacity": int(layer.capacity), "dropless": cfg.dropless,
+                   "parallelism": "single GPU", "g_aux": g_aux, "g_z": g_z},
+        "forward_ms": round(float(np.mean(fwd)), 4),
+        "backward_ms": round(bwd_ms, 4),
+        "step_tflops": round((work["layer_flops"] + bw["flops"]) / (ms_per_step * 1e-3) / 1e12, 2),
+        # the whole backward call against the bf16 MFMA peak: its expert GEMM
+        # FLOPs (input and weight gradients) over its wall time, all of its
+        # layout kernels included
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "moe_layer_backward (whole call)",
+                     "kernel_ms": round(bwd_ms, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +197,8 @@ def main():
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--train", action="store_true",
+                    help="time forward (saving for the backward) + backward")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -145,6 +219,9 @@ def main():
           flush=True)
     layer = MoeLayer(cfg, dev)
     x, eps = dev["x"], dev.get("eps")
+    if args.train:
+        train_step(args, cfg, layer, x, eps)
+        return
 
     if args.calib_copy_mb:
         src = torch.empty(args.calib_copy_mb << 20, dtype=torch.uint8, device="cuda")

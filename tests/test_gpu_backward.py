@@ -71,3 +71,120 @@ def test_backward_parity(name):
     torch.cuda.synchronize()
     for n in checked:
         assert np.array_equal(host(g2[n]), got[n]), n
+
+
+FULL_TC = ["mixtral_prefill", "mixtral_decode", "switch_top1", "finegrained_shared",
+           "finegrained_reroute"]
+
+
+def _slice_grads(inp, cfg, rows_tokens, gates, e, m, dy, shared=False):
+    """The oracle's gradients of expert e's hidden unit m alone: the FFN's
+    hidden units are independent, so dW1[e, m, :], dW3[e, m, :] and
+    dW2[e, :, m] are those of the one-unit FFN on the expert's rows."""
+    w1 = (inp.ws1 if shared else inp.w1)[e][m:m + 1]
+    w2 = (inp.ws2 if shared else inp.w2)[e][:, m:m + 1]
+    w3 = None
+    if cfg.act == "swiglu":
+        w3 = (inp.ws3 if shared else inp.w3)[e][m:m + 1]
+    b1 = None if shared or inp.b1 is None else inp.b1[e][m:m + 1]
+    return O.expert_ffn_backward(inp.x[rows_tokens], w1, w2, cfg.act,
+                                 gates[:, None] * dy[rows_tokens], w3, b1, None)
+
+
+@pytest.mark.parametrize("name", FULL_TC)
+def test_backward_full_size(name):
+    """Full-size batches through the same calls the training bench times,
+    checked on outputs the oracle computes one by one: whole rows and columns
+    of the expert weight gradients (hidden units are independent), dx of
+    sampled tokens (their experts, shared experts and router share), and the
+    router weight gradient in full where the oracle's forward is cheap, else
+    its softmax-backward invariant (every column of dW_g sums to 0 without
+    the z-loss)."""
+    require_gpu()
+    from workloads import FULL
+    cfg = FULL[name]
+    banner(f"backward full {name}")
+    g_aux = 0.5
+    inp = make_inputs(cfg, 0)
+    dy = make_upstream_grad(cfg, 0)
+    H = O.router_logits(inp.x, inp.w_g, inp.b_g, inp.w_noise, inp.eps)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    idx = O.select_top_k(H, k)
+    g = O.selected_gates(H, idx)
+    C = O.capacity(cfg.capacity_factor, T, k, E)
+    disp = (O.dispatch_reroute(idx, H, E, min(C, T)) if cfg.overflow == "reroute"
+            else O.dispatch(idx, E, C))
+    dev = upload(inp)
+    layer = MoeLayer(cfg, weights_of(dev))
+    layer.forward_train(dev["x"], dev.get("eps"), torch.from_numpy(H).cuda())
+    got = layer.backward(dev["x"], torch.from_numpy(dy).cuda(), dev.get("eps"), g_aux, 0.0)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(layer.out["offsets"]), disp["offsets"])
+    tol = y_tol(cfg)
+    offsets, row_token, dest = disp["offsets"], disp["row_token"], disp["dest"]
+    row_gate = np.zeros(int(offsets[-1]))
+    row_gate[dest[dest >= 0]] = g[dest >= 0]
+
+    # expert weight-gradient slices: the busiest and the idlest expert that has rows
+    kept = np.diff(offsets)
+    busy = [int(np.argmax(kept)), int(np.argmin(np.where(kept > 0, kept, kept.max() + 1)))]
+    rng = np.random.default_rng(5)
+    for e in busy:
+        rows = np.arange(offsets[e], offsets[e + 1])
+        for m in rng.choice(cfg.h, 2, replace=False):
+            want = _slice_grads(inp, cfg, row_token[rows], row_gate[rows], e, int(m), dy)
+            assert rel_l2(host(got["dw1"][e, m]), want["dw1"][0]) <= tol, ("dw1", e, m)
+            assert rel_l2(host(got["dw2"][e, :, m]), want["dw2"][:, 0]) <= tol, ("dw2", e, m)
+            if cfg.act == "swiglu":
+                assert rel_l2(host(got["dw3"][e, m]), want["dw3"][0]) <= tol, ("dw3", e, m)
+    for s in range(cfg.n_shared):
+        m = int(rng.integers(cfg.h))
+        want = _slice_grads(inp, cfg, np.arange(T), np.ones(T), s, m, dy, shared=True)
+        assert rel_l2(host(got["dws1"][s, m]), want["dw1"][0]) <= tol, ("dws1", s, m)
+        assert rel_l2(host(got["dws2"][s, :, m]), want["dw2"][:, 0]) <= tol, ("dws2", s, m)
+
+    # dx of sampled tokens, one that lost a slot among them when there is one
+    f = np.asarray(disp["counts"], np.float64) / (T * k)
+    aux = g_aux * O.aux_loss_logit_grad(H, f)
+    lost = np.flatnonzero((dest < 0).any(axis=1))
+    tokens = [0, T - 1] + ([int(lost[0])] if lost.size else [])
+    for t in tokens:
+        dx = np.zeros(cfg.d)
+        dg = np.zeros(k)
+        for s in range(k):
+            r = int(dest[t, s])
+            if r < 0:
+                continue
+            e = int(np.searchsorted(offsets, r, side="right") - 1)
+            res = O.expert_ffn_backward(inp.x[t:t + 1], inp.w1[e], inp.w2[e], cfg.act,
+                                        g[t, s] * dy[t:t + 1],
+                                        None if inp.w3 is None else inp.w3[e],
+                                        None if inp.b1 is None else inp.b1[e],
+                                        None if inp.b2 is None else inp.b2[e])
+            dx += res["dx"][0]
+            dg[s] = float(dy[t] @ res["y"][0])
+        for s in range(cfg.n_shared):
+            dx += O.expert_ffn_backward(inp.x[t:t + 1], inp.ws1[s], inp.ws2[s], cfg.act,
+                                        dy[t:t + 1],
+                                        None if inp.ws3 is None else inp.ws3[s])["dx"][0]
+        dH = aux[t:t + 1].copy()
+        dH[0, idx[t]] += O.gate_softmax_backward(g[t:t + 1], dg[None, :])[0]
+        dx += O.router_backward(inp.x[t:t + 1], inp.w_g, dH, inp.w_noise,
+                                None if inp.eps is None else inp.eps[t:t + 1])["dx"][0]
+        assert rel_l2(host(got["dx"][t]), dx) <= tol, ("dx", t)
+
+    dw_g = host(got["dw_g"])
+    if T * k * cfg.d * cfg.h <= 2e10:  # the whole oracle backward is cheap here
+        want = O.moe_backward(inp.x, inp.w_g, inp.w1, inp.w2, k=k, act=cfg.act,
+                              capacity_factor=cfg.capacity_factor, dy=dy, g_aux=g_aux,
+                              w3=inp.w3, b_g=inp.b_g, w_noise=inp.w_noise, eps=inp.eps,
+                              b1=inp.b1, b2=inp.b2, ws1=inp.ws1, ws3=inp.ws3, ws2=inp.ws2,
+                              logits=H, overflow=cfg.overflow)
+        assert rel_l2(dw_g, want["dw_g"]) <= tol
+        if want["dw_noise"] is not None:
+            assert rel_l2(host(got["dw_noise"]), want["dw_noise"]) <= tol
+    col = np.abs(dw_g.astype(np.float64).sum(axis=0))
+    assert col.max() <= 1e-4 * np.abs(dw_g).sum(axis=0).max() + 1e-6
+    if "db_g" in got:
+        db = host(got["db_g"]).astype(np.float64)
+        assert abs(db.sum()) <= 1e-4 * np.abs(db).sum() + 1e-6
