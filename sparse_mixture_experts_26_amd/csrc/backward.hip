@@ -189,6 +189,7 @@ __global__ __launch_bounds__(256) void to_bf16_kernel(const float* src, int64_t 
 }
 
 // dst[g][c][coff + r] = src[g][r][c] for r < R, c < C (64 x 64 tiles via LDS).
+// Scalar form, for float32 layers.
 template <typename TE>
 __global__ __launch_bounds__(256) void transpose_kernel(const TE* src, int R, int C, TE* dst,
                                                         int ld, int coff) {
@@ -207,6 +208,39 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TE* src, int R, in
     const int cc = i / 64, rr = i % 64;
     const int r = r0 + rr, c = c0 + cc;
     if (r < R && c < C) o[(int64_t)c * ld + coff + r] = tile[rr][cc];
+  }
+}
+
+// The same for 16-bit elements with 16-byte accesses (R, C, ld, coff multiples
+// of 8): 8 lanes load one 128-byte input row segment and 8 lanes store one
+// 128-byte output row segment; rows of the LDS tile are padded to 66 elements
+// so the column reads of 8 rows 8 apart hit distinct banks.
+__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* src, int R, int C,
+                                                          uint16_t* dst, int ld, int coff) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][66];
+  const int g = blockIdx.z;
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const uint16_t* s = src + (int64_t)g * R * C;
+  uint16_t* o = dst + (int64_t)g * C * ld;
+  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+    const int rr = i >> 3, ch = i & 7;
+    const int r = r0 + rr, c = c0 + ch * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < R && c < C) v = *reinterpret_cast<const u32x4*>(s + (int64_t)r * C + c);
+    uint32_t* t = reinterpret_cast<uint32_t*>(&tile[rr][ch * 8]);  // 4-byte aligned rows
+#pragma unroll
+    for (int q = 0; q < 4; ++q) t[q] = v[q];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+    const int cc = i >> 3, ch = i & 7;
+    const int c = c0 + cc, r = r0 + ch * 8;
+    if (c >= C || r >= R) continue;
+    u32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = (uint32_t)tile[ch * 8 + 2 * q][cc] | ((uint32_t)tile[ch * 8 + 2 * q + 1][cc] << 16);
+    *reinterpret_cast<u32x4*>(o + (int64_t)c * ld + coff + r) = v;
   }
 }
 
@@ -264,14 +298,18 @@ __device__ __forceinline__ int group_of(const GroupDesc* desc, int groups, int q
 }
 
 // Transposed, zero-padded operand of the weight gradients:
-//   dst[M*poff_g + c*kp_g + j] = scale(row) * src[srow(row), coff + c]
+//   dst[C*poff_g + c*kp_g + j] = scale(row) * src[srow(row), coff + c]
 // for the group's rows j < rows_g (row = row0_g + j), 0 for rows_g <= j < kp_g.
 // srow: the token of the row (gathered sources: x, dy) or the row itself
 // (hidden, du, dv); scale: the row's gate for routed rows of dy, else 1.
-// Block: 64 padded columns x 64 features.
+// Block: 64 padded columns x 64 features.  Sources are read in 16-byte chunks
+// along the features, results written in 16-byte chunks along the rows (8
+// lanes per 128-byte segment; C, ld and coff are multiples of 8); the float
+// tile's rows are padded to 65 words so 8 rows 8 apart hit distinct banks.
 template <typename TS, typename TD>
 __global__ __launch_bounds__(256) void pack_t_kernel(PackParams p, const TS* src, TD* dst) {
   __shared__ float tile[64][65];
+  constexpr int EPC = 16 / sizeof(TS);  // source elements per 16-byte chunk
   const int q0 = blockIdx.x * 64;
   const int f0 = blockIdx.y * 64;
   if (q0 >= *p.total) return;
@@ -280,33 +318,48 @@ __global__ __launch_bounds__(256) void pack_t_kernel(PackParams p, const TS* src
   const GroupDesc gd = p.desc[g];
   const bool routed = g < p.G;
   const int j0 = q0 - gd.poff;  // first group-local row of the block
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int jj = i / 64, ff = i % 64;
-    const int j = j0 + jj, f = f0 + ff;
-    float v = 0.f;
+  constexpr int CPR = 64 / EPC;  // chunks per tile row
+  for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
+    const int jj = i / CPR, ch = i % CPR;
+    const int j = j0 + jj, f = f0 + ch * EPC;
+    float v[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) v[e] = 0.f;
     if (j < gd.rows && f < p.C) {
       const int64_t row = (int64_t)gd.row0 + j;
       int64_t srow = row;
       if (p.gathered) srow = routed ? p.row_token[row] : j;
-      float sc = 1.f;
-      if (p.row_gate && routed) sc = p.row_gate[row];
-      const TS x = src[srow * p.ld + p.coff + f];
-      if constexpr (sizeof(TS) == 2) v = bf16_to_f32(x);
-      else v = x;
-      v *= sc;
+      const float sc = (p.row_gate && routed) ? p.row_gate[row] : 1.f;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(src + srow * p.ld + p.coff + f);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        if constexpr (sizeof(TS) == 2)
+          v[e] = bf16_to_f32((uint16_t)(e & 1 ? x[e >> 1] >> 16 : x[e >> 1] & 0xffffu)) * sc;
+        else
+          v[e] = __uint_as_float(x[e]) * sc;
+      }
     }
-    tile[jj][ff] = v;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) tile[jj][ch * EPC + e] = v[e];
   }
   __syncthreads();
   TD* o = dst + (int64_t)p.C * gd.poff;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int ff = i / 64, jj = i % 64;
+  constexpr int DPC = 16 / sizeof(TD);  // destination elements per 16-byte chunk
+  for (int i = threadIdx.x; i < 64 * (64 / DPC); i += 256) {
+    const int ff = i / (64 / DPC), ch = i % (64 / DPC);
     const int f = f0 + ff;
     if (f >= p.C) continue;
-    const float v = tile[jj][ff];
-    TD* d = o + (int64_t)f * gd.kp + j0 + jj;
-    if constexpr (sizeof(TD) == 2) *d = f32_to_bf16(v);
-    else *d = v;
+    u32x4 w;
+    if constexpr (sizeof(TD) == 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        w[q] = (uint32_t)f32_to_bf16(tile[ch * 8 + 2 * q][ff]) |
+               ((uint32_t)f32_to_bf16(tile[ch * 8 + 2 * q + 1][ff]) << 16);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = __float_as_uint(tile[ch * 4 + q][ff]);
+    }
+    *reinterpret_cast<u32x4*>(o + (int64_t)f * gd.kp + j0 + ch * DPC) = w;
   }
 }
 
@@ -459,7 +512,7 @@ hipError_t launch_transpose(const void* src, int groups, int R, int C, void* dst
   const dim3 grid((C + 63) / 64, (R + 63) / 64, groups);
   if (groups <= 0 || R <= 0 || C <= 0) return hipGetLastError();
   if (esz == 2)
-    hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, stream,
                        static_cast<const uint16_t*>(src), R, C, static_cast<uint16_t*>(dst), ld,
                        coff);
   else
