@@ -412,7 +412,8 @@ size_t moe_backward_workspace_bytes(const moe_config_t* cfg);
  *   grads        outputs, every member float32, overwritten (not accumulated)
  * The weights must be the ones the forward used.  Workspace: at least
  * moe_backward_workspace_bytes(cfg).  MOE_ERR_UNSUPPORTED for expert choice
- * or when a bf16 intermediate would exceed 2^30 elements.
+ * when a bf16 intermediate would exceed 2^30 elements, or when E + n_shared
+ * > 512.
  */
 moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
                                 const void* x, const float* eps, const float* dy,

@@ -255,6 +255,7 @@ struct BwdWs {
   GroupDesc* desc; int32_t* total;
   void* dyT; void* xT; void* hidT; void* duT; void* dvT;
   FfnWs fw;
+  int32_t* xcd_bounds;
 };
 
 int64_t padded_rows_bound(const Cfg& c) {
@@ -300,6 +301,7 @@ BwdWs carve_backward(Carve& cv, const Cfg& c, bool noise) {
                                         wgrad_entries((int)groups, (int)std::max(c.d, c.h)));
   w.fw.entries = static_cast<TileEntry*>(cv.take((size_t)ent * sizeof(TileEntry)));
   w.fw.n_entries = static_cast<int32_t*>(cv.take(4));
+  w.xcd_bounds = static_cast<int32_t*>(cv.take(16 * 4));
   return w;
 }
 
@@ -775,7 +777,7 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   if (c.S > 0 && (!gr->dws1 || !gr->dws2 || (swi && !gr->dws3))) return MOE_ERR_INVALID_ARGUMENT;
   if (!isfinite(g_aux) || !isfinite(g_z)) return MOE_ERR_INVALID_ARGUMENT;
   if (c.d % 8 || c.h % 8) return MOE_ERR_UNSUPPORTED;
-  if (!backward_fits(c)) return MOE_ERR_UNSUPPORTED;
+  if (!backward_fits(c) || c.E + c.S > 512) return MOE_ERR_UNSUPPORTED;
   const void* ptrs[] = {x, eps, dy, ws, w->w_g, w->w_noise, w->w1, w->w3, w->w2, w->ws1, w->ws3,
                         w->ws2, sv->logits, sv->topk_idx, sv->topk_gate, sv->counts,
                         sv->offsets, sv->dest, sv->row_token, sv->hidden, sv->pre, sv->y_rows,
@@ -895,7 +897,7 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
     q.w_main = Bt; q.w_shared = Bt; q.u_main = nullptr; q.u_shared = nullptr;
     q.bias_main = nullptr; q.bias_shared = nullptr;
     q.out = out; q.out_shared = out_s; q.out_bf16 = 0; q.accumulate = 0;
-    q.M = M; q.N = N; q.K = 0; q.act = kActWgrad; q.gdesc = B.desc;
+    q.M = M; q.N = N; q.K = 0; q.act = kActWgrad; q.gdesc = B.desc; q.xcd_bounds = B.xcd_bounds;
     return launch_ffn_tiled(q, stream);
   };
   MOE_TRY(wgrad(B.dyT, B.hidT, (int)c.d, (int)c.h, gr->dw2, gr->dws2));

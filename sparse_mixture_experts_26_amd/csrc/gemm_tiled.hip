@@ -140,8 +140,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
   const int n_entries = *p.n_entries;
   const int tiles = n_entries * n_tiles_n;
   const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3, nq = (gridDim.x + 7 - xcd) >> 3;
+  // weight gradients: tiles differ in depth, so the XCD ranges balance work
+  // (computed with the schedule); otherwise equal tile counts
   const int per = (tiles + 7) >> 3;
-  const int t_end = min(tiles, (xcd + 1) * per);
+  const int t_begin = WGRAD ? p.xcd_bounds[xcd] : xcd * per;
+  const int t_end = WGRAD ? p.xcd_bounds[xcd + 1] : min(tiles, (xcd + 1) * per);
   const int N = p.N;
   constexpr uint32_t kOOB = 0x80000000u;
 
@@ -164,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     rb[ni] = br & 127;
   }
 
-  for (int t = xcd * per + q; t < t_end; t += nq) {
+  for (int t = t_begin + q; t < t_end; t += nq) {
     // groups of 8 row tiles sweep the columns together
     const int per_group = kGroupM * n_tiles_n;
     const int grp = t / per_group, rem = t - grp * per_group;
@@ -474,13 +477,23 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
 
 // Weight-gradient schedule: every group (routed, then shared) gets the row
 // tiles of its M x N output, whatever its number of rows (a group without
-// rows gets zeros).
+// rows gets zeros).  A tile's depth is its group's padded row count, so the
+// 8 XCD ranges are cut where the running work (stages + a fixed per-tile
+// cost) crosses each eighth: a heavily loaded expert spreads over several
+// XCDs instead of holding one back.  One block.
+constexpr int kMaxGroups = 512;  // routed + shared groups a schedule may hold
+
 __global__ __launch_bounds__(256) void build_wgrad_tiles_kernel(int groups, int G, int M,
+                                                                int n_tiles_n,
+                                                                const GroupDesc* gdesc,
                                                                 TileEntry* entries,
-                                                                int32_t* n_entries) {
+                                                                int32_t* n_entries,
+                                                                int32_t* xcd_bounds) {
+  __shared__ long long scan[256];
+  const int tid = threadIdx.x;
   const int mt = (M + BM - 1) / BM;
   const int n = groups * mt;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+  for (int i = tid; i < n; i += 256) {
     const int g = i / mt, m0 = (i - g * mt) * BM;
     TileEntry e;
     e.group = g;
@@ -489,7 +502,49 @@ __global__ __launch_bounds__(256) void build_wgrad_tiles_kernel(int groups, int 
     e.c_row0 = (g < G ? g : g - G) * M + m0;
     entries[i] = e;
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) *n_entries = n;
+  const int tiles = n * n_tiles_n;
+  __shared__ int s_kp[kMaxGroups];
+  for (int g = tid; g < min(groups, kMaxGroups); g += 256) s_kp[g] = gdesc[g].kp / BK + 8;
+  __syncthreads();
+  // tile t -> its entry, as the GEMM decomposes it
+  auto work = [&](int t) {
+    const int per_group = kGroupM * n_tiles_n;
+    const int grp = t / per_group, rem = t - grp * per_group;
+    const int gsize = min(kGroupM, n - grp * kGroupM);
+    const int e_idx = grp * kGroupM + rem % gsize;
+    return (long long)s_kp[min(e_idx / mt, kMaxGroups - 1)];
+  };
+  // each thread a contiguous chunk of tiles: chunk sums, an exclusive scan
+  // over the chunks, then every thread cuts inside its own chunk
+  const int chunk = (tiles + 255) / 256;
+  const int t0 = min(tiles, tid * chunk), t1 = min(tiles, t0 + chunk);
+  long long part = 0;
+  for (int t = t0; t < t1; ++t) part += work(t);
+  scan[tid] = part;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const long long v = tid >= o ? scan[tid - o] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  const long long total = scan[255];
+  long long run = scan[tid] - part;  // work before this chunk
+  // XCD x starts at the first tile whose running work reaches x/8 of the total
+  for (int t = t0; t < t1; ++t) {
+    const long long before = run;
+    run += work(t);
+    for (int x = 1; x < 8; ++x)
+      if (before * 8 < total * x && run * 8 >= total * x) xcd_bounds[x] = t + 1;
+  }
+  if (tid == 0) {
+    xcd_bounds[0] = 0;
+    xcd_bounds[8] = tiles;
+    *n_entries = n;
+  }
+  // every tile weighs at least 8, so with tiles every eighth is crossed
+  // exactly once above; without tiles every range is empty
+  if (tiles == 0 && tid >= 1 && tid < 8) xcd_bounds[tid] = 0;
 }
 
 }  // namespace
@@ -521,15 +576,17 @@ hipError_t launch_ffn_tiled(const FfnParams& p, hipStream_t stream) {
   const int cols = gated ? BR / 2 : BR;
   const int n_tiles_n = (p.N + cols - 1) / cols;
   if (wgrad) {
-    const int blocks = (int)std::min<int64_t>(64, (max_entries + 255) / 256);
-    hipLaunchKernelGGL(build_wgrad_tiles_kernel, dim3(std::max(blocks, 1)), dim3(256), 0, stream,
-                       p.G + p.S, p.G, p.M, p.entries, p.n_entries);
+    hipLaunchKernelGGL(build_wgrad_tiles_kernel, dim3(1), dim3(256), 0, stream, p.G + p.S, p.G,
+                       p.M, n_tiles_n, p.gdesc, p.entries, p.n_entries, p.xcd_bounds);
   } else {
     hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, stream, p.offsets, p.G, p.S,
                        p.T, p.rows_bound, (int)max_entries, p.entries, p.n_entries);
   }
-  // one resident block per CU (128 KiB of LDS each), never more blocks than tiles
-  const int64_t grid = std::min<int64_t>(device_cus(), max_entries * n_tiles_n);
+  // one resident block per CU (160 KiB of LDS each), never more blocks than
+  // tiles; the weight gradients' work-balanced XCD ranges need a block on
+  // every XCD (block P serves XCD P % 8), so at least 8 there
+  int64_t grid = std::min<int64_t>(device_cus(), max_entries * n_tiles_n);
+  if (wgrad) grid = std::max<int64_t>(grid, 8);
   if (grid > 0) {
     const dim3 g((unsigned)grid), block(kThreads);
     switch (p.act) {

@@ -110,6 +110,7 @@ struct FfnParams {
   int M;
   const GroupDesc* gdesc;    // [G + S]
   void* out_shared;
+  int32_t* xcd_bounds;       // [9] scratch: each XCD's tile range
 };
 constexpr int kActBwd = 4;   // act codes 4, 5, 6: GELU, ReLU, SwiGLU backward
 constexpr int kActWgrad = 8;
