@@ -26,8 +26,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int NF = 2;      // 16-column fragments per unit: 32 output columns
-constexpr int kCols = NF * 16;
+constexpr int kMaxNF = 4;  // 16-column fragments per unit: 32 or 64 output columns
 constexpr int UNR = 2;     // 32-deep k-steps per pipeline stage
 constexpr int kStep = 32 * UNR;  // depth of one pipeline stage
 constexpr uint32_t kOOB = 0x80000000u;
@@ -41,7 +40,7 @@ constexpr int kBlocksPerCU = MOE_SKINNY_BLOCKS_PER_CU;
 struct UnitDesc {
   int g, rows, c_row0;
   uint32_t a_off[2];
-  uint32_t b_off[NF];
+  uint32_t b_off[kMaxNF];
   const uint16_t* W;
   const uint16_t* U;
   const void* A;
@@ -57,9 +56,12 @@ __device__ __forceinline__ void* uniform_ptr(const void* q) {
   return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
 }
 
-template <int ACT>
+// NF: 16-column fragments per unit (2 or 4); wider units put more bytes in
+// flight per step and halve the number of unit reductions.
+template <int ACT, int NF>
 __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n_slabs,
                                                               int n_units) {
+  constexpr int kCols = NF * 16;
   constexpr bool GATED = ACT == 2;
   constexpr int NB = GATED ? 2 : 1;           // weight sets (w1 and w3 when gated)
   constexpr int NFRAG = 2 * NF * NB;          // (row fragment, column fragment, set)
@@ -284,19 +286,36 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
 int device_cus();
 
 hipError_t launch_ffn_skinny(const FfnParams& p, hipStream_t stream) {
-  const int n_slabs = (p.N + kCols - 1) / kCols;
-  const int64_t n_units = (int64_t)(p.G + p.S) * n_slabs;
+  // Unit width: the one whose busiest block streams the fewest columns
+  // (ceil(units / blocks) * width); ties go to the wider unit.
+  const int64_t groups = p.G + p.S;
+  const int64_t cap = (int64_t)device_cus() * kBlocksPerCU;
+  auto busiest = [&](int nf) {
+    const int64_t units = groups * ((p.N + nf * 16 - 1) / (nf * 16));
+    const int64_t blocks = std::min<int64_t>(units, cap);
+    return blocks > 0 ? (units + blocks - 1) / blocks * nf : 0;
+  };
+  const int nf = busiest(4) <= busiest(2) ? 4 : 2;
+  const int n_slabs = (p.N + nf * 16 - 1) / (nf * 16);
+  const int64_t n_units = groups * n_slabs;
   // two resident blocks per CU walk equal runs of units
-  const int64_t grid = std::min<int64_t>(n_units, (int64_t)device_cus() * kBlocksPerCU);
+  const int64_t grid = std::min<int64_t>(n_units, cap);
   if (grid > 0) {
     const dim3 g((unsigned)grid), block(kThreads);
     const int nu = (int)n_units;
-    switch (p.act) {
-      case 2: hipLaunchKernelGGL(ffn_skinny_kernel<2>, g, block, 0, stream, p, n_slabs, nu); break;
-      case 1: hipLaunchKernelGGL(ffn_skinny_kernel<1>, g, block, 0, stream, p, n_slabs, nu); break;
-      case 0: hipLaunchKernelGGL(ffn_skinny_kernel<0>, g, block, 0, stream, p, n_slabs, nu); break;
-      default: hipLaunchKernelGGL(ffn_skinny_kernel<-1>, g, block, 0, stream, p, n_slabs, nu); break;
+#define MOE_SKINNY_LAUNCH(NFV)                                                                   \
+  switch (p.act) {                                                                               \
+    case 2: hipLaunchKernelGGL((ffn_skinny_kernel<2, NFV>), g, block, 0, stream, p, n_slabs, nu); break;  \
+    case 1: hipLaunchKernelGGL((ffn_skinny_kernel<1, NFV>), g, block, 0, stream, p, n_slabs, nu); break;  \
+    case 0: hipLaunchKernelGGL((ffn_skinny_kernel<0, NFV>), g, block, 0, stream, p, n_slabs, nu); break;  \
+    default: hipLaunchKernelGGL((ffn_skinny_kernel<-1, NFV>), g, block, 0, stream, p, n_slabs, nu); break; \
+  }
+    if (nf == 4) {
+      MOE_SKINNY_LAUNCH(4)
+    } else {
+      MOE_SKINNY_LAUNCH(2)
     }
+#undef MOE_SKINNY_LAUNCH
   }
   return hipGetLastError();
 }
