@@ -446,7 +446,7 @@ def expert_choice_combine(d, S32, slot, rows_out, tokens, shared_out=None) -> np
 def moe_forward_expert_choice(x, w_g, w1, w2, *, k: int, act: str, capacity_factor: float,
                               w3=None, b_g=None, w_noise=None, eps=None, b1=None, b2=None,
                               ws1=None, ws3=None, ws2=None, logits=None, scores=None,
-                              tokens=None) -> dict:
+                              tokens=None, exact_logits: bool = False) -> dict:
     """The layer forward with expert-choice routing.
 
     1. router logits H (or the supplied float32 ``logits``);
@@ -455,11 +455,18 @@ def moe_forward_expert_choice(x, w_g, w1, w2, *, k: int, act: str, capacity_fact
     4. every expert on its rows (restricted to ``tokens`` if given);
     5. y_t = shared experts + the sum over the experts that took t, in expert
        order, of S[t, e] * FFN_e(x_t) (EC4); statistics (EC6).
+    ``exact_logits`` keeps H and S in float64, unrounded (derivative checks;
+    the selection is still decided on float32 scores).
     """
     T, d = np.asarray(x).shape
     E = np.asarray(w_g).shape[0]
-    H = router_logits(x, w_g, b_g, w_noise, eps) if logits is None else np.asarray(logits, np.float32)
-    S = expert_choice_scores(H) if scores is None else np.asarray(scores, np.float32)
+    if exact_logits:
+        H = (router_logits(x, w_g, b_g, w_noise, eps, rounded=False) if logits is None
+             else np.asarray(logits, np.float64))
+        S = full_softmax(H) if scores is None else np.asarray(scores, np.float64)
+    else:
+        H = router_logits(x, w_g, b_g, w_noise, eps) if logits is None else np.asarray(logits, np.float32)
+        S = expert_choice_scores(H) if scores is None else np.asarray(scores, np.float32)
     P = full_softmax(H).mean(axis=0)
     C = capacity(capacity_factor, T, k, E)
     sel = expert_choice_select(S, C)

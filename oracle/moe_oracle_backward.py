@@ -28,6 +28,13 @@ discrete).  Readings:
   B6  Noise (R6) is a supplied input: eps gets no gradient, W_noise gets the
       gradient through softplus, whose derivative is the logistic sigmoid.
   B7  Every gradient is returned in float64; the library returns float32.
+Expert-choice routing (EC1-EC6) adds one reading:
+  EB1 The scores are the full softmax of the logits (their float32 rounding
+      taken as the identity, B3) and the experts' token choices carry no
+      gradient (B2), so the logits receive the full-softmax backward of
+      dS[t,e] = dy_t . FFN_e(x_t) over the pairs some expert took (0 for the
+      rest).  With every expert holding C' rows, f_i = 1/E and the
+      load-balancing term's logit gradient vanishes.
 """
 from __future__ import annotations
 
@@ -36,12 +43,13 @@ import math
 import numpy as np
 from scipy.special import erf, expit
 
-from .moe_oracle import activation, full_softmax, moe_forward, to_f64
+from .moe_oracle import activation, full_softmax, moe_forward, moe_forward_expert_choice, to_f64
 
 __all__ = [
     "activation_backward", "expert_ffn_backward", "gate_softmax_backward",
     "aux_loss_logit_grad", "z_loss", "z_loss_logit_grad", "router_backward",
-    "layer_loss", "moe_backward",
+    "layer_loss", "moe_backward", "softmax_backward", "layer_loss_expert_choice",
+    "moe_backward_expert_choice",
 ]
 
 
@@ -257,6 +265,101 @@ def moe_backward(x, w_g, w1, w2, *, k: int, act: str, capacity_factor: float, dy
     dx += rb["dx"]
     out = {"dx": dx, "dw_g": rb["dw_g"], "db_g": rb["db_g"] if b_g is not None else None,
            "dw_noise": rb["dw_noise"], "dg": dg, "dH": dH, "row_gate": row_gate,
+           "y_rows": y_rows, "fwd": fwd}
+    out.update(grads)
+    return out
+
+
+def softmax_backward(p, dS) -> np.ndarray:
+    """Scores p = softmax(H) over all experts: dH[t,j] = p_tj (dS_tj - sum_i p_ti dS_ti)."""
+    p = np.asarray(p, np.float64)
+    dS = np.asarray(dS, np.float64)
+    return p * (dS - (p * dS).sum(axis=1, keepdims=True))
+
+
+def layer_loss_expert_choice(x, w_g, w1, w2, *, k: int, act: str, capacity_factor: float, dy,
+                             g_aux: float = 0.0, g_z: float = 0.0, exact_logits: bool = True,
+                             **kw) -> float:
+    """B1's objective for the expert-choice forward (derivative checks)."""
+    fwd = moe_forward_expert_choice(x, w_g, w1, w2, k=k, act=act,
+                                    capacity_factor=capacity_factor,
+                                    exact_logits=exact_logits, **kw)
+    return (float(np.sum(np.asarray(dy, np.float64) * fwd["y"])) + g_aux * fwd["l_aux"]
+            + g_z * z_loss(fwd["logits"]))
+
+
+def moe_backward_expert_choice(x, w_g, w1, w2, *, k: int, act: str, capacity_factor: float, dy,
+                               g_aux: float = 0.0, g_z: float = 0.0, w3=None, b_g=None,
+                               w_noise=None, eps=None, b1=None, b2=None, ws1=None, ws3=None,
+                               ws2=None, logits=None, exact_logits: bool = False) -> dict:
+    """Gradients of L (B1) for expert-choice routing (EB1), in float64:
+    every taken pair's row runs the expert backward with upstream S[t,e]*dy_t,
+    dS[t,e] = dy_t . FFN_e(x_t), the logits get the full-softmax backward of
+    dS plus the loss terms, then the router's parameters."""
+    fwd = moe_forward_expert_choice(x, w_g, w1, w2, k=k, act=act,
+                                    capacity_factor=capacity_factor, w3=w3, b_g=b_g,
+                                    w_noise=w_noise, eps=eps, b1=b1, b2=b2, logits=logits,
+                                    exact_logits=exact_logits)
+    H = np.asarray(fwd["logits"], np.float64)
+    S = np.asarray(fwd["scores"], np.float64)
+    slot = np.asarray(fwd["slot"], np.int64)
+    offsets = np.asarray(fwd["offsets"], np.int64)
+    row_token = np.asarray(fwd["row_token"], np.int64)
+    xs = np.asarray(x)
+    T, d = xs.shape
+    E = np.asarray(w_g).shape[0]
+    dy = np.asarray(dy, np.float64)
+    h = np.asarray(w1).shape[1]
+    R = int(offsets[-1])
+    row_gate = np.zeros(R)
+    taken = slot >= 0
+    row_gate[slot[taken]] = S[taken]
+
+    dx = np.zeros((T, d))
+    y_rows = np.zeros((R, d))
+    grads = {"dw1": np.zeros((E, h, d)), "dw2": np.zeros((E, d, h)),
+             "dw3": np.zeros((E, h, d)) if w3 is not None else None,
+             "db1": np.zeros((E, h)) if b1 is not None else None,
+             "db2": np.zeros((E, d)) if b2 is not None else None}
+    for e in range(E):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        if rows.size == 0:
+            continue
+        toks = row_token[rows]
+        res = expert_ffn_backward(xs[toks], w1[e], w2[e], act, row_gate[rows, None] * dy[toks],
+                                  None if w3 is None else w3[e], None if b1 is None else b1[e],
+                                  None if b2 is None else b2[e])
+        y_rows[rows] = res["y"]
+        np.add.at(dx, toks, res["dx"])
+        for n in ("dw1", "dw2", "dw3", "db1", "db2"):
+            if grads[n] is not None:
+                grads[n][e] = res[n]
+    if ws1 is not None:
+        S_ = np.asarray(ws1).shape[0]
+        grads["dws1"] = np.zeros((S_, h, d))
+        grads["dws2"] = np.zeros((S_, d, h))
+        grads["dws3"] = np.zeros((S_, h, d)) if ws3 is not None else None
+        for s in range(S_):
+            res = expert_ffn_backward(xs, ws1[s], ws2[s], act, dy, None if ws3 is None else ws3[s])
+            dx += res["dx"]
+            grads["dws1"][s] = res["dw1"]
+            grads["dws2"][s] = res["dw2"]
+            if ws3 is not None:
+                grads["dws3"][s] = res["dw3"]
+
+    dS = np.zeros((T, E))
+    for t, e in zip(*np.nonzero(taken)):
+        dS[t, e] = float(dy[t] @ y_rows[slot[t, e]])
+    f = np.asarray(fwd["f"], np.float64)
+    dH = softmax_backward(full_softmax(H), dS)
+    if g_aux:
+        dH += g_aux * aux_loss_logit_grad(H, f)
+    if g_z:
+        dH += g_z * z_loss_logit_grad(H)
+    rb = router_backward(xs, w_g, dH, w_noise, eps)
+    dx += rb["dx"]
+    out = {"dx": dx, "dw_g": rb["dw_g"], "db_g": rb["db_g"] if b_g is not None else None,
+           "dw_noise": rb["dw_noise"], "dS": dS, "dH": dH, "row_gate": row_gate,
            "y_rows": y_rows, "fwd": fwd}
     out.update(grads)
     return out

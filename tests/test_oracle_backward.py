@@ -180,6 +180,77 @@ def test_fully_dropped_token_gets_router_gradient_only():
     np.testing.assert_allclose(g["dH"][lost], 0.0, atol=0)
 
 
+# --- expert-choice routing ---------------------------------------------------------------
+
+EC_CASES = {
+    "ec_gelu_partial_noise": dict(seed=21, act="gelu", cf=0.5, E=4, k=2),
+    "ec_swiglu_shared": dict(seed=22, act="swiglu", cf=1.0, E=5, k=2, bias=False, noise=False,
+                             shared=1),
+}
+
+
+@pytest.mark.parametrize("case", sorted(EC_CASES))
+def test_expert_choice_backward_matches_finite_differences(case):
+    """Expert-choice gradients (EB1) against central differences of the
+    expert-choice forward oracle's objective."""
+    p, kw, dy = _layer(**EC_CASES[case])
+    g_aux, g_z = 0.7, 0.3
+    args = {n: v for n, v in p.items() if n not in ("x", "w_g", "w1", "w2")}
+    grads = O.moe_backward_expert_choice(p["x"], p["w_g"], p["w1"], p["w2"], dy=dy, g_aux=g_aux,
+                                         g_z=g_z, exact_logits=True, **kw, **args)
+    covered = (grads["fwd"]["slot"] >= 0).sum(axis=1)
+    assert (covered == 0).any() or (covered > 1).any()  # some token has 0 or several experts
+    names = {"x": "dx", "w_g": "dw_g", "w1": "dw1", "w2": "dw2", "w3": "dw3", "b1": "db1",
+             "b2": "db2", "b_g": "db_g", "w_noise": "dw_noise", "ws1": "dws1", "ws2": "dws2",
+             "ws3": "dws3"}
+    r = RNG(200)
+    for pname, gname in names.items():
+        if pname not in p:
+            continue
+        V = r.normal(size=p[pname].shape)
+
+        def L(delta):
+            q = dict(p)
+            q[pname] = p[pname] + delta * V
+            return B.layer_loss_expert_choice(q.pop("x"), q.pop("w_g"), q.pop("w1"), q.pop("w2"),
+                                              dy=dy, g_aux=g_aux, g_z=g_z, **kw, **q)
+        fd = (L(1e-6) - L(-1e-6)) / 2e-6
+        an = float(np.sum(grads[gname] * V))
+        assert an == pytest.approx(fd, rel=1e-6, abs=1e-7), (pname, an, fd)
+
+
+def test_expert_choice_identical_experts_give_no_router_gradient():
+    """C' = T and identical experts: y = (sum_e S[t,e]) FFN(x_t) = FFN(x_t)
+    whatever the logits, so dS is the same for every expert, its softmax
+    backward is 0, the load-balancing term vanishes (f = 1/E) and the router
+    gets nothing; dx is the dense FFN's."""
+    p, kw, dy = _layer(23, act="gelu", cf=2.0, E=3, k=2, noise=False, router_bias=False)
+    p["w1"][:] = p["w1"][0]
+    p["w2"][:] = p["w2"][0]
+    p["b1"][:] = p["b1"][0]
+    p["b2"][:] = p["b2"][0]
+    args = {n: v for n, v in p.items() if n not in ("x", "w_g", "w1", "w2")}
+    # unrounded scores, so that they sum to 1 exactly
+    g = O.moe_backward_expert_choice(p["x"], p["w_g"], p["w1"], p["w2"], dy=dy, g_aux=0.9,
+                                     exact_logits=True, **kw, **args)
+    assert (g["fwd"]["slot"] >= 0).all()
+    assert np.abs(g["dw_g"]).max() < 1e-12
+    dense = O.expert_ffn_backward(p["x"], p["w1"][0], p["w2"][0], "gelu", dy, None, p["b1"][0],
+                                  p["b2"][0])
+    np.testing.assert_allclose(g["dx"], dense["dx"], rtol=1e-10, atol=1e-12)
+
+
+def test_expert_choice_aux_gradient_vanishes():
+    """Every expert holds C' rows, so f = 1/E and g_aux changes nothing."""
+    p, kw, dy = _layer(24, act="relu", cf=0.75, E=4, k=2)
+    args = {n: v for n, v in p.items() if n not in ("x", "w_g", "w1", "w2")}
+    a = O.moe_backward_expert_choice(p["x"], p["w_g"], p["w1"], p["w2"], dy=dy, g_aux=0.0, **kw,
+                                     **args)
+    b = O.moe_backward_expert_choice(p["x"], p["w_g"], p["w1"], p["w2"], dy=dy, g_aux=5.0, **kw,
+                                     **args)
+    np.testing.assert_allclose(a["dw_g"], b["dw_g"], rtol=0, atol=1e-12)
+
+
 # --- planted mistakes ------------------------------------------------------------------
 
 def _gelu_no_density(act, u, v, dhid):
@@ -230,6 +301,16 @@ def _expert_bwd_transposed_dw2(*a, **kw):
     return res
 
 
+def _softmax_bwd_no_sum(p, dS):
+    return np.asarray(p) * np.asarray(dS)
+
+
+def _softmax_bwd_sign(p, dS):
+    p = np.asarray(p)
+    dS = np.asarray(dS)
+    return p * (dS + (p * dS).sum(axis=1, keepdims=True))
+
+
 ORIG_ACT = B.activation_backward
 ORIG_AUX = B.aux_loss_logit_grad
 ORIG_ROUTER = B.router_backward
@@ -244,6 +325,8 @@ MUTATIONS = {
     "z_grad_no_lse": ("z_loss_logit_grad", _z_grad_no_lse),
     "router_noise_no_sigmoid": ("router_backward", _router_noise_no_sigmoid),
     "expert_dw2_transposed": ("expert_ffn_backward", _expert_bwd_transposed_dw2),
+    "ec_softmax_bwd_no_sum": ("softmax_backward", _softmax_bwd_no_sum),
+    "ec_softmax_bwd_sign": ("softmax_backward", _softmax_bwd_sign),
 }
 
 PINS = [
@@ -254,6 +337,9 @@ PINS = [
     test_activation_derivatives_against_closed_values,
     test_logit_gradient_rows_sum_to_zero_without_z_loss,
     test_fully_dropped_token_gets_router_gradient_only,
+    lambda: [test_expert_choice_backward_matches_finite_differences(c) for c in sorted(EC_CASES)],
+    test_expert_choice_identical_experts_give_no_router_gradient,
+    test_expert_choice_aux_gradient_vanishes,
 ]
 
 
