@@ -396,24 +396,27 @@ typedef struct moe_grads {
   float* dws2;      /* [S,d,h]  required when n_shared > 0                      */
 } moe_grads_t;
 
-/* (host) Workspace bytes for moe_layer_backward; 0 for an invalid config or
- * one the backward does not cover (expert choice). */
+/* (host) Workspace bytes for moe_layer_backward; 0 for an invalid config. */
 size_t moe_backward_workspace_bytes(const moe_config_t* cfg);
 
 /*
- * Backward of moe_layer_forward for token-choice routing (drop or re-route).
+ * Backward of moe_layer_forward, token choice (drop or re-route) or expert
+ * choice.  With expert choice the scores are the full softmax of the logits,
+ * so the logits receive its backward of dS[t,e] = dy_t . (expert e's output
+ * for t) over the pairs an expert took; every expert holds C' rows, so
+ * f = 1/E and L_aux adds no logit gradient.
  *   x, eps       the forward's inputs (eps: [T,E] when router_noise)
  *   dy           [T,d] float32 upstream gradient of y
  *   g_aux, g_z   weights of L_aux and of the z-loss in L (0 disables each)
  *   saved        what moe_layer_forward wrote for this batch; required members:
- *                logits, topk_idx, topk_gate, counts, offsets, dest, row_token,
- *                hidden, pre, y_rows (the offsets and dest are the final ones
- *                when re-routing; counts are the router's)
+ *                logits, counts, offsets, row_token, hidden, pre, y_rows, and
+ *                topk_idx, topk_gate, dest (token choice; the final offsets
+ *                and dest when re-routing, the router's counts) or scores,
+ *                slot (expert choice)
  *   grads        outputs, every member float32, overwritten (not accumulated)
  * The weights must be the ones the forward used.  Workspace: at least
- * moe_backward_workspace_bytes(cfg).  MOE_ERR_UNSUPPORTED for expert choice
- * when a bf16 intermediate would exceed 2^30 elements, or when E + n_shared
- * > 512.
+ * moe_backward_workspace_bytes(cfg).  MOE_ERR_UNSUPPORTED when a bf16
+ * intermediate would exceed 2^30 elements, or when E + n_shared > 512.
  */
 moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
                                 const void* x, const float* eps, const float* dy,

@@ -272,7 +272,7 @@ BwdWs carve_backward(Carve& cv, const Cfg& c, bool noise) {
   const int64_t groups = c.E + c.S;
   const size_t te = (size_t)c.T * c.E * 4, tk = (size_t)c.T * c.k * 4;
   w.row_gate = static_cast<float*>(cv.take((size_t)std::max<int64_t>(c.R, 1) * 4));
-  w.dg = static_cast<float*>(cv.take(tk));
+  w.dg = static_cast<float*>(cv.take(c.ec ? te : tk));
   w.dH = static_cast<float*>(cv.take(te));
   if (noise) {
     w.dHn = static_cast<float*>(cv.take(te));
@@ -748,7 +748,7 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
 
 size_t moe_backward_workspace_bytes(const moe_config_t* cfg) {
   Cfg c;
-  if (check_cfg(cfg, &c) != MOE_OK || c.ec) return 0;
+  if (check_cfg(cfg, &c) != MOE_OK) return 0;
   Carve cv(nullptr);
   carve_backward(cv, c, cfg->router_noise != 0);
   return cv.off + 256;
@@ -761,14 +761,15 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   Cfg c;
   moe_status_t st = check_cfg(cfg, &c);
   if (st != MOE_OK) return st;
-  if (c.ec) return MOE_ERR_UNSUPPORTED;
   const bool swi = c.act == MOE_ACT_SWIGLU, noise = cfg->router_noise != 0;
   if (!w || !x || !dy || !sv || !gr || !ws) return MOE_ERR_INVALID_ARGUMENT;
   if (!w->w_g || !w->w1 || !w->w2 || (swi && !w->w3)) return MOE_ERR_INVALID_ARGUMENT;
   if (noise && (!w->w_noise || !eps || !gr->dw_noise)) return MOE_ERR_INVALID_ARGUMENT;
   if (c.S > 0 && (!w->ws1 || !w->ws2 || (swi && !w->ws3))) return MOE_ERR_INVALID_ARGUMENT;
-  if (!sv->logits || !sv->topk_idx || !sv->topk_gate || !sv->counts || !sv->offsets ||
-      !sv->dest || !sv->row_token || !sv->hidden || !sv->pre || !sv->y_rows)
+  if (!sv->logits || !sv->counts || !sv->offsets || !sv->row_token || !sv->hidden || !sv->pre ||
+      !sv->y_rows)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (c.ec ? (!sv->scores || !sv->slot) : (!sv->topk_idx || !sv->topk_gate || !sv->dest))
     return MOE_ERR_INVALID_ARGUMENT;
   if (!gr->dx || !gr->dw_g || !gr->dw1 || !gr->dw2 || (swi && !gr->dw3))
     return MOE_ERR_INVALID_ARGUMENT;
@@ -781,6 +782,7 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   const void* ptrs[] = {x, eps, dy, ws, w->w_g, w->w_noise, w->w1, w->w3, w->w2, w->ws1, w->ws3,
                         w->ws2, sv->logits, sv->topk_idx, sv->topk_gate, sv->counts,
                         sv->offsets, sv->dest, sv->row_token, sv->hidden, sv->pre, sv->y_rows,
+                        sv->scores, sv->slot,
                         gr->dx, gr->dw_g, gr->db_g, gr->dw_noise, gr->dw1, gr->dw3, gr->dw2,
                         gr->db1, gr->db2, gr->dws1, gr->dws3, gr->dws2};
   for (const void* q : ptrs)
@@ -800,7 +802,11 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   if ((e = (call)) != hipSuccess) return MOE_ERR_HIP;
 
   // 1. gates of the routed rows, gate gradients, logit gradients
-  MOE_TRY(launch_row_gate(sv->dest, sv->topk_gate, c.T * c.k, B.row_gate, stream));
+  if (c.ec) {
+    MOE_TRY(launch_ec_row_gate(sv->slot, sv->scores, c.T * c.E, B.row_gate, stream));
+  } else {
+    MOE_TRY(launch_row_gate(sv->dest, sv->topk_gate, c.T * c.k, B.row_gate, stream));
+  }
   if (noise) {
     RouteParams rp0;
     rp0.x = x; rp0.w_g = w->w_g; rp0.b_g = cfg->router_bias ? w->b_g : nullptr;
@@ -818,6 +824,10 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   bp.dx_rows = B.dxr; bp.dx = gr->dx; bp.g_aux = g_aux; bp.g_z = g_z;
   bp.rows_bound = c.R; bp.T = (int)c.T; bp.d = (int)c.d; bp.E = (int)c.E; bp.k = (int)c.k;
   bp.S = S;
+  // f: routed counts over T*k (token choice), rows over all rows (expert choice)
+  const double f_den = c.ec ? (double)c.E * (double)c.C : (double)c.T * (double)c.k;
+  bp.inv_f_den = f_den > 0 ? (float)(1.0 / f_den) : 0.f;
+  bp.ec = c.ec ? 1 : 0; bp.slot = sv->slot; bp.scores = sv->scores;
   MOE_TRY(launch_router_backward(bp, stream));
 
   // 2. router weights

@@ -1,5 +1,6 @@
-// Backward pass of the token-choice layer: everything except the grouped
-// expert GEMMs (which run on the tiled / float32 FFN kernels).
+// Backward pass of the layer (token choice, or expert choice): everything
+// except the grouped expert GEMMs (which run on the tiled / float32 FFN
+// kernels).
 //
 // The pages train these layers without printing a backward ("Mixture-of-
 // Experts & Sparse Model Scaling", Mathematical Formulation: the router learns
@@ -29,15 +30,17 @@ __global__ __launch_bounds__(256) void row_gate_kernel(const int32_t* dest, cons
   if (r >= 0) row_gate[r] = gate[i];
 }
 
-// dg[t,s] = dy[t] . y_rows[dest[t,s]] (0 for a dropped slot); one wave per
-// token, lanes over 4-column chunks, a fixed-order wave reduction.
+// dg[t,s] = dy[t] . y_rows[dest[t,s]] (0 for a dropped slot); with expert
+// choice dS[t,e] = dy[t] . y_rows[slot[t,e]] (0 where e did not take t).  One
+// wave per token, lanes over 4-column chunks, a fixed-order wave reduction.
 __global__ __launch_bounds__(256) void gate_grad_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= p.T) return;
   const f32x4* dy = reinterpret_cast<const f32x4*>(p.dy + t * p.d);
-  for (int s = 0; s < p.k; ++s) {
-    const int r = p.dest[t * p.k + s];
+  const int n = p.ec ? p.E : p.k;
+  for (int s = 0; s < n; ++s) {
+    const int r = p.ec ? p.slot[t * p.E + s] : p.dest[t * p.k + s];
     float acc = 0.f;
     if (r >= 0) {
       const f32x4* yr = reinterpret_cast<const f32x4*>(p.y_rows + (int64_t)r * p.d);
@@ -47,8 +50,17 @@ __global__ __launch_bounds__(256) void gate_grad_kernel(BwdParams p) {
       }
       acc = wave_sum(acc);
     }
-    if (lane == 0) p.dg[t * p.k + s] = acc;
+    if (lane == 0) p.dg[t * n + s] = acc;
   }
+}
+
+// Expert choice: the gate of row slot[t,e] is scores[t,e].
+__global__ __launch_bounds__(256) void ec_row_gate_kernel(const int32_t* slot, const float* scores,
+                                                          int64_t n, float* row_gate) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int r = slot[i];
+  if (r >= 0) row_gate[r] = scores[i];
 }
 
 // dH[t,:] = selected-softmax backward of the gates + g_aux dL_aux/dH +
@@ -76,17 +88,22 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(BwdParams p) {
   }
   sum = wave_sum(sum);
   const float lse = mx + logf(sum);
-  const float inv_tk = 1.0f / ((float)p.T * (float)p.k);
-  float fp = 0.f;  // sum_i f_i p_i
+  const float inv_f = p.inv_f_den;
+  float fp = 0.f, pds = 0.f;  // sum_i f_i p_i; expert choice: sum_i p_i dS_i
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
-    if (e < p.E) fp += (float)p.counts[e] * inv_tk * (ex[j] / sum);
+    if (e < p.E) {
+      fp += (float)p.counts[e] * inv_f * (ex[j] / sum);
+      if (p.ec) pds += (ex[j] / sum) * p.dg[t * p.E + e];
+    }
   }
   fp = wave_sum(fp);
+  if (p.ec) pds = wave_sum(pds);
   // gates: sum_m g_m dg_m over the token's slots (k <= 8, every lane)
   float gdg = 0.f;
-  for (int s = 0; s < p.k; ++s) gdg += p.gate[t * p.k + s] * p.dg[t * p.k + s];
+  if (!p.ec)
+    for (int s = 0; s < p.k; ++s) gdg += p.gate[t * p.k + s] * p.dg[t * p.k + s];
   const float c_aux = p.g_aux * (float)p.E / (float)p.T;
   const float c_z = p.g_z * 2.0f * lse / (float)p.T;
 #pragma unroll
@@ -94,11 +111,16 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(BwdParams p) {
     const int e = lane + 64 * j;
     if (e >= p.E) continue;
     const float pe = ex[j] / sum;
-    float d = c_aux * pe * ((float)p.counts[e] * inv_tk - fp) + c_z * pe;
-    for (int s = 0; s < p.k; ++s) {
-      if (p.idx[t * p.k + s] == e) {
-        const float g = p.gate[t * p.k + s];
-        d += g * (p.dg[t * p.k + s] - gdg);
+    float d = c_aux * pe * ((float)p.counts[e] * inv_f - fp) + c_z * pe;
+    if (p.ec) {
+      // scores are the full softmax: its backward over all experts
+      d += pe * (p.dg[t * p.E + e] - pds);
+    } else {
+      for (int s = 0; s < p.k; ++s) {
+        if (p.idx[t * p.k + s] == e) {
+          const float g = p.gate[t * p.k + s];
+          d += g * (p.dg[t * p.k + s] - gdg);
+        }
       }
     }
     p.dH[t * p.E + e] = d;
@@ -442,9 +464,16 @@ __global__ __launch_bounds__(256) void dx_kernel(BwdParams p, const TW* w_g, con
     for (int tt = 0; tt < nt; ++tt) {
       const int64_t t = t0 + tt;
       float x = 0.f;
-      for (int s = 0; s < p.k; ++s) {
-        const int r = p.dest[t * p.k + s];
-        if (r >= 0) x += p.dx_rows[(int64_t)r * p.d + c];
+      if (p.ec) {
+        for (int e = 0; e < p.E; ++e) {  // the experts that took t, in order
+          const int r = p.slot[t * p.E + e];
+          if (r >= 0) x += p.dx_rows[(int64_t)r * p.d + c];
+        }
+      } else {
+        for (int s = 0; s < p.k; ++s) {
+          const int r = p.dest[t * p.k + s];
+          if (r >= 0) x += p.dx_rows[(int64_t)r * p.d + c];
+        }
       }
       for (int s = 0; s < p.S; ++s) x += p.dx_rows[(p.rows_bound + (int64_t)s * p.T + t) * p.d + c];
       p.dx[t * p.d + c] = x + acc[tt];
@@ -459,6 +488,14 @@ hipError_t launch_row_gate(const int32_t* dest, const float* gate, int64_t n, fl
   if (n > 0)
     hipLaunchKernelGGL(row_gate_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
                        dest, gate, n, row_gate);
+  return hipGetLastError();
+}
+
+hipError_t launch_ec_row_gate(const int32_t* slot, const float* scores, int64_t n,
+                              float* row_gate, hipStream_t stream) {
+  if (n > 0)
+    hipLaunchKernelGGL(ec_row_gate_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       stream, slot, scores, n, row_gate);
   return hipGetLastError();
 }
 

@@ -200,11 +200,19 @@ struct BwdParams {
   const float* dx_rows;      // [rows_bound + S*T, d] expert input gradients
   float* dx;                 // [T,d] out
   float g_aux, g_z;          // weights of L_aux and the z-loss
+  float inv_f_den;           // f_e = counts[e] * inv_f_den
   int64_t rows_bound;
   int T, d, E, k, S;
+  // expert-choice routing: slot [T,E] (row of (t,e) or -1) and scores [T,E]
+  // replace dest / idx / gate, and dg is [T,E] (dS)
+  int ec;
+  const int32_t* slot;
+  const float* scores;
 };
 hipError_t launch_row_gate(const int32_t* dest, const float* gate, int64_t n, float* row_gate,
                            hipStream_t stream);
+hipError_t launch_ec_row_gate(const int32_t* slot, const float* scores, int64_t n,
+                              float* row_gate, hipStream_t stream);
 // gate gradients, then the logit gradients
 hipError_t launch_router_backward(const BwdParams& p, hipStream_t stream);
 int router_wgrad_splits(int64_t T, int64_t E, int64_t d);

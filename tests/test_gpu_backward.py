@@ -19,7 +19,6 @@ from workloads import SMALL, make_inputs, make_upstream_grad
 pytestmark = pytest.mark.gpu
 
 G_AUX, G_Z = 0.5, 0.1
-TC_SMALL = [n for n, c in SMALL.items() if c.routing == "token"]
 
 NAMES = ("dx", "dw_g", "db_g", "dw_noise", "dw1", "dw3", "dw2", "db1", "db2", "dws1", "dws3",
          "dws2")
@@ -27,11 +26,12 @@ NAMES = ("dx", "dw_g", "db_g", "dw_noise", "dw1", "dw3", "dw2", "db1", "db2", "d
 
 def oracle_backward(inp, dy, logits):
     c = inp.cfg
-    return O.moe_backward(inp.x, inp.w_g, inp.w1, inp.w2, k=c.k, act=c.act,
-                          capacity_factor=c.capacity_factor, dy=dy, g_aux=G_AUX, g_z=G_Z,
-                          w3=inp.w3, b_g=inp.b_g, w_noise=inp.w_noise, eps=inp.eps, b1=inp.b1,
-                          b2=inp.b2, ws1=inp.ws1, ws3=inp.ws3, ws2=inp.ws2, logits=logits,
-                          overflow=c.overflow)
+    kw = dict(k=c.k, act=c.act, capacity_factor=c.capacity_factor, dy=dy, g_aux=G_AUX, g_z=G_Z,
+              w3=inp.w3, b_g=inp.b_g, w_noise=inp.w_noise, eps=inp.eps, b1=inp.b1, b2=inp.b2,
+              ws1=inp.ws1, ws3=inp.ws3, ws2=inp.ws2, logits=logits)
+    if c.routing == "expert":
+        return O.moe_backward_expert_choice(inp.x, inp.w_g, inp.w1, inp.w2, **kw)
+    return O.moe_backward(inp.x, inp.w_g, inp.w1, inp.w2, overflow=c.overflow, **kw)
 
 
 def gpu_backward(cfg, inp, dy, logits):
@@ -43,19 +43,24 @@ def gpu_backward(cfg, inp, dy, logits):
     return layer, dev, {n: host(t) for n, t in g.items()}
 
 
-@pytest.mark.parametrize("name", TC_SMALL)
+@pytest.mark.parametrize("name", list(SMALL))
 def test_backward_parity(name):
+    """Every small workload, token choice (drop, re-route) and expert choice.
+    With expert choice the GPU forms its float32 scores from the replayed
+    logits itself, and its selection must equal the oracle's bit for bit
+    before the gradients are compared."""
     require_gpu()
     cfg = SMALL[name]
     banner(f"backward {name}")
     inp = make_inputs(cfg, 0)
     dy = make_upstream_grad(cfg, 0)
-    fwd = O.moe_forward(inp.x, inp.w_g, inp.w1, inp.w2, k=cfg.k, act=cfg.act,
-                        capacity_factor=cfg.capacity_factor, w3=inp.w3, b_g=inp.b_g,
-                        w_noise=inp.w_noise, eps=inp.eps, b1=inp.b1, b2=inp.b2, ws1=inp.ws1,
-                        ws3=inp.ws3, ws2=inp.ws2, overflow=cfg.overflow)
-    want = oracle_backward(inp, dy, fwd["logits"])
-    layer, dev, got = gpu_backward(cfg, inp, dy, fwd["logits"])
+    H = O.router_logits(inp.x, inp.w_g, inp.b_g, inp.w_noise, inp.eps)
+    want = oracle_backward(inp, dy, H)
+    layer, dev, got = gpu_backward(cfg, inp, dy, H)
+    if cfg.routing == "expert":
+        assert np.array_equal(host(layer.out["slot"]), want["fwd"]["slot"])
+    else:
+        assert np.array_equal(host(layer.out["dest"]), want["fwd"]["dest"])
     tol = y_tol(cfg)
     checked = []
     for n in NAMES:
@@ -188,3 +193,54 @@ def test_backward_full_size(name):
     if "db_g" in got:
         db = host(got["db_g"]).astype(np.float64)
         assert abs(db.sum()) <= 1e-4 * np.abs(db).sum() + 1e-6
+
+
+def test_backward_full_size_expert_choice():
+    """The full-size expert-choice layer (Mixtral prefill shape, capacity
+    factor 1): expert weight-gradient rows and columns of the busiest and of
+    one more expert, dx of sampled tokens (one no expert took among them when
+    there is one), and the invariant that dW_g's columns sum to 0 without the
+    z-loss (the load-balancing term adds nothing with expert choice)."""
+    require_gpu()
+    from workloads import FULL
+    cfg = FULL["mixtral_prefill_ec"]
+    banner("backward full mixtral_prefill_ec")
+    inp = make_inputs(cfg, 0)
+    dy = make_upstream_grad(cfg, 0)
+    T, E = cfg.T, cfg.E
+    H = O.router_logits(inp.x, inp.w_g, inp.b_g, inp.w_noise, inp.eps)
+    S = O.expert_choice_scores(H)
+    sel = O.expert_choice_select(S, O.capacity(cfg.capacity_factor, T, cfg.k, E))
+    dev = upload(inp)
+    layer = MoeLayer(cfg, weights_of(dev))
+    layer.forward_train(dev["x"], dev.get("eps"), torch.from_numpy(H).cuda())
+    got = layer.backward(dev["x"], torch.from_numpy(dy).cuda(), dev.get("eps"), 0.5, 0.0)
+    torch.cuda.synchronize()
+    slot = sel["slot"]
+    assert np.array_equal(host(layer.out["slot"]), slot)
+    tol = y_tol(cfg)
+    offsets, row_token = sel["offsets"], sel["row_token"]
+    rng = np.random.default_rng(6)
+    for e in (0, E - 1):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        toks = row_token[rows]
+        for m in rng.choice(cfg.h, 2, replace=False):
+            want = _slice_grads(inp, cfg, toks, S[toks, e].astype(np.float64), e, int(m), dy)
+            assert rel_l2(host(got["dw1"][e, m]), want["dw1"][0]) <= tol, ("dw1", e, m)
+            assert rel_l2(host(got["dw3"][e, m]), want["dw3"][0]) <= tol, ("dw3", e, m)
+            assert rel_l2(host(got["dw2"][e, :, m]), want["dw2"][:, 0]) <= tol, ("dw2", e, m)
+    p = O.full_softmax(H)
+    uncovered = np.flatnonzero((slot < 0).all(axis=1))
+    for t in [0, T - 1] + ([int(uncovered[0])] if uncovered.size else []):
+        dx = np.zeros(cfg.d)
+        dS = np.zeros(E)
+        for e in np.flatnonzero(slot[t] >= 0):
+            res = O.expert_ffn_backward(inp.x[t:t + 1], inp.w1[e], inp.w2[e], cfg.act,
+                                        float(S[t, e]) * dy[t:t + 1], inp.w3[e])
+            dx += res["dx"][0]
+            dS[e] = float(dy[t] @ res["y"][0])
+        dH = O.softmax_backward(p[t:t + 1], dS[None, :])
+        dx += O.router_backward(inp.x[t:t + 1], inp.w_g, dH)["dx"][0]
+        assert rel_l2(host(got["dx"][t]), dx) <= tol, ("dx", t)
+    dw_g = host(got["dw_g"]).astype(np.float64)
+    assert np.abs(dw_g.sum(axis=0)).max() <= 1e-4 * np.abs(dw_g).sum(axis=0).max() + 1e-6
