@@ -3,9 +3,10 @@
 "Mixture-of-Experts & Sparse Model Scaling", Advanced Theory & Extensions:
 every expert takes the tokens it scores highest, up to its capacity.
   - counts, offsets, row_token and slot bit-exact when the GPU is fed the
-    oracle's float32 scores (replay), and bit-exact against the oracle's
-    selection run on the GPU's own scores;
-  - the GPU's scores within 1e-6 absolute of the oracle's;
+    oracle's float32 scores (replay);
+  - the GPU's scores within 1e-6 absolute of the oracle's, and its selection
+    on them satisfying the properties that define it (checked directly, not
+    by running the oracle on GPU values);
   - outputs within 2e-2 relative L2 (bf16) / 1e-5 (float32), f, P, L_aux,
     drop rate as for token choice; the single call equals the stage calls.
 """
@@ -70,10 +71,41 @@ def test_ec_replay_scores_parity(name):
     assert rel_l2(host(got["y"]), want["y"]) <= y_tol(cfg)
 
 
+def _selection_properties(cfg, S, got):
+    """The selection the GPU made on its own float32 scores S is the one
+    [MoE&SMS] and readings EC2, EC3, EC5 define, checked from its properties:
+    every expert holds exactly C' = min(C, T) tokens in ascending order, slot
+    indexes them, and every token it took outranks every token it left
+    (higher score, or an equal score and a lower index)."""
+    T, E = S.shape
+    Cp = min(O.capacity(cfg.capacity_factor, T, cfg.k, E), T)
+    counts, offsets = host(got["counts"]), host(got["offsets"])
+    rows, slot = host(got["row_token"]), host(got["slot"])
+    assert np.all(counts == Cp)
+    assert np.array_equal(offsets, np.arange(E + 1) * Cp)
+    for e in range(E):
+        taken = rows[e * Cp:(e + 1) * Cp].astype(np.int64)
+        assert np.all(np.diff(taken) > 0)
+        mask = np.zeros(T, bool)
+        mask[taken] = True
+        want_slot = np.full(T, -1)
+        want_slot[taken] = e * Cp + np.arange(Cp)
+        assert np.array_equal(slot[:, e], want_slot)
+        if 0 < Cp < T:
+            s_in, s_out = S[mask, e], S[~mask, e]
+            lo = s_in.min()
+            assert lo >= s_out.max()
+            # at the boundary score, every token taken precedes every token left
+            tied_in = np.flatnonzero(mask & (S[:, e] == lo))
+            tied_out = np.flatnonzero(~mask & (S[:, e] == lo))
+            if tied_out.size:
+                assert tied_in.max() < tied_out.min()
+
+
 @pytest.mark.parametrize("name", EC_SMALL)
 def test_ec_gpu_scores_and_selection(name):
-    """The GPU's own scores (from the oracle's logits) are within 1e-6, and the
-    GPU's selection is exactly the oracle's selection on those same scores."""
+    """The GPU's own scores (from the oracle's logits) are within 1e-6 of the
+    oracle's, and the GPU's selection on them has the defining properties."""
     require_gpu()
     cfg = SMALL[name]
     banner(f"ec scores {name}")
@@ -84,14 +116,15 @@ def test_ec_gpu_scores_and_selection(name):
     torch.cuda.synchronize()
     S = host(got["scores"])
     assert np.abs(S - want["scores"]).max() <= 1e-6
-    again = O.expert_choice_select(S, O.capacity(cfg.capacity_factor, cfg.T, cfg.k, cfg.E))
-    _selection_exact(cfg, again, got)
+    _selection_properties(cfg, S, got)
 
 
 @pytest.mark.parametrize("name", EC_SMALL)
 def test_ec_end_to_end_and_single_call(name):
-    """GPU router through the single call; the oracle then recomputes every
-    step after the logits from the GPU's logits and scores (shared routing);
+    """The GPU router through the single call: logits and scores against the
+    oracle's, the selection's defining properties on the GPU's own scores,
+    and y against the oracle's on every token whose set of experts is the
+    oracle's (a near-tie at an expert's capacity boundary may move a token);
     the stage calls give the same bits as the single call."""
     require_gpu()
     cfg = SMALL[name]
@@ -100,12 +133,18 @@ def test_ec_end_to_end_and_single_call(name):
     dev, layer = _layer(cfg, inp)
     got = layer.forward(dev["x"], dev.get("eps"))
     torch.cuda.synchronize()
-    want = oracle_ec(inp, logits=host(got["logits"]), scores=host(got["scores"]))
-    ref = oracle_ec(inp)
-    assert rel_l2(host(got["logits"]), ref["logits"]) <= 1e-5
-    _selection_exact(cfg, want, got)
-    _stats(cfg, want, got)
-    assert rel_l2(host(got["y"]), want["y"]) <= y_tol(cfg)
+    want = oracle_ec(inp)
+    assert rel_l2(host(got["logits"]), want["logits"]) <= 1e-5
+    S = host(got["scores"])
+    assert np.abs(S - want["scores"]).max() <= 1e-6
+    _selection_properties(cfg, S, got)
+    same = np.all((host(got["slot"]) >= 0) == (want["slot"] >= 0), axis=1)
+    assert same.mean() >= 0.99
+    assert rel_l2(host(got["y"])[same], want["y"][same]) <= y_tol(cfg)
+    E = cfg.E
+    st = host(got["stats"]).astype(np.float64)
+    assert rel_l2(st[:E], want["f"]) <= 1e-6
+    assert rel_l2(st[E:2 * E], want["P"]) <= 1e-5
     y1, slot1 = got["y"].clone(), got["slot"].clone()
     dev2, layer2 = _layer(cfg, inp)
     got2 = layer2.staged(dev2["x"], dev2.get("eps"))
