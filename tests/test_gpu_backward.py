@@ -244,3 +244,60 @@ def test_backward_full_size_expert_choice():
         assert rel_l2(host(got["dx"][t]), dx) <= tol, ("dx", t)
     dw_g = host(got["dw_g"]).astype(np.float64)
     assert np.abs(dw_g.sum(axis=0)).max() <= 1e-4 * np.abs(dw_g).sum(axis=0).max() + 1e-6
+
+
+def _edge_cfg(**kw):
+    from workloads import LayerConfig
+    base = dict(name="bwd_edge", cfg_id=980, T=70, d=64, E=4, k=2, h=96, act="swiglu",
+                capacity_factor=0.0, dtype="bf16")
+    base.update(kw)
+    return LayerConfig(**base)
+
+
+BWD_EDGES = [
+    dict(name="ragged_tiled_bf16", T=333, d=136, E=5, k=3, h=200, act="swiglu"),
+    dict(name="ragged_gelu_bf16", T=300, d=72, E=3, k=2, h=264, act="gelu"),
+    dict(name="ragged_relu_skinny", T=45, d=136, E=6, k=2, h=200, act="relu", capacity_factor=1.0),
+    dict(name="fp32_biases_noise_shared", T=50, d=40, E=5, k=3, h=24, act="gelu",
+         capacity_factor=1.25, dtype="f32", n_shared=2, ffn_bias=True, router_noise=True,
+         router_bias="normal", router_bias_std=0.5),
+    dict(name="single_token", T=1, d=64, E=4, k=2, h=96),
+    dict(name="k_equals_E", T=90, d=64, E=4, k=4, h=96),
+    dict(name="many_experts", T=400, d=64, E=256, k=8, h=64, act="relu", capacity_factor=1.5),
+    dict(name="noise_E128_k1", T=257, d=96, E=128, k=1, h=64, act="relu", capacity_factor=1.0,
+         router_noise=True),
+    dict(name="capacity_zero_shared", T=64, capacity_factor=1e-6, n_shared=2),
+    dict(name="dense_E1_k1", T=130, d=64, E=1, k=1, h=96, act="gelu", capacity_factor=1.0),
+    dict(name="ec_many_experts", T=300, E=256, k=8, h=64, act="relu", capacity_factor=1.0,
+         routing="expert"),
+    dict(name="ec_single_token", T=1, E=4, k=2, capacity_factor=2.0, routing="expert"),
+    dict(name="ec_fp32_shared_noise", T=50, d=40, E=5, k=3, h=24, capacity_factor=1.25,
+         dtype="f32", n_shared=2, ffn_bias=True, router_noise=True, routing="expert"),
+]
+
+
+@pytest.mark.parametrize("kw", BWD_EDGES, ids=[e["name"] for e in BWD_EDGES])
+def test_backward_edge_configs(kw):
+    """Ragged sizes through both GEMM kernels, float32 with every optional
+    term (FFN and router biases, noise, shared experts), one token, k = E,
+    256 experts with k = 8, a noisy 128-expert top-1 router, capacity 0 (only
+    the shared experts and the router's loss terms carry gradient), E = 1, and
+    expert choice at the extremes."""
+    require_gpu()
+    cfg = _edge_cfg(**kw)
+    banner(f"backward edge {cfg.name}")
+    inp = make_inputs(cfg, 0)
+    dy = make_upstream_grad(cfg, 0)
+    H = O.router_logits(inp.x, inp.w_g, inp.b_g, inp.w_noise, inp.eps)
+    want = oracle_backward(inp, dy, H)
+    layer, dev, got = gpu_backward(cfg, inp, dy, H)
+    if cfg.routing == "expert":
+        assert np.array_equal(host(layer.out["slot"]), want["fwd"]["slot"])
+    else:
+        assert np.array_equal(host(layer.out["dest"]), want["fwd"]["dest"])
+    tol = y_tol(cfg)
+    for n in NAMES:
+        if want.get(n) is None:
+            continue
+        err = rel_l2(got[n], want[n])
+        assert err <= tol, (n, err)
