@@ -58,25 +58,31 @@ __device__ __forceinline__ void* uniform_ptr(const void* q) {
 
 // NF: 16-column fragments per unit (2 or 4); wider units put more bytes in
 // flight per step and halve the number of unit reductions.
-template <int ACT, int NF>
+// WU: every wave owns whole units (the full reduction axis, no LDS reduction,
+// no barriers), for short reductions with units enough for every wave;
+// otherwise the block's 4 waves split each unit's reduction axis.
+template <int ACT, int NF, bool WU>
 __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n_slabs,
                                                               int n_units) {
   constexpr int kCols = NF * 16;
   constexpr bool GATED = ACT == 2;
   constexpr int NB = GATED ? 2 : 1;           // weight sets (w1 and w3 when gated)
   constexpr int NFRAG = 2 * NF * NB;          // (row fragment, column fragment, set)
-  __shared__ float red[4][NFRAG][4][64];
+  __shared__ float red[WU ? 1 : 4][NFRAG][4][64];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int K = p.K, N = p.N;
   const int64_t wstride = (int64_t)N * K;
-  const int u_begin = (int)((int64_t)blockIdx.x * n_units / gridDim.x);
-  const int u_end = (int)((int64_t)(blockIdx.x + 1) * n_units / gridDim.x);
+  // a contiguous run of units per block (per wave with WU)
+  const int64_t workers = WU ? (int64_t)gridDim.x * 4 : gridDim.x;
+  const int64_t me = WU ? (int64_t)blockIdx.x * 4 + w : blockIdx.x;
+  const int u_begin = (int)(me * n_units / workers);
+  const int u_end = (int)((me + 1) * n_units / workers);
   // this wave's contiguous reduction range; every wave runs `per` steps
   // per unit (steps past its range read zeros), so the waves stay in step
-  const int kch = (K + kStep - 1) / kStep, per = (kch + 3) / 4;
-  const int kb = min(K, w * per * kStep), ke = min(K, (w + 1) * per * kStep);
+  const int kch = (K + kStep - 1) / kStep, per = WU ? kch : (kch + 3) / 4;
+  const int kb = WU ? 0 : min(K, w * per * kStep), ke = WU ? K : min(K, (w + 1) * per * kStep);
   const int kl = (lane >> 4) * 8;
   const int total = (u_end - u_begin) * per;
 
@@ -192,8 +198,56 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
                 __builtin_bit_cast(bf16x8, sg.a[v][mf]), b, acc[mf][nf][s], 0, 0, 0);
         }
   };
-  // sum the 4 waves' partial products in wave order, activation, store
+  // one output element of the unit: bias, pre-activations, activation, store
+  auto emit = [&](const UnitDesc& d, int slab, int row, int col, float a, float up)
+      __attribute__((always_inline)) {
+    const bool routed = d.g < p.G;
+    const int gw = routed ? d.g : d.g - p.G;
+    const float* bias = routed ? p.bias_main : p.bias_shared;
+    if (bias) a += bias[(int64_t)gw * N + col];
+    if (ACT >= 0 && p.pre) {  // pre-activations for the backward
+      uint16_t* pre = static_cast<uint16_t*>(p.pre) +
+                      (int64_t)(d.c_row0 + row) * (GATED ? 2 * N : N) + col;
+      pre[0] = f32_to_bf16(a);
+      if (GATED) pre[N] = f32_to_bf16(up);
+    }
+    float out;
+    if (GATED) {
+      out = silu_f32(a) * up;
+    } else if (ACT == 0) {
+      out = gelu_f32(a);
+    } else if (ACT == 1) {
+      out = fmaxf(a, 0.f);
+    } else {
+      out = a;
+    }
+    const int64_t idx = (int64_t)(d.c_row0 + row) * N + col;
+    if (p.out_bf16) {
+      static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(out);
+    } else {
+      float* dst = static_cast<float*>(p.out) + idx;
+      *dst = p.accumulate ? *dst + out : out;
+    }
+  };
+  // sum the 4 waves' partial products in wave order, activation, store (with
+  // WU the wave's own products, straight from the 16x16 result layout: lane
+  // holds column lane%16 of rows 4*(lane/16) + i)
   auto finish = [&](const UnitDesc& d, int u) __attribute__((always_inline)) {
+    if constexpr (WU) {
+      const int slab = u - d.g * n_slabs;
+#pragma unroll
+      for (int mf = 0; mf < 2; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = mf * 16 + (lane >> 4) * 4 + i;
+            const int col = slab * kCols + nf * 16 + (lane & 15);
+            if (row < d.rows && col < N)
+              emit(d, slab, row, col, acc[mf][nf][0][i], GATED ? acc[mf][nf][NB - 1][i] : 0.f);
+          }
+      return;
+    }
 #pragma unroll
     for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
@@ -203,10 +257,7 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
 #pragma unroll
           for (int i = 0; i < 4; ++i) red[w][(mf * NF + nf) * NB + s][i][lane] = acc[mf][nf][s][i];
     lds_barrier();
-    const bool routed = d.g < p.G;
-    const int gw = routed ? d.g : d.g - p.G;
     const int slab = u - d.g * n_slabs;
-    const float* bias = routed ? p.bias_main : p.bias_shared;
     for (int o = threadIdx.x; o < 2 * NF * 256; o += kThreads) {
       const int mf = o / (NF * 256), rem = o - mf * NF * 256;
       const int nf = rem >> 8, i = (rem >> 6) & 3, l = rem & 63;
@@ -214,34 +265,12 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
       const int col = slab * kCols + nf * 16 + (l & 15);
       if (row >= d.rows || col >= N) continue;
       const int f0 = (mf * NF + nf) * NB;
-      float a = ((red[0][f0][i][l] + red[1][f0][i][l]) + red[2][f0][i][l]) + red[3][f0][i][l];
-      if (bias) a += bias[(int64_t)gw * N + col];
-      float out, up = 0.f;
+      const float a = ((red[0][f0][i][l] + red[1][f0][i][l]) + red[2][f0][i][l]) + red[3][f0][i][l];
+      float up = 0.f;
       if (GATED)
         up = ((red[0][f0 + 1][i][l] + red[1][f0 + 1][i][l]) + red[2][f0 + 1][i][l]) +
              red[3][f0 + 1][i][l];
-      if (ACT >= 0 && p.pre) {  // pre-activations for the backward
-        uint16_t* pre = static_cast<uint16_t*>(p.pre) +
-                        (int64_t)(d.c_row0 + row) * (GATED ? 2 * N : N) + col;
-        pre[0] = f32_to_bf16(a);
-        if (GATED) pre[N] = f32_to_bf16(up);
-      }
-      if (GATED) {
-        out = silu_f32(a) * up;
-      } else if (ACT == 0) {
-        out = gelu_f32(a);
-      } else if (ACT == 1) {
-        out = fmaxf(a, 0.f);
-      } else {
-        out = a;
-      }
-      const int64_t idx = (int64_t)(d.c_row0 + row) * N + col;
-      if (p.out_bf16) {
-        static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(out);
-      } else {
-        float* dst = static_cast<float*>(p.out) + idx;
-        *dst = p.accumulate ? *dst + out : out;
-      }
+      emit(d, slab, row, col, a, up);
     }
     lds_barrier();  // red is reused by the next unit
   };
@@ -286,34 +315,50 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
 int device_cus();
 
 hipError_t launch_ffn_skinny(const FfnParams& p, hipStream_t stream) {
-  // Unit width: the one whose busiest block streams the fewest columns
-  // (ceil(units / blocks) * width); ties go to the wider unit.
+  // Unit width and work split from a cost model in wave-steps of one
+  // 16-column fragment: the busiest worker's units times their steps (the
+  // K-split pays about 3 more steps per unit for its LDS reduction), times
+  // the width.  Whole-unit waves must beat the K-split by 15% to be chosen;
+  // between widths, ties go to the wider unit.
   const int64_t groups = p.G + p.S;
   const int64_t cap = (int64_t)device_cus() * kBlocksPerCU;
-  auto busiest = [&](int nf) {
-    const int64_t units = groups * ((p.N + nf * 16 - 1) / (nf * 16));
+  const int64_t kch = (p.K + kStep - 1) / kStep;
+  int nf = 2;
+  bool wu = false;
+  double best = 1e300;
+  for (int cand = 4; cand >= 2; cand -= 2) {
+    const int64_t units = groups * ((p.N + cand * 16 - 1) / (cand * 16));
+    if (units == 0) continue;
     const int64_t blocks = std::min<int64_t>(units, cap);
-    return blocks > 0 ? (units + blocks - 1) / blocks * nf : 0;
-  };
-  const int nf = busiest(4) <= busiest(2) ? 4 : 2;
+    const double ksplit = (double)((units + blocks - 1) / blocks) * ((kch + 3) / 4 + 3) * cand;
+    const int64_t wblocks = std::min<int64_t>((units + 3) / 4, cap);
+    const double whole = (double)((units + 4 * wblocks - 1) / (4 * wblocks)) * kch * cand * 1.15;
+    if (ksplit < best) { best = ksplit; nf = cand; wu = false; }
+    if (whole < best) { best = whole; nf = cand; wu = true; }
+  }
   const int n_slabs = (p.N + nf * 16 - 1) / (nf * 16);
   const int64_t n_units = groups * n_slabs;
-  // two resident blocks per CU walk equal runs of units
-  const int64_t grid = std::min<int64_t>(n_units, cap);
+  // two resident blocks per CU walk equal runs of units (of whole-unit
+  // waves: a block's 4 waves take 4 consecutive runs)
+  const int64_t grid = std::min<int64_t>(wu ? (n_units + 3) / 4 : n_units, cap);
   if (grid > 0) {
     const dim3 g((unsigned)grid), block(kThreads);
     const int nu = (int)n_units;
-#define MOE_SKINNY_LAUNCH(NFV)                                                                   \
+#define MOE_SKINNY_LAUNCH(NFV, WUV)                                                              \
   switch (p.act) {                                                                               \
-    case 2: hipLaunchKernelGGL((ffn_skinny_kernel<2, NFV>), g, block, 0, stream, p, n_slabs, nu); break;  \
-    case 1: hipLaunchKernelGGL((ffn_skinny_kernel<1, NFV>), g, block, 0, stream, p, n_slabs, nu); break;  \
-    case 0: hipLaunchKernelGGL((ffn_skinny_kernel<0, NFV>), g, block, 0, stream, p, n_slabs, nu); break;  \
-    default: hipLaunchKernelGGL((ffn_skinny_kernel<-1, NFV>), g, block, 0, stream, p, n_slabs, nu); break; \
+    case 2: hipLaunchKernelGGL((ffn_skinny_kernel<2, NFV, WUV>), g, block, 0, stream, p, n_slabs, nu); break;  \
+    case 1: hipLaunchKernelGGL((ffn_skinny_kernel<1, NFV, WUV>), g, block, 0, stream, p, n_slabs, nu); break;  \
+    case 0: hipLaunchKernelGGL((ffn_skinny_kernel<0, NFV, WUV>), g, block, 0, stream, p, n_slabs, nu); break;  \
+    default: hipLaunchKernelGGL((ffn_skinny_kernel<-1, NFV, WUV>), g, block, 0, stream, p, n_slabs, nu); break; \
   }
-    if (nf == 4) {
-      MOE_SKINNY_LAUNCH(4)
+    if (nf == 4 && wu) {
+      MOE_SKINNY_LAUNCH(4, true)
+    } else if (nf == 4) {
+      MOE_SKINNY_LAUNCH(4, false)
+    } else if (wu) {
+      MOE_SKINNY_LAUNCH(2, true)
     } else {
-      MOE_SKINNY_LAUNCH(2)
+      MOE_SKINNY_LAUNCH(2, false)
     }
 #undef MOE_SKINNY_LAUNCH
   }
