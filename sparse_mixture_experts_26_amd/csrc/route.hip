@@ -6,36 +6,41 @@
 // eps * softplus(x W_noise) on the logits and a softmax over the selected
 // logits; "Mixture-of-experts Models", Level 2: a fixed tie rule.
 //
-// One block handles 16 tokens with 4 or 16 waves.  Phase 1 (skipped when
+// One block handles 16 tokens with up to 16 waves.  Phase 1 (skipped when
 // replaying logits) computes the [16, E(+E)] logit tile with bf16 MFMA 16x16x32
 // (float32 accumulate): the waves split the model width into contiguous
 // ranges, so even a decode batch of a few tokens keeps many waves streaming x
-// and W_g, and the partial tiles are summed in LDS in a fixed order.  Bias and
+// and W_g, and wide tiles (more than 64 columns) also give their 64-column
+// groups to different waves; the partial tiles are summed in LDS in a fixed
+// order.  Bias and
 // noise are applied and the logits written out.  Phase 2 gives every token to
 // one wave: lanes hold experts e = lane + 64j, k rounds of a wave-wide argmax
 // on (value desc, index asc) pick the experts, and the same registers yield
 // the full softmax, whose per-expert sums over the block's tokens are written
 // per block and reduced in a fixed order by a second kernel (no atomics, so
 // results are deterministic).
+#include <algorithm>
+
 #include "launch.hpp"
 
 namespace moe {
 
 namespace {
 
-// 16 waves split the model width when the logit tile is narrow (decode-sized
-// batches then still keep many loads in flight), 4 waves otherwise.
 constexpr int kMaxWaves = 16;
 constexpr int kMaxThreads = 64 * kMaxWaves;
 constexpr uint32_t kOOB = 0x80000000u;
 
 // Phase 1, bf16: this wave's partial products over its model-width range into
-// part[m*ldh + n], n < ncols (gate columns, then noise columns).  The block's
-// nw waves split the model width into nw contiguous ranges.
+// part[m*ldh + n] (gate columns, then noise columns).  The block's waves form
+// nk x nc: nk contiguous model-width ranges, and nc interleaved sets of
+// 64-column groups (wide tiles: the column groups run in parallel instead of
+// one after another); wave w takes range w % nk and set w / nk.
 __device__ void router_tile_bf16(const RouteParams& p, float* part, int ldh, int t_base,
-                                 int ncols, int nw) {
+                                 int ncols, int nk, int nc) {
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = wid % nk, wc = wid / nk;
   const int d = p.d;
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(p.x), (short)0, 0x7fffffff, 0x00020000);
@@ -47,9 +52,9 @@ __device__ void router_tile_bf16(const RouteParams& p, float* part, int ldh, int
   const int kofs = (lane >> 4) * 8;
   const uint32_t a_base = row < p.T ? (uint32_t)row * (uint32_t)d * 2u : kOOB;
   // contiguous model-width range of this wave, in steps of 32
-  const int steps = (d + 31) / 32, per = (steps + nw - 1) / nw;
+  const int steps = (d + 31) / 32, per = (steps + nk - 1) / nk;
   const int kb = w * per * 32, ke = min(d, (w + 1) * per * 32);
-  for (int nb = 0; nb < ncols; nb += 64) {
+  for (int nb = wc * 64; nb < ncols; nb += nc * 64) {
     uint32_t b_base[4];
     bool noise_col[4];
 #pragma unroll
@@ -115,11 +120,15 @@ __global__ __launch_bounds__(kMaxThreads) void route_kernel(RouteParams p) {
 
   if (p.x != nullptr) {
     if (p.bf16) {
-      router_tile_bf16(p, lds + w * tile, ldh, t_base, ncols, nw);
+      // wide tiles: up to 4 column-group sets, the rest of the waves split
+      // the model width; every (range, column) partial lands in tile w % nk
+      const int nc = ncols > 64 ? min(4, min(nw, (ncols + 63) / 64)) : 1;
+      const int nk = nw / nc;
+      router_tile_bf16(p, lds + (w % nk) * tile, ldh, t_base, ncols, nk, nc);
       __syncthreads();
       for (int i = threadIdx.x; i < tile; i += nt) {
         float v = lds[i];
-        for (int q = 1; q < nw; ++q) v += lds[q * tile + i];  // fixed order
+        for (int q = 1; q < nk; ++q) v += lds[q * tile + i];  // fixed order
         sH[i] = v;
       }
     } else {
@@ -242,8 +251,18 @@ __global__ __launch_bounds__(256) void prob_reduce_kernel(const float* partial, 
 hipError_t launch_route(const RouteParams& p, hipStream_t stream) {
   const int blocks = route_blocks(p.T);
   const int ncols = p.E * (p.w_noise ? 2 : 1);
-  const int nw = (p.bf16 && p.x && ncols <= 64) ? kMaxWaves : 4;
-  const size_t lds = (size_t)nw * kRouteTokens * (ncols + 1) * sizeof(float);
+  const size_t tile = (size_t)kRouteTokens * (ncols + 1) * sizeof(float);
+  // bf16 tiles: up to 4 column-group sets run in parallel (wide tiles) and
+  // the other waves split the model width, 16 waves in all unless the
+  // partial tiles (one per width range) and the 32 KiB of probability
+  // partials would outgrow the 160 KiB of LDS; float32 and replay use 4 waves
+  // and one tile
+  const bool mma = p.bf16 && p.x;
+  const int nc = (mma && ncols > 64) ? std::min(4, (ncols + 63) / 64) : 1;
+  int nk = mma ? kMaxWaves / nc : 4;
+  while (mma && nk > 1 && nk * tile + sizeof(double) * kMaxWaves * 256 > 160 * 1024) nk >>= 1;
+  const int nw = mma ? nk * nc : 4;
+  const size_t lds = (mma ? nk : 1) * tile;
   hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(64 * nw), lds, stream, p);
   hipLaunchKernelGGL(prob_reduce_kernel, dim3((p.E + 3) / 4), dim3(256), 0, stream,
                      (const float*)p.prob_partial, p.prob_sum, blocks, p.E);
