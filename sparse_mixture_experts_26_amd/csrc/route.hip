@@ -108,7 +108,7 @@ __device__ void router_tile_f32(const RouteParams& p, float* sH, int ldh, int t_
 
 __global__ __launch_bounds__(kMaxThreads) void route_kernel(RouteParams p) {
   extern __shared__ float lds[];  // nw partial tiles [16][ldh]; tile 0 becomes the logits
-  __shared__ double sP[kMaxWaves][256];
+  __shared__ float sP[kMaxWaves][256];  // per-wave probability sums (float)
   const int nt = blockDim.x, nw = nt >> 6;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t_base = blockIdx.x * kRouteTokens;
@@ -223,12 +223,12 @@ __global__ __launch_bounds__(kMaxThreads) void route_kernel(RouteParams p) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
-    if (e < 256) sP[w][e] = (double)pacc[j];
+    if (e < 256) sP[w][e] = pacc[j];
   }
   __syncthreads();
   for (int e = threadIdx.x; e < p.E; e += nt) {
-    double v = sP[0][e];
-    for (int q = 1; q < nw; ++q) v += sP[q][e];  // fixed order
+    double v = (double)sP[0][e];
+    for (int q = 1; q < nw; ++q) v += (double)sP[q][e];  // fixed order, double
     p.prob_partial[(int64_t)blockIdx.x * p.E + e] = (float)v;
   }
 }
@@ -254,13 +254,16 @@ hipError_t launch_route(const RouteParams& p, hipStream_t stream) {
   const size_t tile = (size_t)kRouteTokens * (ncols + 1) * sizeof(float);
   // bf16 tiles: up to 4 column-group sets run in parallel (wide tiles) and
   // the other waves split the model width, 16 waves in all unless the
-  // partial tiles (one per width range) and the 32 KiB of probability
-  // partials would outgrow the 160 KiB of LDS; float32 and replay use 4 waves
-  // and one tile
+  // partial tiles (one per width range) and the 16 KiB of probability
+  // partials outgrow the 160 KiB of LDS; narrow tiles give up width ranges
+  // (down to 8) so that two blocks share a CU.  float32 and replay use 4
+  // waves and one tile.
   const bool mma = p.bf16 && p.x;
   const int nc = (mma && ncols > 64) ? std::min(4, (ncols + 63) / 64) : 1;
   int nk = mma ? kMaxWaves / nc : 4;
-  while (mma && nk > 1 && nk * tile + sizeof(double) * kMaxWaves * 256 > 160 * 1024) nk >>= 1;
+  const size_t fixed = sizeof(float) * kMaxWaves * 256, cap = 160 * 1024;
+  while (mma && nk > 1 && nk * tile + fixed > cap) nk >>= 1;
+  while (mma && nc == 1 && nk > 8 && 2 * (nk * tile + fixed) > cap) nk >>= 1;
   const int nw = mma ? nk * nc : 4;
   const size_t lds = (mma ? nk : 1) * tile;
   hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(64 * nw), lds, stream, p);
