@@ -103,6 +103,8 @@ struct DiagWs { double* partial_d; int32_t* partial_i; };
 struct RerouteWs {
   uint8_t* fallback; int32_t* list_a; int32_t* list_b; int32_t* fe; int32_t* rin;
   int32_t* off_prim;
+  int32_t* chunk_cnt; int32_t* chunk_base; int32_t* chunk_hist; int32_t* chunk_ebase;
+  int32_t* local_rank; int32_t* prop; int32_t* pcnt; int32_t* load_g; int32_t* n_g;
 };
 
 RouteWs carve_route(Carve& cv, const Cfg& c) {
@@ -123,6 +125,16 @@ RerouteWs carve_reroute(Carve& cv, const Cfg& c) {
   w.fe = static_cast<int32_t*>(cv.take(tk * 4));
   w.rin = static_cast<int32_t*>(cv.take(tk * 4));
   w.off_prim = static_cast<int32_t*>(cv.take((size_t)(c.E + 1) * 4));
+  const size_t ch = (size_t)std::max(reroute_chunks((int64_t)tk), 1);
+  w.chunk_cnt = static_cast<int32_t*>(cv.take(ch * 4));
+  w.chunk_base = static_cast<int32_t*>(cv.take(ch * 4));
+  w.chunk_hist = static_cast<int32_t*>(cv.take(ch * c.E * 4));
+  w.chunk_ebase = static_cast<int32_t*>(cv.take(ch * c.E * 4));
+  w.local_rank = static_cast<int32_t*>(cv.take(tk * 4));
+  w.prop = static_cast<int32_t*>(cv.take(tk * 4));
+  w.pcnt = static_cast<int32_t*>(cv.take(tk * 4));
+  w.load_g = static_cast<int32_t*>(cv.take(2 * 256 * 4));
+  w.n_g = static_cast<int32_t*>(cv.take(2 * 4));
   return w;
 }
 DiagWs carve_diag(Carve& cv, const Cfg& c) {
@@ -443,6 +455,9 @@ moe_status_t moe_dispatch_reroute(const moe_config_t* cfg, const int32_t* topk_i
   r.dest = dest; r.dest_out = dest; r.row_token = row_token; r.final_expert = final_expert;
   r.fallback = rw.fallback; r.list_a = rw.list_a; r.list_b = rw.list_b; r.fe = rw.fe;
   r.rin = rw.rin; r.off_prim = rw.off_prim;
+  r.chunk_cnt = rw.chunk_cnt; r.chunk_base = rw.chunk_base; r.chunk_hist = rw.chunk_hist;
+  r.chunk_ebase = rw.chunk_ebase; r.local_rank = rw.local_rank; r.prop = rw.prop;
+  r.pcnt = rw.pcnt; r.load_g = rw.load_g; r.n_g = rw.n_g;
   r.T = (int)c.T; r.E = (int)c.E; r.k = (int)c.k; r.C = (int)c.C;
   return hip_status(launch_reroute(r, stream));
 }
@@ -682,6 +697,10 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
       r.final_expert = L.final_expert;
       r.fallback = L.rrw.fallback; r.list_a = L.rrw.list_a; r.list_b = L.rrw.list_b;
       r.fe = L.rrw.fe; r.rin = L.rrw.rin; r.off_prim = L.rrw.off_prim;
+      r.chunk_cnt = L.rrw.chunk_cnt; r.chunk_base = L.rrw.chunk_base;
+      r.chunk_hist = L.rrw.chunk_hist; r.chunk_ebase = L.rrw.chunk_ebase;
+      r.local_rank = L.rrw.local_rank; r.prop = L.rrw.prop; r.pcnt = L.rrw.pcnt;
+      r.load_g = L.rrw.load_g; r.n_g = L.rrw.n_g;
       r.T = (int)c.T; r.E = (int)c.E; r.k = (int)c.k; r.C = (int)c.C;
       if ((st = hip_status(launch_reroute(r, stream))) != MOE_OK) return st;
     }

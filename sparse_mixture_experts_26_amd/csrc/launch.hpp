@@ -62,7 +62,19 @@ struct RerouteParams {
   int32_t* rin;             // [T*k] scratch
   int32_t* off_prim;        // [E+1] scratch: the primary offsets
   int T, E, k, C;
+  // multi-block list build and first rounds (scratch; chunks = ceil(T*k/1024))
+  int32_t* chunk_cnt;       // [chunks]
+  int32_t* chunk_base;      // [chunks]
+  int32_t* chunk_hist;      // [chunks, E]
+  int32_t* chunk_ebase;     // [chunks, E]
+  int32_t* local_rank;      // [T*k]
+  int32_t* prop;            // [T*k]
+  int32_t* pcnt;            // [T*k]
+  int32_t* load_g;          // [2, 256]
+  int32_t* n_g;             // [2]
 };
+constexpr int kRrChunk = 1024;  // list positions per block in the multi-block passes
+inline int reroute_chunks(int64_t n) { return (int)((n + kRrChunk - 1) / kRrChunk); }
 hipError_t launch_reroute(const RerouteParams& p, hipStream_t stream);
 
 // x_perm[r] = x[row_token[r]] for r < offsets[E]; row_bytes % 16 == 0.

@@ -16,7 +16,13 @@
 // Three steps after the primary dispatch (which leaves counts, offsets and
 // dest of the arrival-order pass):
 //   1. fallback lists, one wave per token that lost a slot;
-//   2. the rounds, in one block: per chunk of 1024 proposals in arrival order,
+//   2. the rounds.  Large batches build the unplaced list and run the first
+//      rounds (the large ones) as multi-block passes over chunks of 1024 list
+//      positions: proposals with their stable rank per expert inside the
+//      chunk; one block for the per-expert chunk bases, the acceptance
+//      totals and the ordered bases of the rejected pairs; acceptance and the
+//      ordered compaction.  The remaining rounds run in one block: per chunk
+//      of 1024 proposals in arrival order,
 //      ranks per expert from 9 ballots per 64-lane slice and slice
 //      histograms, a running count per expert across chunks, acceptance
 //      against the expert's load at the start of the round, and an ordered
@@ -24,6 +30,8 @@
 //   3. offsets over the final loads (same block), then dest, row_token and
 //      final_expert in a kernel of one thread per assignment.
 // Every step is ordered, so the integer results are exact and deterministic.
+#include <algorithm>
+
 #include "launch.hpp"
 
 namespace moe {
@@ -83,6 +91,221 @@ __device__ __forceinline__ int rr_excl_count(bool flag, int* wtot, int& total) {
   return before + __popcll(b & ((1ull << lane) - 1ull));
 }
 
+// Exclusive sum of v over the block in thread order, block total.
+__device__ __forceinline__ int rr_excl_sum(int v, int* wtot, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) wtot[w] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int i = 0; i < kRrWaves; ++i) {
+    const int c = wtot[i];
+    before += i < w ? c : 0;
+    all += c;
+  }
+  __syncthreads();
+  total = all;
+  return before + incl - v;
+}
+
+// ---- multi-block list build and rounds ------------------------------------------
+// Chunk c covers slots (list positions) [1024 c, 1024 c + 1024); thread order
+// is arrival order inside a chunk, chunk order across chunks.
+
+__global__ __launch_bounds__(kRrThreads) void rr_list_count_kernel(RerouteParams p) {
+  __shared__ int wtot[kRrWaves];
+  const int64_t i = (int64_t)blockIdx.x * kRrChunk + threadIdx.x;
+  const bool f = i < (int64_t)p.T * p.k && p.dest[i] < 0;
+  int total;
+  rr_excl_count(f, wtot, total);
+  if (threadIdx.x == 0) p.chunk_cnt[blockIdx.x] = total;
+}
+
+// chunk bases of the unplaced list, its length, the loads after the primary
+// pass (both load buffers), the primary offsets
+__global__ __launch_bounds__(kRrThreads) void rr_list_scan_kernel(RerouteParams p, int chunks) {
+  __shared__ int wtot[kRrWaves];
+  const int tid = threadIdx.x;
+  int carry = 0;
+  for (int c0 = 0; c0 < chunks; c0 += kRrThreads) {
+    const int c = c0 + tid;
+    const int v = c < chunks ? p.chunk_cnt[c] : 0;
+    int total;
+    const int ex = rr_excl_sum(v, wtot, total);
+    if (c < chunks) p.chunk_base[c] = carry + ex;
+    carry += total;
+  }
+  if (tid == 0) p.n_g[0] = carry;
+  for (int e = tid; e < 256; e += kRrThreads) {
+    const int c = e < p.E ? p.counts[e] : 0;
+    const int l = c < p.C ? c : p.C;
+    p.load_g[e] = l;
+    p.load_g[256 + e] = l;
+  }
+  for (int e = tid; e <= p.E; e += kRrThreads) p.off_prim[e] = p.offsets[e];
+}
+
+__global__ __launch_bounds__(kRrThreads) void rr_list_write_kernel(RerouteParams p) {
+  __shared__ int wtot[kRrWaves];
+  const int64_t i = (int64_t)blockIdx.x * kRrChunk + threadIdx.x;
+  const bool f = i < (int64_t)p.T * p.k && p.dest[i] < 0;
+  int total;
+  const int ex = rr_excl_count(f, wtot, total);
+  if (f) {
+    const int pos = p.chunk_base[blockIdx.x] + ex;
+    p.list_a[2 * pos] = (int)i;
+    p.list_a[2 * pos + 1] = 0;
+    p.fe[i] = -1;
+  }
+}
+
+// Round r, pass 1: every pair of the chunk proposes its token's next untried
+// fallback (its position j among the token's unplaced slots picks the j-th
+// one after the pointer); its rank among the chunk's proposals to the same
+// expert, in arrival order; the chunk's count per expert.
+__global__ __launch_bounds__(kRrThreads) void rr_propose_kernel(RerouteParams p, int r) {
+  __shared__ int hist[kRrWaves][257];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int k = p.k, nf = p.E - p.k;
+  const int* cur = (r & 1) ? p.list_b : p.list_a;
+  const int n = p.n_g[r & 1];
+  const int c = blockIdx.x;
+  if (c * kRrChunk >= n) return;  // the whole block: no list positions here
+  for (int x = tid; x < kRrWaves * 257; x += kRrThreads) (&hist[0][0])[x] = 0;
+  const int pos = c * kRrChunk + tid;
+  int e = kNoExpert;
+  if (pos < n) {
+    const int i = cur[2 * pos], ptr = cur[2 * pos + 1], t = i / k;
+    int jn = 0, after = 0;
+    for (int b = 1; b < k && pos - b >= 0 && cur[2 * (pos - b)] / k == t; ++b) ++jn;
+    for (int b = 1; b < k && pos + b < n && cur[2 * (pos + b)] / k == t; ++b) ++after;
+    const int q = ptr + jn;
+    if (q < nf) e = p.fallback[(int64_t)t * nf + q];
+    p.prop[pos] = e == kNoExpert ? -1 : e;
+    p.pcnt[pos] = jn + 1 + after;
+  }
+  // lanes of the wave with the same proposal: 9 ballots on the expert bits
+  uint64_t peers = ~0ull;
+#pragma unroll
+  for (int bit = 0; bit < 9; ++bit) {
+    const bool on = (e >> bit) & 1;
+    const uint64_t bal = __ballot(on);
+    peers &= on ? bal : ~bal;
+  }
+  const int r_w = __popcll(peers & ((1ull << lane) - 1ull));
+  __syncthreads();  // hist is zero
+  if (e != kNoExpert && r_w == 0) hist[w][e] = __popcll(peers);
+  __syncthreads();
+  for (int x = tid; x < p.E; x += kRrThreads) {  // per expert, exclusive over the waves
+    int run = 0;
+    for (int q = 0; q < kRrWaves; ++q) {
+      const int v = hist[q][x];
+      hist[q][x] = run;
+      run += v;
+    }
+    p.chunk_hist[(int64_t)c * p.E + x] = run;
+  }
+  __syncthreads();
+  if (pos < n && e != kNoExpert) p.local_rank[pos] = hist[w][e] + r_w;
+}
+
+// Round r, pass 2 (one block): per expert, the chunk bases (exclusive over the
+// chunks), the proposals in all and the load after the round; per chunk, how
+// many of its proposals are rejected (those of expert e ranked at or past the
+// expert's spare capacity), their bases in chunk order, and the next list's
+// length.
+__global__ __launch_bounds__(kRrThreads) void rr_round_scan_kernel(RerouteParams p, int r) {
+  __shared__ int s_spare[256];
+  __shared__ int wtot[kRrWaves];
+  const int tid = threadIdx.x;
+  const int E = p.E;
+  const int n = p.n_g[r & 1];
+  const int chunks = (n + kRrChunk - 1) / kRrChunk;
+  const int* load_in = p.load_g + (r & 1) * 256;
+  int* load_out = p.load_g + ((r + 1) & 1) * 256;
+  constexpr int kBatch = 16;
+  for (int e = tid; e < E; e += kRrThreads) {
+    int run = 0;
+    for (int c0 = 0; c0 < chunks; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        v[j] = c0 + j < chunks ? p.chunk_hist[(int64_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (c0 + j < chunks) p.chunk_ebase[(int64_t)(c0 + j) * E + e] = run;
+        run += v[j];
+      }
+    }
+    const int spare = p.C - load_in[e];
+    s_spare[e] = spare;
+    load_out[e] = load_in[e] + (run < spare ? run : spare);
+  }
+  __syncthreads();  // the bases written above are visible to the whole block
+  int carry = 0;
+  for (int c0 = 0; c0 < chunks; c0 += kRrThreads) {
+    const int c = c0 + tid;
+    int rej = 0;
+    if (c < chunks) {
+      for (int e = 0; e < E; ++e) {
+        const int cnt = p.chunk_hist[(int64_t)c * E + e];
+        int ok = s_spare[e] - p.chunk_ebase[(int64_t)c * E + e];
+        ok = ok < 0 ? 0 : (ok > cnt ? cnt : ok);
+        rej += cnt - ok;
+      }
+    }
+    int total;
+    const int ex = rr_excl_sum(rej, wtot, total);
+    if (c < chunks) p.chunk_base[c] = carry + ex;
+    carry += total;
+  }
+  if (tid == 0) p.n_g[(r + 1) & 1] = carry;
+}
+
+// Round r, pass 3: acceptance against the load at the start of the round, and
+// the ordered compaction of the rejected pairs into the next list (their
+// token pointer moves past all of the token's proposals of the round).
+__global__ __launch_bounds__(kRrThreads) void rr_accept_kernel(RerouteParams p, int r) {
+  __shared__ int wtot[kRrWaves];
+  const int tid = threadIdx.x;
+  const int* cur = (r & 1) ? p.list_b : p.list_a;
+  int* nxt = (r & 1) ? p.list_a : p.list_b;
+  const int n = p.n_g[r & 1];
+  const int c = blockIdx.x;
+  if (c * kRrChunk >= n) return;
+  const int pos = c * kRrChunk + tid;
+  const int* load_in = p.load_g + (r & 1) * 256;
+  bool rej = false;
+  int i = 0, ptr = 0;
+  if (pos < n) {
+    const int e = p.prop[pos];
+    i = cur[2 * pos];
+    ptr = cur[2 * pos + 1];
+    if (e >= 0) {
+      const int rank = p.chunk_ebase[(int64_t)c * p.E + e] + p.local_rank[pos];
+      const int l = load_in[e];
+      if (l + rank < p.C) {
+        p.fe[i] = e;
+        p.rin[i] = l + rank;
+      } else {
+        rej = true;
+      }
+    }
+  }
+  int total;
+  const int ex = rr_excl_count(rej, wtot, total);
+  if (rej) {
+    const int o = p.chunk_base[c] + ex;
+    nxt[2 * o] = i;
+    nxt[2 * o + 1] = ptr + p.pcnt[pos];
+  }
+}
+
 // The rounds, in one block of 1024 threads.  The unplaced list holds pairs
 // (assignment i, its token's fallback pointer at the start of the round) in
 // arrival order.  Chunks of proposals go through a three-stage software
@@ -106,7 +329,9 @@ constexpr int kSlices = kSub * kRrWaves;       // 64-lane slices per step
 constexpr int kRing = 3 * kStep;
 static_assert(kSlices == 64, "one lane per slice in the scans");
 
-__global__ __launch_bounds__(kRrThreads) void reroute_kernel(RerouteParams p) {
+// start_round > 0: the multi-block passes built the list and ran rounds
+// 0 .. start_round-1; the list, its length and the loads continue from there.
+__global__ __launch_bounds__(kRrThreads) void reroute_kernel(RerouteParams p, int start_round) {
   // (tag << 16) | count, then | base; rows padded to 257 words so the scan's
   // column reads (lane = slice) fall in 64 distinct banks
   __shared__ uint32_t hist[kSlices][257];
@@ -116,15 +341,26 @@ __global__ __launch_bounds__(kRrThreads) void reroute_kernel(RerouteParams p) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int E = p.E, k = p.k, C = p.C, nf = p.E - p.k;
   const int n_all = p.T * k;
-  for (int e = tid; e < 256; e += kRrThreads) {
-    const int c = e < E ? p.counts[e] : 0;
-    load[e] = c < C ? c : C;
-  }
-  for (int e = tid; e <= E; e += kRrThreads) p.off_prim[e] = p.offsets[e];
   for (int x = tid; x < kSlices * 257; x += kRrThreads) (&hist[0][0])[x] = 0u;
-  // the unplaced list, in arrival order, with pointer 0; four slots a thread
   int n = 0;
-  for (int i0 = 0; i0 < n_all; i0 += 4 * kRrThreads) {
+  int* cur = p.list_a;
+  int* nxt = p.list_b;
+  if (start_round > 0) {
+    for (int e = tid; e < 256; e += kRrThreads) load[e] = p.load_g[(start_round & 1) * 256 + e];
+    n = p.n_g[start_round & 1];
+    if (start_round & 1) {
+      cur = p.list_b;
+      nxt = p.list_a;
+    }
+  } else {
+    for (int e = tid; e < 256; e += kRrThreads) {
+      const int c = e < E ? p.counts[e] : 0;
+      load[e] = c < C ? c : C;
+    }
+    for (int e = tid; e <= E; e += kRrThreads) p.off_prim[e] = p.offsets[e];
+  }
+  // the unplaced list, in arrival order, with pointer 0; four slots a thread
+  for (int i0 = 0; start_round == 0 && i0 < n_all; i0 += 4 * kRrThreads) {
     int cnt = 0, fl[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -159,12 +395,10 @@ __global__ __launch_bounds__(kRrThreads) void reroute_kernel(RerouteParams p) {
     }
     n += all;
   }
-  int* cur = p.list_a;
-  int* nxt = p.list_b;
   uint32_t tag = 0;
   __syncthreads();
 
-  for (int round = 0; round <= nf && n > 0; ++round) {
+  for (int round = start_round; round <= nf && n > 0; ++round) {
     for (int e = tid; e < 256; e += kRrThreads) run[e] = 0;
     int m = 0;
     // position of this thread's proposal u in step-chunk c
@@ -357,7 +591,22 @@ __global__ __launch_bounds__(256) void reroute_place_kernel(RerouteParams p) {
 hipError_t launch_reroute(const RerouteParams& p, hipStream_t stream) {
   if (p.T > 0 && p.E > p.k)
     hipLaunchKernelGGL(fallback_kernel, dim3((p.T + 3) / 4), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL(reroute_kernel, dim3(1), dim3(kRrThreads), 0, stream, p);
+  // batches of 4096 assignments or more run the list build and the first
+  // (up to 3) rounds as multi-block passes; the rest stay in one block
+  const int64_t n_all = (int64_t)p.T * p.k;
+  const int chunks = reroute_chunks(n_all);
+  const int mb = n_all >= 4096 ? std::min(3, p.E - p.k + 1) : 0;
+  if (mb > 0) {
+    hipLaunchKernelGGL(rr_list_count_kernel, dim3(chunks), dim3(kRrThreads), 0, stream, p);
+    hipLaunchKernelGGL(rr_list_scan_kernel, dim3(1), dim3(kRrThreads), 0, stream, p, chunks);
+    hipLaunchKernelGGL(rr_list_write_kernel, dim3(chunks), dim3(kRrThreads), 0, stream, p);
+    for (int r = 0; r < mb; ++r) {
+      hipLaunchKernelGGL(rr_propose_kernel, dim3(chunks), dim3(kRrThreads), 0, stream, p, r);
+      hipLaunchKernelGGL(rr_round_scan_kernel, dim3(1), dim3(kRrThreads), 0, stream, p, r);
+      hipLaunchKernelGGL(rr_accept_kernel, dim3(chunks), dim3(kRrThreads), 0, stream, p, r);
+    }
+  }
+  hipLaunchKernelGGL(reroute_kernel, dim3(1), dim3(kRrThreads), 0, stream, p, mb);
   const int64_t n = (int64_t)p.T * p.k;
   if (n > 0)
     hipLaunchKernelGGL(reroute_place_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
