@@ -273,7 +273,9 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     };
     auto barrier = [&]() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
 
-    // Pipeline.  The ring holds 2.5 stages: quarters are loaded in the order
+    // Pipeline.  The wave's priority is raised while it issues a step's loads
+  // (right after the barrier), so the loads of a SIMD's two waves go out
+  // ahead of either wave's MFMAs.  The ring holds 2.5 stages: quarters are loaded in the order
     // (stage, quarter) and quarter j of that order goes to slot j % 10.  Step
     // kt waits for this wave's loads of stage kt (the 4 loads of stage kt+1's
     // first half may stay in flight); the barrier publishes stage kt and frees
@@ -296,10 +298,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     wait_vmcnt<4>();                                           \
     __builtin_amdgcn_s_waitcnt(0xc07f); /* lgkmcnt(0) */        \
     barrier();                                                 \
+    __builtin_amdgcn_s_setprio(2);                             \
     issue(((B) + 6) % kSlots, 2, (kt) + 1);                    \
     issue(((B) + 7) % kSlots, 3, (kt) + 1);                    \
     issue(((B) + 8) % kSlots, 0, (kt) + 2);                    \
     issue(((B) + 9) % kSlots, 1, (kt) + 2);                    \
+    __builtin_amdgcn_s_setprio(0);                             \
     read(f0, (B), 0);                                          \
     mfma(f1);                                                  \
     read(f1, (B), 1);                                          \
