@@ -23,18 +23,25 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 }
 
 // float32 -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN.
+// gfx950 converts in one instruction (v_cvt_pk_bf16_f32, two values at once
+// when the compiler can pair them).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ float softplus_f32(float z) {
   return fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
 }
 
-__device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + expf(-a)); }
+// 1 / (1 + e^-a) from the hardware base-2 exponential and reciprocal (each
+// within about an ulp); e^-a = 2^(-a log2 e).  Large positive a gives 1, large
+// negative a gives 0, as the exact function does in float32.
+__device__ __forceinline__ float sigmoid_f32(float a) {
+  const float e = __builtin_amdgcn_exp2f(-a * 1.44269504088896340736f);
+  return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__device__ __forceinline__ float silu_f32(float a) { return a * sigmoid_f32(a); }
 
 __device__ __forceinline__ float gelu_f32(float a) {
   return 0.5f * a * (1.0f + erff(a * 0.70710678118654752440f));
@@ -56,7 +63,7 @@ __device__ __forceinline__ void act_backward(int act, float dh, float u, float v
                                              float& dv) {
   dv = 0.0f;
   if (act == 2) {
-    const float s = 1.0f / (1.0f + expf(-u));
+    const float s = sigmoid_f32(u);
     du = dh * v * s * (1.0f + u * (1.0f - s));
     dv = dh * u * s;
   } else if (act == 1) {
