@@ -98,7 +98,7 @@ struct Carve {
 
 struct RouteWs { float* prob_partial; };
 struct DispatchWs { int32_t* local_rank; int32_t* chunk_hist; };
-struct FfnWs { TileEntry* entries; int32_t* n_entries; };
+struct FfnWs { TileEntry* entries; int32_t* n_entries; float* split; int split_cap; };
 struct DiagWs { double* partial_d; int32_t* partial_i; };
 struct RerouteWs {
   uint8_t* fallback; int32_t* list_a; int32_t* list_b; int32_t* fe; int32_t* rin;
@@ -143,11 +143,15 @@ DiagWs carve_diag(Carve& cv, const Cfg& c) {
   w.partial_i = static_cast<int32_t*>(cv.take((size_t)diag_blocks(c.T) * 2 * sizeof(int32_t)));
   return w;
 }
-FfnWs carve_ffn(Carve& cv, int64_t rows_bound, int64_t groups, int64_t S, int64_t T) {
+// Tile schedule of the tiled GEMM, plus the tail-split partials of its float32
+// (N = d) launches.
+FfnWs carve_ffn(Carve& cv, int64_t rows_bound, int64_t groups, int64_t S, int64_t T, int64_t d) {
   FfnWs w;
-  w.entries = static_cast<TileEntry*>(
-      cv.take((size_t)ffn_max_entries(rows_bound, (int)groups, (int)S, (int)T) * sizeof(TileEntry)));
+  const int64_t ent = ffn_max_entries(rows_bound, (int)groups, (int)S, (int)T);
+  w.entries = static_cast<TileEntry*>(cv.take((size_t)ent * sizeof(TileEntry)));
   w.n_entries = static_cast<int32_t*>(cv.take(4));
+  w.split_cap = (int)ffn_split_cap(ent, d);
+  w.split = static_cast<float*>(cv.take((size_t)w.split_cap * 256 * 256 * 4));
   return w;
 }
 
@@ -190,7 +194,7 @@ LayerWs carve_layer(Carve& cv, const Cfg& c, const moe_aux_t* aux) {
   w.y_rows = static_cast<float*>(pick(aux ? aux->y_rows : nullptr, (size_t)rows * c.d * 4));
   w.rw = carve_route(cv, c);
   w.dw = carve_dispatch(cv, c);
-  w.fw = carve_ffn(cv, c.R, c.E, c.S, c.T);
+  w.fw = carve_ffn(cv, c.R, c.E, c.S, c.T, c.d);
   w.gw = carve_diag(cv, c);
   w.rrw = RerouteWs{};
   if (c.rr) w.rrw = carve_reroute(cv, c);
@@ -206,7 +210,7 @@ size_t layer_ws_bytes(const Cfg& c) {
 // Expert FFN workspace for a stage call: tile schedule (+ hidden rows).
 size_t ffn_ws_bytes(const Cfg& c, int64_t rows_bound, int64_t groups, bool with_hidden) {
   Carve cv(nullptr);
-  carve_ffn(cv, rows_bound, groups, 0, c.T);
+  carve_ffn(cv, rows_bound, groups, 0, c.T, c.d);
   if (with_hidden) cv.take((size_t)rows_bound * c.h * c.esz);
   return cv.off + 256;
 }
@@ -224,6 +228,8 @@ FfnParams ffn_params(const Cfg& c, int64_t n_groups, const int32_t* offsets, int
   p.bf16 = c.bf16;
   p.entries = fw.entries;
   p.n_entries = fw.n_entries;
+  p.split = fw.split;
+  p.split_cap = fw.split_cap;
   return p;
 }
 
@@ -313,6 +319,8 @@ BwdWs carve_backward(Carve& cv, const Cfg& c, bool noise) {
                                         wgrad_entries((int)groups, (int)std::max(c.d, c.h)));
   w.fw.entries = static_cast<TileEntry*>(cv.take((size_t)ent * sizeof(TileEntry)));
   w.fw.n_entries = static_cast<int32_t*>(cv.take(4));
+  w.fw.split_cap = (int)ffn_split_cap(ffn_max_entries(c.R, (int)c.E, (int)c.S, (int)c.T), c.d);
+  w.fw.split = static_cast<float*>(cv.take((size_t)w.fw.split_cap * 256 * 256 * 4));
   w.xcd_bounds = static_cast<int32_t*>(cv.take(16 * 4));
   return w;
 }
@@ -479,7 +487,7 @@ moe_status_t moe_expert_up(const moe_config_t* cfg, int64_t n_groups, const void
   if (ws_bytes < ffn_ws_bytes(c, rows_bound, n_groups, false)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (n_groups == 0 || rows_bound == 0) return MOE_OK;
   Carve wv(ws);
-  FfnWs fw = carve_ffn(wv, rows_bound, n_groups, 0, c.T);
+  FfnWs fw = carve_ffn(wv, rows_bound, n_groups, 0, c.T, c.d);
   return run_up(c, ffn_params(c, n_groups, offsets, rows_bound, group_bound, fw), x_rows,
                 row_token, w1, w3, b1, hidden, stream);
 }
@@ -500,7 +508,7 @@ moe_status_t moe_expert_down(const moe_config_t* cfg, int64_t n_groups, const vo
   if (ws_bytes < ffn_ws_bytes(c, rows_bound, n_groups, false)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (n_groups == 0 || rows_bound == 0) return MOE_OK;
   Carve wv(ws);
-  FfnWs fw = carve_ffn(wv, rows_bound, n_groups, 0, c.T);
+  FfnWs fw = carve_ffn(wv, rows_bound, n_groups, 0, c.T, c.d);
   return run_down(c, ffn_params(c, n_groups, offsets, rows_bound, group_bound, fw), hidden, w2,
                   b2, y_rows, accumulate, stream);
 }
@@ -523,7 +531,7 @@ moe_status_t moe_expert_ffn(const moe_config_t* cfg, int64_t n_groups, const voi
   if (ws_bytes < ffn_ws_bytes(c, rows_bound, n_groups, true)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (n_groups == 0 || rows_bound == 0) return MOE_OK;
   Carve wv(ws);
-  FfnWs fw = carve_ffn(wv, rows_bound, n_groups, 0, c.T);
+  FfnWs fw = carve_ffn(wv, rows_bound, n_groups, 0, c.T, c.d);
   void* hidden = wv.take((size_t)rows_bound * c.h * c.esz);
   FfnParams p = ffn_params(c, n_groups, offsets, rows_bound, group_bound, fw);
   st = run_up(c, p, x_rows, row_token, w1, w3, b1, hidden, stream);

@@ -117,6 +117,31 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* offsets
   if (tid == 0) *n_entries = min(base, max_entries);
 }
 
+// Tile t of a launch -> its schedule entry and column block: groups of
+// kGroupM row tiles sweep the output columns together.
+__device__ __forceinline__ void tile_coords(int t, int n_entries, int n_tiles_n, int& e_idx,
+                                            int& n_idx) {
+  const int per_group = kGroupM * n_tiles_n;
+  const int grp = t / per_group, rem = t - grp * per_group;
+  const int gsize = min(kGroupM, n_entries - grp * kGroupM);
+  e_idx = grp * kGroupM + rem % gsize;
+  n_idx = rem / gsize;
+}
+
+// Tail split.  With tiles = w P + r on P persistent blocks, the last round
+// holds only r tiles and leaves P - r blocks idle.  When 2r <= P each of those
+// tiles is cut into two halves of its reduction that run on different blocks,
+// so the launch takes w + 1/2 tile times instead of w + 1.  Tiles [0, full)
+// run whole; half-unit u (0 <= u < halves) is tile full + u/2, half u%2.
+struct SplitPlan {
+  int full, halves;
+};
+__device__ __forceinline__ SplitPlan split_plan(int tiles, int P, int nk, int cap) {
+  const int w = tiles / P, r = tiles - w * P;
+  if (r > 0 && 2 * r <= P && r <= cap && nk >= 2) return {w * P, 2 * r};
+  return {tiles, 0};
+}
+
 // ACT: moe_act_t for the up projection (2 = gated SwiGLU), -1 for none
 // (float32 output); kActBwd + a: the down projection's input gradient with
 // the backward of activation a applied in the epilogue; kActWgrad: the
@@ -125,7 +150,10 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* offsets
 // Persistent: one block per CU walks tiles.  XCD x (the hardware hands block
 // P to XCD P % 8) owns the contiguous tile range [x*per, (x+1)*per) with
 // per = ceil(tiles / 8), read from the device-side schedule, so every XCD gets
-// an equal share of real tiles and neighbouring tiles share an L2.
+// an equal share of real tiles and neighbouring tiles share an L2.  Float32
+// outputs (act -1) may split the last round's tiles (split_plan): each XCD
+// then also owns a contiguous range of the half-units, run after its whole
+// tiles, and the second halves' partials are added by split_fixup_kernel.
 template <int ACT>
 __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int n_tiles_n) {
   constexpr bool GATED = ACT == 2;
@@ -142,9 +170,16 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
   const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3, nq = (gridDim.x + 7 - xcd) >> 3;
   // weight gradients: tiles differ in depth, so the XCD ranges balance work
   // (computed with the schedule); otherwise equal tile counts
-  const int per = (tiles + 7) >> 3;
+  constexpr bool SPLITS = ACT == -1;
+  const SplitPlan plan = SPLITS && p.split
+                             ? split_plan(tiles, gridDim.x, (p.K + BK - 1) / BK, p.split_cap)
+                             : SplitPlan{tiles, 0};
+  const int per = (plan.full + 7) >> 3;
   const int t_begin = WGRAD ? p.xcd_bounds[xcd] : xcd * per;
-  const int t_end = WGRAD ? p.xcd_bounds[xcd + 1] : min(tiles, (xcd + 1) * per);
+  const int t_end = WGRAD ? p.xcd_bounds[xcd + 1] : min(plan.full, (xcd + 1) * per);
+  const int per_h = (plan.halves + 7) >> 3;
+  const int h_begin = xcd * per_h, h_end = min(plan.halves, (xcd + 1) * per_h);
+  const int n_whole = t_begin + q < t_end ? (t_end - t_begin - q + nq - 1) / nq : 0;
   const int N = p.N;
   constexpr uint32_t kOOB = 0x80000000u;
 
@@ -167,13 +202,19 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     rb[ni] = br & 127;
   }
 
-  for (int t = t_begin + q; t < t_end; t += nq) {
-    // groups of 8 row tiles sweep the columns together
-    const int per_group = kGroupM * n_tiles_n;
-    const int grp = t / per_group, rem = t - grp * per_group;
-    const int gsize = min(kGroupM, n_entries - grp * kGroupM);
-    const int e_idx = grp * kGroupM + rem % gsize;
-    const int n_idx = rem / gsize;
+  for (int it = 0;; ++it) {
+    // this block's whole tiles, then its half-units
+    int t, half = -1;  // -1: whole tile; 0 / 1: first / second half of its reduction
+    if (it < n_whole) {
+      t = t_begin + q + it * nq;
+    } else {
+      const int u = h_begin + q + (it - n_whole) * nq;
+      if (u >= h_end) break;
+      t = plan.full + (u >> 1);
+      half = u & 1;
+    }
+    int e_idx, n_idx;
+    tile_coords(t, n_entries, n_tiles_n, e_idx, n_idx);
     const TileEntry te = p.entries[e_idx];
     const bool routed = te.group < p.G;
     const int gw = routed ? te.group : te.group - p.G;
@@ -198,6 +239,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
       A = static_cast<const uint16_t*>(routed ? p.a_main : p.a_shared);
     }
     const int nk = (K + BK - 1) / BK;
+    // stages [kb, kb + nks) of the reduction; chunks at or past k_end read zeros
+    const int kb = half == 1 ? nk / 2 : 0;
+    const int nks = half < 0 ? nk : (half == 0 ? nk / 2 : nk - nk / 2);
+    const int k_end = half == 0 ? (nk / 2) * BK : K;
     const int n_out0 = n_idx * (GATED ? BR / 2 : BR);
 
     // ---- direct-to-LDS loads.  A quarter is 16 loads of 1 KiB (8 rows x 128
@@ -240,11 +285,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     // quarter qq (0..3) of stage kt into ring slot `slot`; stages past the
     // end read zeros
     auto issue = [&](int slot, int qq, int kt) __attribute__((always_inline)) {
-      const int k0 = kt * BK;
+      const int k0 = (kb + kt) * BK;
       const __amdgpu_buffer_rsrc_t rs = qq >= 2 ? a_rs : (GATED && qq == 1 ? u_rs : w_rs);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint32_t kadd = (k0 + l_kc[j] * 8 < K) ? (uint32_t)k0 * 2u : kOOB;
+        const uint32_t kadd = (k0 + l_kc[j] * 8 < k_end) ? (uint32_t)k0 * 2u : kOOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rs, MOE_LDS(L + slot * kQuarter + (wid * 2 + j) * 1024), 16, off[qq][j] + kadd, 0, 0, 0);
       }
@@ -327,17 +372,17 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     issue(4, 0, 1);
     issue(5, 1, 1);
     int kt = 0;
-    for (; kt + 5 <= nk; kt += 5) {
+    for (; kt + 5 <= nks; kt += 5) {
       MOE_STEP(0, kt)
       MOE_STEP(4, kt + 1)
       MOE_STEP(8, kt + 2)
       MOE_STEP(2, kt + 3)
       MOE_STEP(6, kt + 4)
     }
-    if (kt < nk) MOE_STEP(0, kt)
-    if (kt + 1 < nk) MOE_STEP(4, kt + 1)
-    if (kt + 2 < nk) MOE_STEP(8, kt + 2)
-    if (kt + 3 < nk) MOE_STEP(2, kt + 3)
+    if (kt < nks) MOE_STEP(0, kt)
+    if (kt + 1 < nks) MOE_STEP(4, kt + 1)
+    if (kt + 2 < nks) MOE_STEP(8, kt + 2)
+    if (kt + 3 < nks) MOE_STEP(2, kt + 3)
 #undef MOE_STEP
 #undef MOE_PATTERN
     mfma(f1);  // the last sub-step
@@ -465,6 +510,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
                *reinterpret_cast<u32x2*>(out + r * ld + N + colc) = o;
              }
            });
+    } else if (SPLITS && half == 1) {
+      // second half of a split tile: float32 partials (no bias), tile-local
+      // rows of BR values
+      float* part = p.split + (int64_t)(t - plan.full) * (BM * BR);
+      emit([&](int mi, int nj, int v) __attribute__((always_inline)) { return acc[mi][nj][v]; },
+           [&](int row, int colc, const u32x4& ch) __attribute__((always_inline)) {
+             *reinterpret_cast<u32x4*>(part + row * BR + (colc - n_out0)) = ch;
+           });
     } else {
       // float32 rows (down projection, input gradients) or weight gradients
       float* out = static_cast<float*>(WGRAD && !routed ? p.out_shared : p.out);
@@ -512,10 +565,8 @@ __global__ __launch_bounds__(256) void build_wgrad_tiles_kernel(int groups, int 
   __syncthreads();
   // tile t -> its entry, as the GEMM decomposes it
   auto work = [&](int t) {
-    const int per_group = kGroupM * n_tiles_n;
-    const int grp = t / per_group, rem = t - grp * per_group;
-    const int gsize = min(kGroupM, n - grp * kGroupM);
-    const int e_idx = grp * kGroupM + rem % gsize;
+    int e_idx, n_idx;
+    tile_coords(t, n, n_tiles_n, e_idx, n_idx);
     return (long long)s_kp[min(e_idx / mt, kMaxGroups - 1)];
   };
   // each thread a contiguous chunk of tiles: chunk sums, an exclusive scan
@@ -551,7 +602,36 @@ __global__ __launch_bounds__(256) void build_wgrad_tiles_kernel(int groups, int 
   if (tiles == 0 && tid >= 1 && tid < 8) xcd_bounds[tid] = 0;
 }
 
+// Adds the second-half partials of the split tiles into the float32 output
+// (same plan as the GEMM with P of its blocks).  One block per split tile;
+// runs after the GEMM on the same stream.
+__global__ __launch_bounds__(256) void split_fixup_kernel(FfnParams p, int n_tiles_n, int P) {
+  const int n_entries = *p.n_entries;
+  const SplitPlan plan = split_plan(n_entries * n_tiles_n, P, (p.K + BK - 1) / BK, p.split_cap);
+  const int j = blockIdx.x;
+  if (2 * j >= plan.halves) return;
+  int e_idx, n_idx;
+  tile_coords(plan.full + j, n_entries, n_tiles_n, e_idx, n_idx);
+  const TileEntry te = p.entries[e_idx];
+  const int n_out0 = n_idx * BR;
+  float* out = static_cast<float*>(p.out);
+  const float* part = p.split + (int64_t)j * (BM * BR);
+  constexpr int kChunks = BR / 4;  // float4 chunks per tile row
+  for (int i = threadIdx.x; i < te.rows * kChunks; i += 256) {
+    const int row = i / kChunks, c = (i - row * kChunks) * 4;
+    if (n_out0 + c >= p.N) continue;
+    f32x4* dst = reinterpret_cast<f32x4*>(out + (int64_t)(te.c_row0 + row) * p.N + n_out0 + c);
+    *dst += *reinterpret_cast<const f32x4*>(part + row * BR + c);
+  }
+}
+
 }  // namespace
+
+int64_t ffn_split_cap(int64_t max_entries, int64_t N) {
+  // never more than half of a 256-block launch; never more than half the tiles
+  const int64_t tiles = max_entries * ((N + BR - 1) / BR);
+  return std::min<int64_t>(128, (tiles + 1) / 2);
+}
 
 int64_t ffn_max_entries(int64_t rows_bound, int G, int S, int T) {
   return (rows_bound + BM - 1) / BM + G + (int64_t)S * ((T + BM - 1) / BM);
@@ -610,6 +690,13 @@ hipError_t launch_ffn_tiled(const FfnParams& p, hipStream_t stream) {
       case 1: hipLaunchKernelGGL(ffn_tiled_kernel<1>, g, block, 0, stream, p, n_tiles_n); break;
       case 0: hipLaunchKernelGGL(ffn_tiled_kernel<0>, g, block, 0, stream, p, n_tiles_n); break;
       default: hipLaunchKernelGGL(ffn_tiled_kernel<-1>, g, block, 0, stream, p, n_tiles_n); break;
+    }
+    // second-half partials of a tail split (the plan is made on the device)
+    if (p.act == -1 && p.split && p.split_cap > 0) {
+      const int fix = (int)std::min<int64_t>(p.split_cap, grid / 2);
+      if (fix > 0)
+        hipLaunchKernelGGL(split_fixup_kernel, dim3(fix), dim3(256), 0, stream, p, n_tiles_n,
+                           (int)grid);
     }
   }
   return hipGetLastError();

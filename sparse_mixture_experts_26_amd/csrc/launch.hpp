@@ -123,10 +123,17 @@ struct FfnParams {
   const GroupDesc* gdesc;    // [G + S]
   void* out_shared;
   int32_t* xcd_bounds;       // [9] scratch: each XCD's tile range
+  // act = -1 on the tiled path: float32 partials of the tiles whose reduction
+  // is cut in two (tail split), split_cap tiles of 256 x 256; null = no split
+  float* split;
+  int split_cap;
 };
 constexpr int kActBwd = 4;   // act codes 4, 5, 6: GELU, ReLU, SwiGLU backward
 constexpr int kActWgrad = 8;
 int64_t ffn_max_entries(int64_t rows_bound, int G, int S, int T);
+// tiles the tail-split scratch of a float32 tiled launch with N output
+// columns holds (each 256 x 256 floats)
+int64_t ffn_split_cap(int64_t max_entries, int64_t N);
 hipError_t launch_ffn(const FfnParams& p, hipStream_t stream);
 
 // ---- expert-choice routing ---------------------------------------------------------

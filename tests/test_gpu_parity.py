@@ -103,8 +103,17 @@ def test_staged_entry_points_match_layer_forward(name):
     got2 = layer2.staged(dev["x"], dev.get("eps"))
     torch.cuda.synchronize()
     assert torch.equal(got2["dest"], dest1)
-    assert torch.equal(got2["y"].view(torch.int16) if cfg.dtype == "bf16" else got2["y"],
-                       y1.view(torch.int16) if cfg.dtype == "bf16" else y1)
+    if cfg.n_shared == 0:
+        # the same GEMM launches on both paths: bit-identical
+        assert torch.equal(got2["y"].view(torch.int16) if cfg.dtype == "bf16" else got2["y"],
+                           y1.view(torch.int16) if cfg.dtype == "bf16" else y1)
+    else:
+        # the staged path runs the shared experts as launches of their own, so
+        # the tail split of the down projection may cut other tiles (float32
+        # partial sums in another order): equal up to the output's last bit
+        a, b = host(got2["y"]).astype(np.float64), host(y1).astype(np.float64)
+        assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 1e-30)
+        assert rel_l2(a, b) <= 1e-4
 
 
 def test_bitwise_determinism():

@@ -1,0 +1,83 @@
+"""Tail split of the tiled expert GEMM (float32 down projection).
+
+When the last round of 256 x 256 output tiles would leave at least half the
+persistent blocks idle, those tiles are cut into two halves of their reduction
+and the second halves' partials are added afterwards.  These cases pick group
+sizes and row bounds that make the split happen, both after whole rounds of
+tiles (w >= 1) and with fewer tiles than half the launch (w = 0), and compare
+the staged expert FFN with the oracle's expert FFN per group, with biases and
+with accumulation into the output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_mixture_experts_26_amd as M
+from sparse_mixture_experts_26_amd import _lib as L
+from sparse_mixture_experts_26_amd.layer import config_of
+from tests.gpu_util import banner, host, rel_l2, require_gpu
+from workloads import LayerConfig, make_inputs, to_torch
+
+pytestmark = pytest.mark.gpu
+
+BM = BR = 256  # output tile of the tiled kernel
+
+
+def _split_expected(offsets, rows_bound, n_groups, N, K, cus):
+    """Whether the launch splits, from the documented plan (host-side mirror)."""
+    sizes = np.diff(offsets)
+    entries = int(sum((s + BM - 1) // BM for s in sizes))
+    n_tiles_n = (N + BR - 1) // BR
+    max_entries = (rows_bound + BM - 1) // BM + n_groups
+    P = min(cus, max_entries * n_tiles_n)
+    tiles = entries * n_tiles_n
+    w, r = divmod(tiles, P)
+    cap = min(128, (max_entries * n_tiles_n + 1) // 2)
+    nk = (K + 63) // 64
+    return r > 0 and 2 * r <= P and r <= cap and nk >= 2, w, r, P
+
+
+@pytest.mark.parametrize("sizes,rows_bound,d,h", [
+    ((4200, 300), 4500, 4096, 256),   # 19 x 16 tiles on 256 blocks: one whole round, 48 split
+    ((300, 200), 4096, 512, 192),     # 3 x 2 tiles on a 36-block launch: every tile split
+])
+def test_tail_split_matches_oracle(sizes, rows_bound, d, h):
+    require_gpu()
+    G = len(sizes)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows = int(offsets[-1])
+    # T = rows_bound tokens, so that moe_workspace_bytes covers the row bound
+    T = rows_bound
+    cfg = LayerConfig(name="tail_split", cfg_id=71, T=T, d=d, E=G, k=1, h=h, act="swiglu",
+                      capacity_factor=0.0, dtype="bf16", ffn_bias=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    split, w, r, P = _split_expected(offsets, rows_bound, G, d, h, cus)
+    banner(f"tail split sizes={sizes} rows_bound={rows_bound} d={d} h={h} w={w} r={r} P={P}")
+    assert split, "case no longer exercises the split"
+    inp = make_inputs(cfg, seed=3)
+    # rows gather tokens in a scrambled order
+    row_token = ((np.arange(rows, dtype=np.int64) * 7919) % T).astype(np.int32)
+    dev = {k: to_torch(v, "cuda") for k, v in inp.tensors().items()}
+    c = config_of(cfg)
+    ws = torch.empty(M.moe_workspace_bytes(c), dtype=torch.uint8, device="cuda")
+    off_d = torch.from_numpy(offsets).cuda()
+    rt_d = torch.from_numpy(row_token).cuda()
+    y = torch.empty(rows_bound, d, dtype=torch.float32, device="cuda")
+    args = (c, G, dev["x"], rt_d, off_d, rows_bound, rows_bound, dev["w1"], dev["w3"], dev["w2"],
+            dev["b1"], dev["b2"], y)
+    L.moe_expert_ffn(*args, 0, ws)
+    torch.cuda.synchronize()
+    y1 = host(y)[:rows].copy()
+    L.moe_expert_ffn(*args, 1, ws)  # accumulate: twice the result
+    torch.cuda.synchronize()
+    y2 = host(y)[:rows]
+    want = np.zeros((rows, d))
+    for g in range(G):
+        sl = slice(int(offsets[g]), int(offsets[g + 1]))
+        want[sl] = O.expert_ffn(inp.x[row_token[sl]], inp.w1[g], inp.w2[g], cfg.act,
+                                w3=inp.w3[g], b1=inp.b1[g], b2=inp.b2[g])
+    assert rel_l2(y1, want) <= 2e-2
+    # the second call adds the same terms onto the first result (in another
+    # float32 order for split tiles)
+    assert rel_l2(y2, 2 * y1) <= 1e-6
