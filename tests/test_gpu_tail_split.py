@@ -41,6 +41,9 @@ def _split_expected(offsets, rows_bound, n_groups, N, K, cus):
 @pytest.mark.parametrize("sizes,rows_bound,d,h", [
     ((4200, 300), 4500, 4096, 256),   # 19 x 16 tiles on 256 blocks: one whole round, 48 split
     ((300, 200), 4096, 512, 192),     # 3 x 2 tiles on a 36-block launch: every tile split
+    # ragged everywhere: 640 columns (2.5 column tiles) and a reduction of 200
+    # (the second half ends in a partial stage)
+    ((700, 50, 333), 4096, 640, 200),
 ])
 def test_tail_split_matches_oracle(sizes, rows_bound, d, h):
     require_gpu()
