@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void column_sum_kernel(const float* G, int T, 
   s[threadIdx.x] = a;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) s[threadIdx.x] += s[threadIdx.x + o];
+    if ((int)threadIdx.x < o) s[threadIdx.x] += s[threadIdx.x + o];
     __syncthreads();
   }
   if (threadIdx.x == 0) out[e] = s[0];

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(DispatchParams p) {
     my_r[r] = rank;
   }
   __syncthreads();
-  if (threadIdx.x < p.E) {
+  if ((int)threadIdx.x < p.E) {
     const int e = threadIdx.x;
     int run = 0;
     for (int s = 0; s < kSlices; ++s) {

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
         }
   };
   // one output element of the unit: bias, pre-activations, activation, store
-  auto emit = [&](const UnitDesc& d, int slab, int row, int col, float a, float up)
+  auto emit = [&](const UnitDesc& d, int row, int col, float a, float up)
       __attribute__((always_inline)) {
     const bool routed = d.g < p.G;
     const int gw = routed ? d.g : d.g - p.G;
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
             const int row = mf * 16 + (lane >> 4) * 4 + i;
             const int col = slab * kCols + nf * 16 + (lane & 15);
             if (row < d.rows && col < N)
-              emit(d, slab, row, col, acc[mf][nf][0][i], GATED ? acc[mf][nf][NB - 1][i] : 0.f);
+              emit(d, row, col, acc[mf][nf][0][i], GATED ? acc[mf][nf][NB - 1][i] : 0.f);
           }
       return;
     }
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
       if (GATED)
         up = ((red[0][f0 + 1][i][l] + red[1][f0 + 1][i][l]) + red[2][f0 + 1][i][l]) +
              red[3][f0 + 1][i][l];
-      emit(d, slab, row, col, a, up);
+      emit(d, row, col, a, up);
     }
     lds_barrier();  // red is reused by the next unit
   };

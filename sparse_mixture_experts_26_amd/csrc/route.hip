@@ -65,17 +65,29 @@ __device__ void router_tile_bf16(const RouteParams& p, float* part, int ldh, int
       b_base[j] = n < ncols ? (uint32_t)nn * (uint32_t)d * 2u : kOOB;
     }
     f32x4 acc[4] = {};
-#pragma unroll 4
-    for (int k0 = kb; k0 < ke; k0 += 32) {
-      const int kk = k0 + kofs;
-      const uint32_t kadd = kk < ke ? (uint32_t)kk * 2u : kOOB;
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, a_base + kadd, 0, 0));
+    // batches of 3 steps: all of a batch's loads are issued before its MFMAs
+    // (steps past the range read zeros), so a wave waits for memory once per
+    // batch rather than once per step
+    constexpr int kBatch = 3;
+    for (int k0 = kb; k0 < ke; k0 += 32 * kBatch) {
+      bf16x8 a[kBatch];
+      u32x4 bv[kBatch][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 bv = noise_col[j] ? __builtin_amdgcn_raw_buffer_load_b128(nr, b_base[j] + kadd, 0, 0)
-                                      : __builtin_amdgcn_raw_buffer_load_b128(gr, b_base[j] + kadd, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bv), acc[j], 0, 0, 0);
+      for (int u = 0; u < kBatch; ++u) {
+        const int kk = k0 + u * 32 + kofs;
+        const uint32_t kadd = kk < ke ? (uint32_t)kk * 2u : kOOB;
+        a[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, a_base + kadd, 0, 0));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bv[u][j] = noise_col[j] ? __builtin_amdgcn_raw_buffer_load_b128(nr, b_base[j] + kadd, 0, 0)
+                                  : __builtin_amdgcn_raw_buffer_load_b128(gr, b_base[j] + kadd, 0, 0);
       }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], __builtin_bit_cast(bf16x8, bv[u][j]),
+                                                          acc[j], 0, 0, 0);
     }
     // 16x16 result layout: lane holds column lane%16, rows 4*(lane/16) + i.
 #pragma unroll
