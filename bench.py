@@ -7,6 +7,12 @@ torch's current stream.  Before the timed single-call loop, the same layer
 runs through the five stage entry points with HIP events between them, for
 the per-stage times and the roofline kernel's time.  Prints ONE JSON line.
 
+The default line is the Mixtral-shaped prefill (the MFMA-bound half of the
+metric); it also carries a "decode" block: the Mixtral-shaped decode batch
+(T=32, the HBM-bound half) measured the same way on its own layer.  The
+routing diagnostics are left out of the timed step (they are not part of the
+layer); the load-balance statistics f, P, L_aux and the drop rate are in it.
+
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--train]
 
 --train times a training step instead: the forward that keeps what the
@@ -40,12 +46,14 @@ DOMINANT = {"ffn_tiled": "ffn_tiled_kernel", "ffn_skinny": "ffn_skinny_kernel",
 
 
 def algorithmic_work(cfg, offsets):
-    """Algorithmic FLOPs and bytes of the layer and of its first expert GEMM.
+    """Algorithmic FLOPs and bytes of the layer and of its routed up projection.
 
     Only work the method must do counts: the rows placed with experts (the
     final offsets: dropped assignments and padding excluded), weights of
     experts that received rows, each operand and result once.  m = weight
-    matrices per expert (3 SwiGLU, 2 otherwise)."""
+    matrices per expert (3 SwiGLU, 2 otherwise).  The "up" figures cover the
+    routed up-projection launch alone, which is what the "up" stage time
+    measures (shared experts run as launches of their own there)."""
     b = 2 if cfg.dtype == "bf16" else 4
     T, d, E, k, h, S = cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, cfg.n_shared
     kept = np.diff(np.asarray(offsets, np.int64))
@@ -53,15 +61,26 @@ def algorithmic_work(cfg, offsets):
     active = int((kept > 0).sum())
     m_up = 2 if cfg.act == "swiglu" else 1
     m = m_up + 1
-    up_flops = 2.0 * d * h * m_up * (rows + S * T)
-    down_flops = 2.0 * d * h * (rows + S * T)
+    up_flops = 2.0 * d * h * m_up * rows
+    down_flops = 2.0 * d * h * rows
+    shared_flops = 2.0 * d * h * m * S * T
     router_flops = 2.0 * T * d * E * (2 if cfg.router_noise else 1)
-    up_bytes = (m_up * h * d * b) * (active + S) + T * d * b + (rows + S * T) * h * b
+    up_bytes = (m_up * h * d * b) * active + T * d * b + rows * h * b
     layer_bytes = (m * h * d * b) * (active + S) + E * d * b * (2 if cfg.router_noise else 1) \
         + 2 * T * d * b + (T * E * 4 if cfg.router_noise else 0)
-    return {"layer_flops": up_flops + down_flops + router_flops, "layer_bytes": float(layer_bytes),
-            "up_flops": up_flops, "up_bytes": float(up_bytes), "kept_rows": rows,
-            "active_experts": active}
+    return {"layer_flops": up_flops + down_flops + shared_flops + router_flops,
+            "layer_bytes": float(layer_bytes), "up_flops": up_flops, "up_bytes": float(up_bytes),
+            "kept_rows": rows, "active_experts": active}
+
+
+def padding(kernel, offsets, group_rows):
+    """MFMA row slots the routed GEMM launches beyond the rows it must
+    compute: each group's rows rounded up to whole tiles of the chosen
+    kernel (capacity padding never happens: rows are compact)."""
+    kept = np.diff(np.asarray(offsets, np.int64))
+    slots = int(sum(group_rows(int(r)) for r in kept))
+    rows = int(kept.sum())
+    return {"padded_rows": slots - rows, "padding_frac": round((slots - rows) / max(slots, 1), 4)}
 
 
 def kernel_source_hash():
@@ -191,53 +210,27 @@ def train_step(args, cfg, layer, x, eps):
     print(json.dumps(rec), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral_prefill")
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--train", action="store_true",
-                    help="time forward (saving for the backward) + backward")
-    ap.add_argument("--calib-copy-mb", type=int, default=0,
-                    help="also run one plain device copy of this many MiB (counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; run with --gpus 1"}))
-        sys.exit(2)
+def group_rows_rule(kernel):
+    """Row slots one group occupies in the routed GEMM launch of `kernel`."""
+    if kernel == "ffn_skinny":
+        return lambda r: 32 if r > 0 else 0   # two 16-row MFMA fragments
+    if kernel == "ffn_tiled":
+        return lambda r: -(-r // 256) * 256   # whole 256-row tiles
+    return lambda r: r                        # float32 kernel: one thread per output
 
+
+def measure_forward(args, cfg, layer, x, eps, steps, warmup):
+    """Stage times (events between the stage entry points) and the timed
+    single-call loop of one workload.  Returns the record's layer fields."""
     import torch
-    from sparse_mixture_experts_26_amd.layer import MoeLayer
-    from workloads import FULL, make_inputs, to_torch
-
-    cfg = FULL[args.workload]
-    t0 = time.time()
-    inp = make_inputs(cfg, args.seed)
-    dev = {k: to_torch(v, "cuda") for k, v in inp.tensors().items()}
-    torch.cuda.synchronize()
-    print(f"[bench] {cfg.name}: inputs ready in {time.time() - t0:.1f} s", file=sys.stderr,
-          flush=True)
-    layer = MoeLayer(cfg, dev)
-    x, eps = dev["x"], dev.get("eps")
-    if args.train:
-        train_step(args, cfg, layer, x, eps)
-        return
-
-    if args.calib_copy_mb:
-        src = torch.empty(args.calib_copy_mb << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
 
     # the same layer through the stage entry points, events between stages
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         layer.staged(x, eps)
     torch.cuda.synchronize()
 
     stages = ["route", "dispatch", "up", "down"] + (["shared"] if cfg.n_shared else []) + ["combine"]
-    ev = {s: [] for s in stages}
+    ev = {s_: [] for s_ in stages}
     marks = []
 
     def mark(name):
@@ -249,37 +242,36 @@ def main():
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         mark("begin")
         layer.staged(x, eps, between=mark)
     stop.record()
     torch.cuda.synchronize()
-    staged_ms = start.elapsed_time(stop) / args.steps
+    staged_ms = start.elapsed_time(stop) / steps
     prev = None
     for name, e in marks:
         if prev is not None and name != "begin":
             ev[name].append(prev.elapsed_time(e))
         prev = e
-    stage_ms = {s: float(np.mean(v)) for s, v in ev.items() if v}
+    stage_ms = {s_: float(np.mean(v)) for s_, v in ev.items() if v}
     # the timed step: the single-call layer (after the staged loop, which
-    # also warms it up)
-    for _ in range(args.warmup):
-        layer.forward(x, eps)
+    # also warms it up); the routing diagnostics are not part of the layer
+    for _ in range(warmup):
+        layer.forward(x, eps, diag=False)
     torch.cuda.synchronize()
     s1 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     s1.record()
     step_ev[0].record()
-    for i in range(args.steps):
-        layer.forward(x, eps)
+    for i in range(steps):
+        layer.forward(x, eps, diag=False)
         step_ev[i + 1].record()
     e1.record()
     torch.cuda.synchronize()
-    ms_per_step = s1.elapsed_time(e1) / args.steps
-    step_ms = [step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps)]
-
+    ms_per_step = s1.elapsed_time(e1) / steps
+    step_ms = [step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(steps)]
 
     out = layer.out
     counts = out["counts"].cpu().numpy()
@@ -290,12 +282,12 @@ def main():
         d = torch.empty((8 + 2 * cfg.E,), dtype=torch.float32, device="cuda")
         L.moe_router_diagnostics(layer.cfg, out["logits"], out["counts"], out["dest"], d, layer.ws)
         diag = d.cpu().numpy()
-    work = algorithmic_work(cfg, out["offsets"].cpu().numpy())
+    offsets = out["offsets"].cpu().numpy()
+    work = algorithmic_work(cfg, offsets)
     kernel = "ffn_f32" if cfg.dtype == "f32" else (
         "ffn_skinny" if layer.group_bound <= 32 and (cfg.n_shared == 0 or cfg.T <= 32) else "ffn_tiled")
     up_ms = stage_ms["up"]
-    mfma_bound = kernel == "ffn_tiled"
-    if mfma_bound:
+    if kernel == "ffn_tiled":
         achieved = work["up_flops"] / (up_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
@@ -304,35 +296,29 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
     roof["traffic"] = read_traffic(cfg.name, kernel)
-    roof["kernel"] = DOMINANT[kernel]
+    roof["kernel"] = DOMINANT[kernel] + " (routed up projection)"
     roof["kernel_ms"] = round(up_ms, 4)
 
     E = cfg.E
-    tokens_per_s = cfg.T / (ms_per_step * 1e-3)
-    rec = {
-        "metric": "MoE-layer tokens/sec at 1 GPU",
-        "value": round(tokens_per_s, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    layer_gbs = work["layer_bytes"] / (ms_per_step * 1e-3) / 1e9
+    layer_tflops = work["layer_flops"] / (ms_per_step * 1e-3) / 1e12
+    return {
         "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
-        "data": "synthetic",
+        "tokens_per_s": round(cfg.T / (ms_per_step * 1e-3), 1),
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "h": cfg.h, "act": cfg.act, "n_shared": cfg.n_shared,
                    "capacity": int(layer.capacity), "dropless": cfg.dropless,
                    "parallelism": "single GPU"},
-        "layer_tflops": round(work["layer_flops"] / (ms_per_step * 1e-3) / 1e12, 2),
-        "layer_gbs": round(work["layer_bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
+        "layer_tflops": round(layer_tflops, 2),
+        "layer_gbs": round(layer_gbs, 1),
+        "layer_frac": {"mfma": round(layer_tflops / PEAK_BF16_TFLOPS, 4),
+                       "hbm": round(layer_gbs / PEAK_HBM_GBS, 4)},
         "p50_ms": round(float(np.percentile(step_ms, 50)), 4),
         "p95_ms": round(float(np.percentile(step_ms, 95)), 4),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "staged_ms_per_step": round(staged_ms, 4),
         "routing": {"kept_rows": work["kept_rows"], "active_experts": work["active_experts"],
+                    **padding(kernel, offsets, group_rows_rule(kernel)),
                     "drop_rate": round(float(stats[2 * E + 1]), 5),
                     "l_aux": round(float(stats[2 * E]), 5),
                     "load_cv": round(float(counts.std() / counts.mean()), 4),
@@ -341,6 +327,82 @@ def main():
                                                 "tokens_fully_dropped": round(float(diag[6]), 5)})},
         "roofline": roof,
     }
+
+
+def load_layer(name, seed):
+    import torch
+    from sparse_mixture_experts_26_amd.layer import MoeLayer
+    from workloads import FULL, make_inputs, to_torch
+
+    cfg = FULL[name]
+    t0 = time.time()
+    inp = make_inputs(cfg, seed)
+    dev = {k: to_torch(v, "cuda") for k, v in inp.tensors().items()}
+    torch.cuda.synchronize()
+    print(f"[bench] {cfg.name}: inputs ready in {time.time() - t0:.1f} s", file=sys.stderr,
+          flush=True)
+    return cfg, inp, MoeLayer(cfg, dev), dev["x"], dev.get("eps")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="leave out the decode-shaped layer's block")
+    ap.add_argument("--train", action="store_true",
+                    help="time forward (saving for the backward) + backward")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU (every figure is a single "
+                                   "MI355X's); run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    cfg, inp, layer, x, eps = load_layer(args.workload, args.seed)
+    if args.train:
+        train_step(args, cfg, layer, x, eps)
+        return
+
+    if args.calib_copy_mb:
+        src = torch.empty(args.calib_copy_mb << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    m = measure_forward(args, cfg, layer, x, eps, args.steps, args.warmup)
+    rec = {
+        "metric": "MoE-layer tokens/sec at 1 GPU",
+        "value": m.pop("tokens_per_s"),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        **m,
+    }
+    # The decode-shaped layer: the HBM half of the metric, its own block
+    # (same protocol, its own layer and weights; no CPU baseline).
+    if args.workload == "mixtral_prefill" and not args.no_decode:
+        del layer, x, eps
+        torch.cuda.empty_cache()
+        dcfg, _, dlayer, dx, deps = load_layer("mixtral_decode", args.seed)
+        dm = measure_forward(args, dcfg, dlayer, dx, deps, max(args.steps, 50), args.warmup)
+        dm["workload"] = dm["config"].pop("workload")
+        rec["decode"] = dm
+        del dlayer
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, inp, 15.0)
     print(json.dumps(rec), flush=True)

@@ -146,6 +146,17 @@ int64_t moe_routed_rows_bound(const moe_config_t* cfg);
  * moe_layer_forward with all moe_aux_t members NULL.  0 for an invalid config. */
 size_t moe_workspace_bytes(const moe_config_t* cfg);
 
+/* (host) Launch shape of the router kernel of moe_route for this config, no
+ * GPU call: `waves` (host) receives the wavefronts per 16-token block and
+ * `lds_bytes` (host) the block's LDS (dynamic plus static).  `device_logits`
+ * nonzero describes the bf16 path that computes the logits on the device,
+ * zero the replay or float32 path.  A block's waves take its 16 tokens in
+ * turn (token m to wave m mod waves) for the top-k step, so every token is
+ * routed whatever the count.  For tests and capacity planning; returns
+ * MOE_OK, or the status moe_route would return for an invalid config. */
+moe_status_t moe_route_launch_shape(const moe_config_t* cfg, int device_logits, int* waves,
+                                    size_t* lds_bytes);
+
 /*
  * Router and gating ([MoE&SMS] Mathematical Formulation; [LLM-09] s.2;
  * [3D-lab] Router).
@@ -222,9 +233,15 @@ moe_status_t moe_dispatch_reroute(const moe_config_t* cfg, const int32_t* topk_i
  * gather straight from the token matrix, so no permuted copy is needed).
  * The hidden layer is stored in the config dtype (bf16 for bf16 configs).
  *   offsets      [n_groups+1] device int32, nondecreasing, offsets[0] = 0
- *   rows_bound   (host) upper bound on offsets[n_groups]; sizes the launch
+ *   rows_bound   (host) upper bound on offsets[n_groups]; sizes the launch.
+ *                A HARD bound: rows at or past it are not computed.
  *   group_bound  (host) upper bound on any single group's row count; small
- *                bounds (<= 32) select the weight-streaming kernels
+ *                bounds (<= 32) select the weight-streaming kernels.  A HARD
+ *                bound: the offsets live on the device, so the host cannot
+ *                check them; when group_bound <= 32 and a group holds more
+ *                than 32 rows, that group's output rows (below rows_bound) are
+ *                all set to NaN instead of being computed, so a broken promise
+ *                shows in the result rather than passing as plausible values.
  *   accumulate   nonzero: add into y_rows instead of overwriting
  * n_groups <= E, and w1/w3/w2/b1/b2 hold at least n_groups experts.
  * Workspace: at least moe_workspace_bytes(cfg).

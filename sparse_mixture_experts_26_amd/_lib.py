@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
             "moe_capacity": (c_int64, [cfgp]),
             "moe_routed_rows_bound": (c_int64, [cfgp]),
             "moe_workspace_bytes": (c_size_t, [cfgp]),
+            "moe_route_launch_shape": (st, [cfgp, c_int, POINTER(c_int), POINTER(c_size_t)]),
             "moe_route": (st, [cfgp] + [vp] * 10 + [c_size_t, vp]),
             "moe_dispatch": (st, [cfgp] + [vp] * 8 + [c_size_t, vp]),
             "moe_dispatch_reroute": (st, [cfgp] + [vp] * 8 + [c_size_t, vp]),
@@ -102,6 +103,7 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ("moe_status_string", "moe_capacity", "moe_routed_rows_bound", "moe_workspace_bytes",
+           "moe_route_launch_shape",
            "moe_route", "moe_dispatch", "moe_dispatch_reroute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
            "moe_combine", "moe_router_diagnostics", "moe_expert_choice", "moe_combine_expert_choice",
            "moe_layer_forward", "moe_backward_workspace_bytes", "moe_layer_backward")
@@ -165,6 +167,14 @@ def moe_routed_rows_bound(cfg: MoeConfig) -> int:
 
 def moe_workspace_bytes(cfg: MoeConfig) -> int:
     return lib().moe_workspace_bytes(ctypes.byref(cfg))
+
+
+def moe_route_launch_shape(cfg: MoeConfig, device_logits: bool) -> tuple[int, int]:
+    """(waves per 16-token router block, LDS bytes per block)."""
+    waves, lds = c_int(0), c_size_t(0)
+    _check("moe_route_launch_shape", lib().moe_route_launch_shape(
+        ctypes.byref(cfg), int(bool(device_logits)), ctypes.byref(waves), ctypes.byref(lds)))
+    return waves.value, lds.value
 
 
 def moe_route(cfg, x, w_g, b_g, w_noise, eps, logits, topk_idx, topk_gate, prob_sum, ws,

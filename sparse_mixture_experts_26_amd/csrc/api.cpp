@@ -369,6 +369,18 @@ size_t moe_workspace_bytes(const moe_config_t* cfg) {
   return b;
 }
 
+moe_status_t moe_route_launch_shape(const moe_config_t* cfg, int device_logits, int* waves,
+                                    size_t* lds_bytes) {
+  Cfg c;
+  moe_status_t st = check_cfg(cfg, &c);
+  if (st != MOE_OK) return st;
+  if (!waves || !lds_bytes) return MOE_ERR_INVALID_ARGUMENT;
+  const RoutePlan rp = route_plan((int)c.E, cfg->router_noise != 0, c.bf16 && device_logits);
+  *waves = rp.waves;
+  *lds_bytes = rp.lds_bytes + rp.static_lds_bytes;
+  return MOE_OK;
+}
+
 moe_status_t moe_route(const moe_config_t* cfg, const void* x, const void* w_g,
                        const float* b_g, const void* w_noise, const float* eps,
                        float* logits, int32_t* topk_idx, float* topk_gate, float* prob_sum,

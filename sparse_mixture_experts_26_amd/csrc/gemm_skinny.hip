@@ -39,6 +39,7 @@ constexpr int kBlocksPerCU = MOE_SKINNY_BLOCKS_PER_CU;
 // the multiply side, so each keeps its own copy across unit boundaries.
 struct UnitDesc {
   int g, rows, c_row0;
+  int over;  // rows of a group that exceeds the 32-row limit (0 otherwise)
   uint32_t a_off[2];
   uint32_t b_off[kMaxNF];
   const uint16_t* W;
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
   // those loads are needed at once, and waiting for them would also wait for
   // the stage in flight.  The stage loads themselves are unconditional, so the
   // compiler's wait counts stay exact.
-  int cached_g = -1, cached_rows = 0, cached_r0 = 0;
+  int cached_g = -1, cached_rows = 0, cached_r0 = 0, cached_over = 0;
   uint32_t cached_a[2] = {kOOB, kOOB};
   auto describe = [&](int u, UnitDesc& d) __attribute__((always_inline)) {
     const int g = u / n_slabs, slab = u - g * n_slabs;
@@ -107,6 +108,10 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
         rows = p.T;
         cached_r0 = (int)(p.rows_bound + (int64_t)(g - p.G) * p.T);
       }
+      // a group above 32 rows breaks the caller's group_bound promise: its
+      // output rows are poisoned with NaN (below) rather than left partly
+      // computed
+      cached_over = rows > 32 ? rows : 0;
       rows = min(rows, 32);
 #pragma unroll
       for (int mf = 0; mf < 2; ++mf) {
@@ -123,6 +128,7 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
     d.g = g;
     d.rows = cached_rows;
     d.c_row0 = cached_r0;
+    d.over = cached_over;
     d.a_off[0] = cached_a[0];
     d.a_off[1] = cached_a[1];
     d.W = static_cast<const uint16_t*>(routed ? p.w_main : p.w_shared) + gw * wstride;
@@ -229,6 +235,20 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
       *dst = p.accumulate ? *dst + out : out;
     }
   };
+  // a group over the limit: NaN in every output row of the group (within
+  // rows_bound) and column of the unit's slab; thread i of n strides
+  auto poison = [&](const UnitDesc& d, int u, int i, int n) __attribute__((always_inline)) {
+    const int slab = u - d.g * n_slabs;
+    const int64_t lim = p.rows_bound - d.c_row0;
+    const int rows = (int)min((int64_t)d.over, lim > 0 ? lim : 0);
+    for (int o = i; o < rows * kCols; o += n) {
+      const int row = o / kCols, col = slab * kCols + (o - row * kCols);
+      if (col >= N) continue;
+      const int64_t idx = (int64_t)(d.c_row0 + row) * N + col;
+      if (p.out_bf16) static_cast<uint16_t*>(p.out)[idx] = 0x7fc0u;
+      else static_cast<float*>(p.out)[idx] = __builtin_nanf("");
+    }
+  };
   // sum the 4 waves' partial products in wave order, activation, store (with
   // WU the wave's own products, straight from the 16x16 result layout: lane
   // holds column lane%16 of rows 4*(lane/16) + i)
@@ -243,9 +263,10 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
           for (int i = 0; i < 4; ++i) {
             const int row = mf * 16 + (lane >> 4) * 4 + i;
             const int col = slab * kCols + nf * 16 + (lane & 15);
-            if (row < d.rows && col < N)
+            if (row < d.rows && col < N && !d.over)
               emit(d, row, col, acc[mf][nf][0][i], GATED ? acc[mf][nf][NB - 1][i] : 0.f);
           }
+      if (d.over) poison(d, u, lane, 64);
       return;
     }
 #pragma unroll
@@ -263,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
       const int nf = rem >> 8, i = (rem >> 6) & 3, l = rem & 63;
       const int row = mf * 16 + (l >> 4) * 4 + i;
       const int col = slab * kCols + nf * 16 + (l & 15);
-      if (row >= d.rows || col >= N) continue;
+      if (row >= d.rows || col >= N || d.over) continue;
       const int f0 = (mf * NF + nf) * NB;
       const float a = ((red[0][f0][i][l] + red[1][f0][i][l]) + red[2][f0][i][l]) + red[3][f0][i][l];
       float up = 0.f;
@@ -272,6 +293,7 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
              red[3][f0 + 1][i][l];
       emit(d, row, col, a, up);
     }
+    if (d.over) poison(d, u, threadIdx.x, kThreads);
     lds_barrier();  // red is reused by the next unit
   };
 

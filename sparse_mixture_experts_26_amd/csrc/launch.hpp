@@ -28,6 +28,10 @@ struct RouteParams {
 constexpr int kRouteTokens = 16;  // tokens per routing block
 inline int route_blocks(int64_t T) { return (int)((T + kRouteTokens - 1) / kRouteTokens); }
 hipError_t launch_route(const RouteParams& p, hipStream_t stream);
+// Launch shape of route_kernel: waves per block, dynamic and static LDS bytes
+// (mma: bf16 logits computed on the device; otherwise float32 or replay).
+struct RoutePlan { int waves; size_t lds_bytes; size_t static_lds_bytes; };
+RoutePlan route_plan(int E, bool noise, bool mma);
 
 // ---- dispatch ----------------------------------------------------------------
 struct DispatchParams {

@@ -169,11 +169,12 @@ __global__ __launch_bounds__(kMaxThreads) void route_kernel(RouteParams p) {
   __syncthreads();
 
   // Phase 2: one token per wave iteration; lane owns experts lane + 64*j.
+  // Wave w takes tokens w, w + nw, w + 2nw, ... of the block, so every one of
+  // the 16 tokens is handled whatever the wave count (which need not divide 16).
   const int nj = (p.E + 63) >> 6;
   float pacc[4] = {0.f, 0.f, 0.f, 0.f};
-  const int tpw = kRouteTokens / nw;  // tokens per wave
-  for (int mi = 0; mi < tpw; ++mi) {
-    const int m = w * tpw + mi, t = t_base + m;
+  for (int m = w; m < kRouteTokens; m += nw) {
+    const int t = t_base + m;
     if (t >= p.T) break;
     float v[4];
     float mx = -INFINITY;
@@ -260,25 +261,31 @@ __global__ __launch_bounds__(256) void prob_reduce_kernel(const float* partial, 
 
 }  // namespace
 
-hipError_t launch_route(const RouteParams& p, hipStream_t stream) {
-  const int blocks = route_blocks(p.T);
-  const int ncols = p.E * (p.w_noise ? 2 : 1);
+// bf16 tiles: up to 4 column-group sets run in parallel (wide tiles) and the
+// other waves split the model width, 16 waves in all unless the partial tiles
+// (one per width range) and the 16 KiB of probability partials outgrow the
+// 160 KiB of LDS; narrow tiles give up width ranges (down to 8) so that two
+// blocks share a CU.  float32 and replay use 4 waves and one tile.  The wave
+// count need not divide the block's 16 tokens (phase 2 strides by it).
+RoutePlan route_plan(int E, bool noise, bool mma) {
+  const int ncols = E * (noise ? 2 : 1);
   const size_t tile = (size_t)kRouteTokens * (ncols + 1) * sizeof(float);
-  // bf16 tiles: up to 4 column-group sets run in parallel (wide tiles) and
-  // the other waves split the model width, 16 waves in all unless the
-  // partial tiles (one per width range) and the 16 KiB of probability
-  // partials outgrow the 160 KiB of LDS; narrow tiles give up width ranges
-  // (down to 8) so that two blocks share a CU.  float32 and replay use 4
-  // waves and one tile.
-  const bool mma = p.bf16 && p.x;
   const int nc = (mma && ncols > 64) ? std::min(4, (ncols + 63) / 64) : 1;
   int nk = mma ? kMaxWaves / nc : 4;
   const size_t fixed = sizeof(float) * kMaxWaves * 256, cap = 160 * 1024;
   while (mma && nk > 1 && nk * tile + fixed > cap) nk >>= 1;
   while (mma && nc == 1 && nk > 8 && 2 * (nk * tile + fixed) > cap) nk >>= 1;
-  const int nw = mma ? nk * nc : 4;
-  const size_t lds = (mma ? nk : 1) * tile;
-  hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(64 * nw), lds, stream, p);
+  RoutePlan r;
+  r.waves = mma ? nk * nc : 4;
+  r.lds_bytes = (mma ? nk : 1) * tile;
+  r.static_lds_bytes = fixed;
+  return r;
+}
+
+hipError_t launch_route(const RouteParams& p, hipStream_t stream) {
+  const int blocks = route_blocks(p.T);
+  const RoutePlan rp = route_plan(p.E, p.w_noise != nullptr, p.bf16 && p.x);
+  hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(64 * rp.waves), rp.lds_bytes, stream, p);
   hipLaunchKernelGGL(prob_reduce_kernel, dim3((p.E + 3) / 4), dim3(256), 0, stream,
                      (const float*)p.prob_partial, p.prob_sum, blocks, p.E);
   return hipGetLastError();

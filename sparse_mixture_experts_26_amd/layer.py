@@ -66,12 +66,13 @@ class MoeLayer:
         self.hidden = torch.empty((max(rows, 1), h), dtype=out_dtype, device=dev)
         self.y_rows = torch.empty((max(rows, 1), d), **f32)
 
-    def forward(self, x, eps=None, logits_in=None, stream=None):
-        """moe_layer_forward with every auxiliary output captured."""
+    def forward(self, x, eps=None, logits_in=None, stream=None, diag=True):
+        """moe_layer_forward with every auxiliary output captured (the routing
+        diagnostics only when ``diag``)."""
         aux = {n: self.out[n] for n in ("logits", "topk_idx", "topk_gate", "prob_sum", "counts",
                                         "offsets", "dest", "row_token", "stats", "scores", "slot",
                                         "diag", "final_expert")
-               if n in self.out}
+               if n in self.out and (diag or n != "diag")}
         if logits_in is not None:
             aux.pop("logits")
         L.moe_layer_forward(self.cfg, self.w, x, eps, logits_in, self.out["y"], aux, self.ws,

@@ -55,3 +55,39 @@ def y_tol(cfg) -> float:
 
 def banner(msg: str):
     print(f"[gpu-case] {msg}", flush=True)
+
+
+def row_tol(cfg) -> float:
+    """Per-token output tolerance (relative L2 of one row): 5e-2 for bf16
+    layers, 1e-5 for float32.  A whole-tensor relative L2 over thousands of
+    tokens would let one wholly wrong token through."""
+    return 5e-2 if cfg.dtype == "bf16" else 1e-5
+
+
+def worst_row_error(got, want) -> float:
+    """Largest per-row relative L2 error; a row whose reference is exactly
+    zero (a token with every assignment dropped and no shared expert) must be
+    exactly zero too (reported as inf otherwise)."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    num = np.linalg.norm(got - want, axis=1)
+    den = np.linalg.norm(want, axis=1)
+    zero = den == 0
+    if np.any(num[zero] != 0):
+        return float("inf")
+    return float(np.max(num[~zero] / den[~zero], initial=0.0))
+
+
+def topk_flips(H_ref, H_gpu, k):
+    """Tokens whose top-k expert set differs between the two float32 logit
+    matrices, and each such token's gap between its k-th and (k+1)-th
+    reference logits (0 when k = E)."""
+    a = np.sort(O.select_top_k(np.asarray(H_ref, np.float32), k), axis=1)
+    b = np.sort(O.select_top_k(np.asarray(H_gpu, np.float32), k), axis=1)
+    diff = np.nonzero(np.any(a != b, axis=1))[0]
+    E = np.asarray(H_ref).shape[1]
+    if k >= E:
+        return diff, np.zeros(diff.size)
+    srt = -np.sort(-np.asarray(H_ref, np.float64), axis=1)
+    gap = srt[:, k - 1] - srt[:, k]
+    return diff, gap[diff]

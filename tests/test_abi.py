@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     assert set(names) == set(M.EXPORTS)
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
@@ -272,3 +272,30 @@ def test_backward_validation_statuses():
     assert _bwd(tc, pre=P[8] + 8) == M.MOE_ERR_UNSUPPORTED
     biased = M.make_config(64, 64, 4, 2, 128, act="gelu", ffn_bias=True)
     assert _bwd(biased, db1=None) == M.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_router_launch_shape_routes_every_token():
+    """The router's launch shape for every accepted expert count, with and
+    without noise, bf16 and float32, device logits or replay: 1-16 waves per
+    16-token block, the block's LDS within 160 KiB, and the top-k step's token
+    assignment (token m to wave m mod waves) reaching all 16 tokens.  Wave
+    counts that do not divide 16 (15 for 129-192 logit columns, 6 or 3 after
+    LDS halving) once left tokens unrouted."""
+    seen = set()
+    for E in range(1, 257):
+        for noise in (False, True):
+            if noise and E > 128:
+                continue
+            for dtype in ("bf16", "f32"):
+                for dev in (True, False):
+                    c = M.make_config(64, 4096, E, 1, 64, dtype=dtype, router_noise=noise)
+                    waves, lds = M.moe_route_launch_shape(c, dev)
+                    assert 1 <= waves <= 16, (E, noise, dtype, dev, waves)
+                    assert lds <= 160 * 1024, (E, noise, dtype, dev, lds)
+                    assert {m % waves for m in range(16)} == set(range(waves))
+                    covered = {w + i * waves for w in range(waves) for i in range(16)
+                               if w + i * waves < 16}
+                    assert covered == set(range(16))
+                    seen.add(waves)
+    # the shapes that exposed the old contiguous split are among those checked
+    assert 15 in seen and 16 in seen

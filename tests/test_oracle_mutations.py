@@ -185,6 +185,20 @@ def _diag_any_loss_is_full(H32, counts, kept, dest, C, T, k, E):
     return d
 
 
+def _stats_cv_sample_std(counts, kept, P, T, k, E):
+    st = ORIG["balance_stats"](counts, kept, P, T, k, E)
+    c = np.asarray(counts, np.float64)
+    st["load_cv"] = float(c.std(ddof=1) / c.mean()) if c.mean() > 0 else 0.0
+    return st
+
+
+def _diag_cv_sample_std(H32, counts, kept, dest, C, T, k, E):
+    d = ORIG["routing_diagnostics"](H32, counts, kept, dest, C, T, k, E)
+    c = np.asarray(counts, np.float64)
+    d["load_cv"] = float(c.std(ddof=1) / c.mean()) if c.mean() > 0 else 0.0
+    return d
+
+
 def _rr_fallback_reversed(H32, k):
     return ORIG["fallback_order"](H32, k)[:, ::-1].copy()
 
@@ -273,6 +287,8 @@ MUTATIONS = {
     "z-loss not squared": ("routing_diagnostics", _diag_z_unsquared),
     "entropy in bits": ("routing_diagnostics", _diag_entropy_bits),
     "a partial drop counted as a full one": ("routing_diagnostics", _diag_any_loss_is_full),
+    "load CV from the sample std (statistics)": ("balance_stats", _stats_cv_sample_std),
+    "load CV from the sample std (diagnostics)": ("routing_diagnostics", _diag_cv_sample_std),
     "re-route: fallbacks from the lowest rank": ("fallback_order", _rr_fallback_reversed),
     "re-route: no retry after a rejection": ("dispatch_reroute", lambda *a: _rr_variant(*a, retry=False)),
     "re-route: later arrivals win": ("dispatch_reroute", lambda *a: _rr_variant(*a, reverse_arrival=True)),
@@ -283,6 +299,7 @@ PIN_TESTS = [
     pins.test_top2_worked_example,
     pins.test_capacity_worked_example,
     pins.test_load_deviation_example,
+    pins.test_load_cv_hand_worked_values,
     pins.test_topk_brute_force_with_ties_and_signed_zero,
     pins.test_gate_closed_forms,
     pins.test_router_identity_rows_give_weight_columns,

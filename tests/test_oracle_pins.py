@@ -80,6 +80,33 @@ def test_load_deviation_example():
     assert st["deviation"] == g["printed_deviation"]
 
 
+def test_load_cv_hand_worked_values():
+    """The load coefficient of variation ('Mixture-of-experts Models', Level 3,
+    asks for it or another stated imbalance measure; read as the population
+    standard deviation of the per-expert counts over their mean), worked by
+    hand on the loads the pages print:
+      [47,26,17,10] (Level 3): mean 25, squared deviations 484+1+64+225 = 774,
+        sqrt(774/4)/25 = 0.5564171...
+      [3,2,1,2] (Level 2 capacity example): mean 2, squared deviations 2,
+        sqrt(2/4)/2 = 0.3535533...
+    A sample standard deviation would give 0.6425 and 0.4082; equal loads
+    give 0."""
+    cases = (([47, 26, 17, 10], math.sqrt(774 / 4) / 25, 0.5564171),
+             ([3, 2, 1, 2], math.sqrt(0.5) / 2, 0.3535534),
+             ([5, 5, 5, 5], 0.0, 0.0))
+    for loads, exact, printed7 in cases:
+        loads = np.array(loads)
+        E = loads.size
+        T = int(loads.sum())
+        st = O.balance_stats(loads, loads, np.full(E, 1.0 / E), T=T, k=1, E=E)
+        H = np.zeros((T, E), np.float32)
+        dest = np.zeros((T, 1), np.int32)
+        d = O.routing_diagnostics(H, loads, loads, dest, C=T, T=T, k=1, E=E)
+        for v in (st["load_cv"], d["load_cv"]):
+            assert v == pytest.approx(exact, rel=1e-12, abs=1e-15)
+            assert round(v, 7) == pytest.approx(printed7, abs=1e-7)
+
+
 # --- top-k and gates -------------------------------------------------------------
 
 def _beats(H, a, b):
