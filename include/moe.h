@@ -375,6 +375,31 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w,
                                hipStream_t stream);
 
 /*
+ * moe_layer_forward without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  The layer's intermediates live in a static
+ * scratch array of MOE_NOALLOC_SCRATCH_BYTES (128 MiB) that the library holds
+ * on every device it runs on until the process ends; the call itself
+ * allocates and frees nothing.  The scratch of the CURRENT device is used, so
+ * `stream` must belong to the current device.  Every argument means what it
+ * means for moe_layer_forward; inputs and outputs (x, y, eps, logits_in and
+ * any aux buffers) are still the caller's.  Buffers named in `aux` take their
+ * part out of the scratch, so they raise the largest layer that fits.
+ * Returns MOE_ERR_WORKSPACE_TOO_SMALL, before anything is enqueued, when the
+ * layer needs more than the scratch holds (a decode batch of the Mixtral
+ * shape needs about 21 MiB, the Switch-shaped layer about 70 MiB; prefill
+ * shapes do not fit).  All calls on one device share its scratch: calls that
+ * overlap on one device (on different streams, or from several host threads
+ * without ordering) race and give undefined results.  Nothing in the scratch
+ * needs to start at zero; it keeps the last call's contents.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+moe_status_t moe_layer_forward_noalloc(const moe_config_t* cfg, const moe_weights_t* w,
+                                       const void* x, const float* eps,
+                                       const float* logits_in, void* y, const moe_aux_t* aux,
+                                       hipStream_t stream);
+
+/*
  * ---- Backward pass (token choice) ----------------------------------------------
  *
  * The pages train these layers but print no backward ([MoE&SMS] Mathematical

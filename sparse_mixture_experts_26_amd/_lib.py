@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
             "moe_combine_expert_choice": (st, [cfgp] + [vp] * 9),
             "moe_layer_forward": (st, [cfgp, POINTER(MoeWeights), vp, vp, vp, vp,
                                        POINTER(MoeAux), vp, c_size_t, vp]),
+            "moe_layer_forward_noalloc": (st, [cfgp, POINTER(MoeWeights), vp, vp, vp, vp,
+                                               POINTER(MoeAux), vp]),
             "moe_backward_workspace_bytes": (c_size_t, [cfgp]),
             "moe_layer_backward": (st, [cfgp, POINTER(MoeWeights), vp, vp, vp, c_float, c_float,
                                         POINTER(MoeAux), POINTER(MoeGrads), vp, c_size_t, vp]),
@@ -106,7 +108,10 @@ EXPORTS = ("moe_status_string", "moe_capacity", "moe_routed_rows_bound", "moe_wo
            "moe_route_launch_shape",
            "moe_route", "moe_dispatch", "moe_dispatch_reroute", "moe_expert_ffn", "moe_expert_up", "moe_expert_down",
            "moe_combine", "moe_router_diagnostics", "moe_expert_choice", "moe_combine_expert_choice",
-           "moe_layer_forward", "moe_backward_workspace_bytes", "moe_layer_backward")
+           "moe_layer_forward", "moe_layer_forward_noalloc", "moe_backward_workspace_bytes",
+           "moe_layer_backward")
+
+MOE_NOALLOC_SCRATCH_BYTES = 128 << 20  # include/moe.h
 
 
 def make_config(T, d, E, k, h, *, act="swiglu", dtype="bf16", capacity_factor=0.0,
@@ -259,6 +264,16 @@ def moe_layer_forward(cfg, weights: dict, x, eps, logits_in, y, aux: dict | None
     _check("moe_layer_forward", lib().moe_layer_forward(
         ctypes.byref(cfg), ctypes.byref(w), _p(x), _p(eps), _p(logits_in), _p(y),
         ctypes.byref(a), wp, wn, _stream(stream)))
+
+
+def moe_layer_forward_noalloc(cfg, weights: dict, x, eps, logits_in, y, aux: dict | None,
+                              stream=None):
+    """moe_layer_forward on the library's static scratch (no workspace)."""
+    w = MoeWeights(**{k: _p(v) for k, v in weights.items() if v is not None})
+    a = MoeAux(**{k: _p(v) for k, v in (aux or {}).items() if v is not None})
+    _check("moe_layer_forward_noalloc", lib().moe_layer_forward_noalloc(
+        ctypes.byref(cfg), ctypes.byref(w), _p(x), _p(eps), _p(logits_in), _p(y),
+        ctypes.byref(a), _stream(stream)))
 
 
 def moe_backward_workspace_bytes(cfg: MoeConfig) -> int:

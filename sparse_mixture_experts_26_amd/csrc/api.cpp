@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "launch.hpp"
@@ -334,6 +335,33 @@ bool backward_fits(const Cfg& c) {
          c.T * c.d < kMaxElems && c.d * kup < kMaxElems;
 }
 
+// Scratch of moe_layer_forward_noalloc: one array per device the library
+// runs on, held until the process ends.  Host code must never pass the
+// array's name to a kernel (on the host it is only a stand-in for the symbol):
+// its device address is looked up once per device, with that device current,
+// and that address is what the launches receive.  No kernel of the layer
+// relies on zeroed workspace (every scratch word is written before it is
+// read within one call), so nothing is cleared between calls.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status_t static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -645,14 +673,16 @@ moe_status_t moe_combine_expert_choice(const moe_config_t* cfg, const float* y_r
   return hip_status(launch_stats_ec(sp, stream));
 }
 
-moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
-                               const float* eps, const float* logits_in, void* y,
-                               const moe_aux_t* aux, void* ws, size_t ws_bytes,
-                               hipStream_t stream) {
+// The whole layer on `ws`; with `noalloc` the caller passes no workspace and
+// the layer runs on the current device's static scratch instead.
+static moe_status_t layer_forward(const moe_config_t* cfg, const moe_weights_t* w,
+                                  const void* x, const float* eps, const float* logits_in,
+                                  void* y, const moe_aux_t* aux, void* ws, size_t ws_bytes,
+                                  hipStream_t stream, bool noalloc) {
   Cfg c;
   moe_status_t st = check_cfg(cfg, &c);
   if (st != MOE_OK) return st;
-  if (!w || !x || !y || !ws || !w->w1 || !w->w2) return MOE_ERR_INVALID_ARGUMENT;
+  if (!w || !x || !y || (!ws && !noalloc) || !w->w1 || !w->w2) return MOE_ERR_INVALID_ARGUMENT;
   if (c.act == MOE_ACT_SWIGLU && !w->w3) return MOE_ERR_INVALID_ARGUMENT;
   if (cfg->ffn_bias && (!w->b1 || !w->b2)) return MOE_ERR_INVALID_ARGUMENT;
   if (!logits_in) {
@@ -680,6 +710,7 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
     if (ws_bytes < cv.off + 256) return MOE_ERR_WORKSPACE_TOO_SMALL;
   }
   if (c.T == 0) return MOE_OK;
+  if (noalloc && (st = static_scratch(&ws)) != MOE_OK) return st;
   Carve wv(ws);
   LayerWs L = carve_layer(wv, c, aux);
 
@@ -783,6 +814,21 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, 
     if ((st = hip_status(launch_stats(sp, stream))) != MOE_OK) return st;
   }
   return MOE_OK;
+}
+
+moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w, const void* x,
+                               const float* eps, const float* logits_in, void* y,
+                               const moe_aux_t* aux, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  return layer_forward(cfg, w, x, eps, logits_in, y, aux, ws, ws_bytes, stream, false);
+}
+
+moe_status_t moe_layer_forward_noalloc(const moe_config_t* cfg, const moe_weights_t* w,
+                                       const void* x, const float* eps,
+                                       const float* logits_in, void* y, const moe_aux_t* aux,
+                                       hipStream_t stream) {
+  return layer_forward(cfg, w, x, eps, logits_in, y, aux, nullptr, MOE_NOALLOC_SCRATCH_BYTES,
+                       stream, true);
 }
 
 size_t moe_backward_workspace_bytes(const moe_config_t* cfg) {

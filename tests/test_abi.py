@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     assert set(names) == set(M.EXPORTS)
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
@@ -299,3 +299,22 @@ def test_router_launch_shape_routes_every_token():
                     seen.add(waves)
     # the shapes that exposed the old contiguous split are among those checked
     assert 15 in seen and 16 in seen
+
+
+def test_noalloc_rejects_layers_beyond_its_scratch():
+    """moe_layer_forward_noalloc checks the layer's intermediates against its
+    static scratch before any HIP call: the Mixtral prefill does not fit,
+    and it fits no better with every output named in aux except the large
+    ones."""
+    c = config_of(FULL["mixtral_prefill"])
+    w = {n: P[i] for i, n in enumerate(("w_g", "b_g", "w1", "w3", "w2"))}
+    with pytest.raises(M.MoeError) as e:
+        M.moe_layer_forward_noalloc(c, w, P[8], None, None, P[9], None, stream=0)
+    assert e.value.status == M.MOE_ERR_WORKSPACE_TOO_SMALL
+    # invalid arguments are still reported first
+    with pytest.raises(M.MoeError) as e:
+        M.moe_layer_forward_noalloc(c, w, None, None, None, P[9], None, stream=0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARGUMENT
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                  open(HEADER).read())
+    assert M.MOE_NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
