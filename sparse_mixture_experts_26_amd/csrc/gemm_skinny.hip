@@ -21,15 +21,22 @@
 
 #include "launch.hpp"
 
+#define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
 namespace moe {
 
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxNF = 4;  // 16-column fragments per unit: 32 or 64 output columns
+constexpr int kMaxGroups = 8;  // 8-row weight groups per unit: 32 or 64 output columns
 constexpr int UNR = 2;     // 32-deep k-steps per pipeline stage
 constexpr int kStep = 32 * UNR;  // depth of one pipeline stage
 constexpr uint32_t kOOB = 0x80000000u;
+// Cache policy of the weight loads: non-temporal.  Every weight byte is read
+// exactly once, so keeping it out of the caches' normal replacement lets the
+// stream run faster (a pure read stream of this size: 7.0 against 6.3 TB/s);
+// the token rows, which every unit of an expert re-reads, keep the default.
+constexpr int kNT = 2;
 #ifndef MOE_SKINNY_BLOCKS_PER_CU
 #define MOE_SKINNY_BLOCKS_PER_CU 2
 #endif
@@ -41,7 +48,7 @@ struct UnitDesc {
   int g, rows, c_row0;
   int over;  // rows of a group that exceeds the 32-row limit (0 otherwise)
   uint32_t a_off[2];
-  uint32_t b_off[kMaxNF];
+  uint32_t b_row[kMaxGroups];  // byte offset of this lane's weight row in group j
   const uint16_t* W;
   const uint16_t* U;
   const void* A;
@@ -69,10 +76,16 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
   constexpr bool GATED = ACT == 2;
   constexpr int NB = GATED ? 2 : 1;           // weight sets (w1 and w3 when gated)
   constexpr int NFRAG = 2 * NF * NB;          // (row fragment, column fragment, set)
-  __shared__ float red[WU ? 1 : 4][NFRAG][4][64];
+  constexpr int kGroups = kCols / 8;          // 8-row groups of a weight slab
+  constexpr int kSlot = NB * kGroups * 1024;  // one step of one wave's weights
+  constexpr int kRed = WU ? 0 : NFRAG * 1024; // one wave's partial products
+  static_assert(kGroups <= kMaxGroups, "weight slab wider than the descriptor");
+  __shared__ __attribute__((aligned(16))) char lds[4 * (kSlot + kRed)];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  char* const slot = lds + w * kSlot;
+  float* const red = reinterpret_cast<float*>(lds + 4 * kSlot);  // [4][NFRAG][4][64]
   const int K = p.K, N = p.N;
   const int64_t wstride = (int64_t)N * K;
   // a contiguous run of units per block (per wave with WU)
@@ -86,12 +99,24 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
   const int kb = WU ? 0 : min(K, w * per * kStep), ke = WU ? K : min(K, (w + 1) * per * kStep);
   const int kl = (lane >> 4) * 8;
   const int total = (u_end - u_begin) * per;
+  // Weight loads: one instruction fetches 8 whole rows of a step (8 x 128
+  // bytes, whole cache lines): lane l takes row l/8 of the group and the
+  // 16-byte chunk (l%8) ^ (l/8), which the load writes to LDS slot l%8 of
+  // that row, so the MFMA operand reads below hit distinct banks.
+  const int ld_row = lane >> 3, ld_chunk = (lane & 7) ^ ld_row;
+  // MFMA operand reads: lane (column n = lane%16, k-slot q = lane/16) of
+  // sub-step v reads chunk 4v + q of slab row 16 nf + n from its swizzled slot
+  int rd_off[UNR];
+#pragma unroll
+  for (int v = 0; v < UNR; ++v) {
+    const int n = lane & 15, q = lane >> 4;
+    rd_off[v] = (n >> 3) * 1024 + (n & 7) * 128 + ((((4 * v + q) ^ (n & 7)) & 7) << 4);
+  }
 
   // Unit descriptor.  The expert's row range and gathered rows are re-read
   // only when the expert changes (consecutive units are slabs of one expert):
   // those loads are needed at once, and waiting for them would also wait for
-  // the stage in flight.  The stage loads themselves are unconditional, so the
-  // compiler's wait counts stay exact.
+  // the stage in flight.
   int cached_g = -1, cached_rows = 0, cached_r0 = 0, cached_over = 0;
   uint32_t cached_a[2] = {kOOB, kOOB};
   auto describe = [&](int u, UnitDesc& d) __attribute__((always_inline)) {
@@ -135,10 +160,10 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
     d.U = GATED ? static_cast<const uint16_t*>(routed ? p.u_main : p.u_shared) + gw * wstride : d.W;
     d.A = routed ? p.a_main : p.a_shared;
 #pragma unroll
-    for (int nf = 0; nf < NF; ++nf) {
-      const int n = slab * kCols + nf * 16 + (lane & 15);
+    for (int j = 0; j < kGroups; ++j) {
+      const int n = slab * kCols + j * 8 + ld_row;
       // an expert with no rows reads no weights: every offset is out of range
-      d.b_off[nf] = (n < N && cached_rows > 0) ? ((uint32_t)n * (uint32_t)K + kl) * 2u : kOOB;
+      d.b_row[j] = (n < N && cached_rows > 0) ? (uint32_t)n * (uint32_t)K * 2u : kOOB;
     }
   };
 
@@ -152,18 +177,20 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
         for (int s = 0; s < NB; ++s) acc[mf][nf][s] = f32x4{};
   };
 
-  // `red` is the only memory the waves share: a barrier needs this wave's LDS
-  // operations done, not its loads in flight (which __syncthreads would drain)
+  // the partial products are the only memory the waves share: a barrier
+  // needs this wave's LDS operations done, not its loads in flight (which
+  // __syncthreads would drain)
   auto lds_barrier = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
   };
 
-  struct Stage { u32x4 a[UNR][2], b[UNR][NF][NB]; };
-  // loads of step `st` (0..per-1) of the unit described by d; `past` (past the
-  // block's last step) turns every offset out of range: the loads read zeros
-  // and move no data, and the code stays branch-free
-  auto load = [&](Stage& sg, const UnitDesc& d, int st, uint32_t past) __attribute__((always_inline)) {
+  struct AStage { u32x4 a[UNR][2]; };
+  // Loads of step `st` (0..per-1) of the unit described by d: the weights
+  // into this wave's LDS slot, the operand rows into registers.  `past` (past
+  // the block's last step) turns every offset out of range: the loads read
+  // zeros and move no data, and the code stays branch-free.
+  auto issue = [&](AStage& sa, const UnitDesc& d, int st, uint32_t past) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
         uniform_ptr(d.A), (short)0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -171,38 +198,48 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
     const __amdgpu_buffer_rsrc_t u_rs = __builtin_amdgcn_make_buffer_rsrc(
         uniform_ptr(d.U), (short)0, (int)(wstride * 2), 0x00020000);
     const int k0 = kb + st * kStep;
+    const uint32_t bk = (k0 + ld_chunk * 8 < ke ? (uint32_t)(k0 + ld_chunk * 8) * 2u : kOOB) | past;
+#pragma unroll
+    for (int s = 0; s < NB; ++s)
+#pragma unroll
+      for (int j = 0; j < kGroups; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s == 0 ? w_rs : u_rs,
+                                                 MOE_LDS(slot + (s * kGroups + j) * 1024), 16,
+                                                 (d.b_row[j] + bk) | past, 0, 0, kNT);
 #pragma unroll
     for (int v = 0; v < UNR; ++v) {
       const int kk = k0 + v * 32 + kl;
       const uint32_t kadd = (kk < ke ? (uint32_t)(k0 + v * 32) * 2u : kOOB) | past;
 #pragma unroll
       for (int mf = 0; mf < 2; ++mf)
-        sg.a[v][mf] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, (d.a_off[mf] + kadd) | past, 0, 0);
-#pragma unroll
-      for (int nf = 0; nf < NF; ++nf) {
-        sg.b[v][nf][0] = __builtin_amdgcn_raw_buffer_load_b128(w_rs, (d.b_off[nf] + kadd) | past, 0, 0);
-        if (GATED)
-          sg.b[v][nf][NB - 1] =
-              __builtin_amdgcn_raw_buffer_load_b128(u_rs, (d.b_off[nf] + kadd) | past, 0, 0);
-      }
+        sa.a[v][mf] = __builtin_amdgcn_raw_buffer_load_b128(a_rs, (d.a_off[mf] + kadd) | past, 0, 0);
     }
   };
-  // Both row fragments are always multiplied: the second reads zeros when the
-  // expert holds 16 rows or fewer, and branch-free code keeps the compiler's
-  // wait counts exact (MFMA time is negligible here).
-  auto compute = [&](const Stage& sg) __attribute__((always_inline)) {
+  struct BRegs { bf16x8 b[UNR][NF][NB]; };
+  // this step's weight fragments, from the wave's slot into registers
+  auto fetch = [&](BRegs& br) __attribute__((always_inline)) {
 #pragma unroll
     for (int v = 0; v < UNR; ++v)
 #pragma unroll
       for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
-        for (int s = 0; s < NB; ++s) {
-          const bf16x8 b = __builtin_bit_cast(bf16x8, sg.b[v][nf][s]);
+        for (int s = 0; s < NB; ++s)
+          br.b[v][nf][s] = *reinterpret_cast<const bf16x8*>(
+              slot + (s * kGroups + 2 * nf) * 1024 + rd_off[v]);
+  };
+  // Both row fragments are always multiplied: the second reads zeros when the
+  // expert holds 16 rows or fewer (MFMA time is negligible here).
+  auto compute = [&](const AStage& sa, const BRegs& br) __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < UNR; ++v)
+#pragma unroll
+      for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+        for (int s = 0; s < NB; ++s)
 #pragma unroll
           for (int mf = 0; mf < 2; ++mf)
             acc[mf][nf][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, sg.a[v][mf]), b, acc[mf][nf][s], 0, 0, 0);
-        }
+                __builtin_bit_cast(bf16x8, sa.a[v][mf]), br.b[v][nf][s], acc[mf][nf][s], 0, 0, 0);
   };
   // one output element of the unit: bias, pre-activations, activation, store
   auto emit = [&](const UnitDesc& d, int row, int col, float a, float up)
@@ -269,6 +306,9 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
       if (d.over) poison(d, u, lane, 64);
       return;
     }
+    auto R = [&](int wv, int f, int i, int l) -> float& {
+      return red[((wv * NFRAG + f) * 4 + i) * 64 + l];
+    };
 #pragma unroll
     for (int mf = 0; mf < 2; ++mf)
 #pragma unroll
@@ -276,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
 #pragma unroll
         for (int s = 0; s < NB; ++s)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) red[w][(mf * NF + nf) * NB + s][i][lane] = acc[mf][nf][s][i];
+          for (int i = 0; i < 4; ++i) R(w, (mf * NF + nf) * NB + s, i, lane) = acc[mf][nf][s][i];
     lds_barrier();
     const int slab = u - d.g * n_slabs;
     for (int o = threadIdx.x; o < 2 * NF * 256; o += kThreads) {
@@ -286,34 +326,41 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
       const int col = slab * kCols + nf * 16 + (l & 15);
       if (row >= d.rows || col >= N || d.over) continue;
       const int f0 = (mf * NF + nf) * NB;
-      const float a = ((red[0][f0][i][l] + red[1][f0][i][l]) + red[2][f0][i][l]) + red[3][f0][i][l];
+      const float a = ((R(0, f0, i, l) + R(1, f0, i, l)) + R(2, f0, i, l)) + R(3, f0, i, l);
       float up = 0.f;
       if (GATED)
-        up = ((red[0][f0 + 1][i][l] + red[1][f0 + 1][i][l]) + red[2][f0 + 1][i][l]) +
-             red[3][f0 + 1][i][l];
+        up = ((R(0, f0 + 1, i, l) + R(1, f0 + 1, i, l)) + R(2, f0 + 1, i, l)) + R(3, f0 + 1, i, l);
       emit(d, row, col, a, up);
     }
     if (d.over) poison(d, u, threadIdx.x, kThreads);
-    lds_barrier();  // red is reused by the next unit
+    lds_barrier();  // the partial products are reused by the next unit
   };
 
-  // One continuous pipeline over the block's units: the loads of step i+1 (of
-  // this unit or the next) are in flight while step i is multiplied, so a
-  // unit's reduction and stores overlap the next unit's first loads.
+  // One continuous pipeline over the block's units.  Step i: wait for its
+  // loads (weights in the slot, operand rows in registers), copy its weight
+  // fragments out of the slot, issue step i+1's loads (of this unit or the
+  // next) into the same slot, then multiply; so one step's loads are always
+  // in flight while the previous one is multiplied, and a unit's reduction
+  // and stores overlap the next unit's first loads.
   if (total <= 0) return;
   UnitDesc ld, cd;  // load side, multiply side
   describe(u_begin, ld);
   cd = ld;
   zero_acc();
-  Stage s0, s1;
-  load(s0, ld, 0, 0u);
-#define MOE_SKINNY_STEP(Scur, Snext, i)                                    \
+  AStage s0, s1;
+  issue(s0, ld, 0, 0u);
+#define MOE_SKINNY_STEP(Acur, Anext, i)                                    \
   {                                                                        \
+    __builtin_amdgcn_s_waitcnt(0x0f70); /* vmcnt(0) */                     \
+    BRegs br;                                                              \
+    fetch(br);                                                             \
+    __builtin_amdgcn_s_waitcnt(0xc07f); /* lgkmcnt(0): slot free */         \
+    asm volatile("" ::: "memory");                                         \
     const int nl = (i) + 1;                                                \
     const int nq = nl < total ? nl : total - 1;                            \
     describe(u_begin + nq / per, ld);                                      \
-    load(Snext, ld, nq % per, nl < total ? 0u : kOOB);                     \
-    compute(Scur);                                                         \
+    issue(Anext, ld, nq % per, nl < total ? 0u : kOOB);                    \
+    compute(Acur, br);                                                     \
     if ((i) % per == per - 1) {                                            \
       finish(cd, u_begin + (i) / per);                                     \
       zero_acc();                                                          \
@@ -321,8 +368,7 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
     }                                                                      \
   }
   // the loop body has no exit of its own: an exit between the two steps
-  // would join the loop's back edge with loads still in flight, and the
-  // compiler would then wait for all of them at the top of every iteration
+  // would join the loop's back edge with loads still in flight
   int i = 0;
   for (; i + 1 < total; i += 2) {
     MOE_SKINNY_STEP(s0, s1, i)
@@ -330,6 +376,8 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
   }
   if (i < total) MOE_SKINNY_STEP(s0, s1, i)
 #undef MOE_SKINNY_STEP
+  // loads issued past the end (zeros) land before the block's LDS is freed
+  __builtin_amdgcn_s_waitcnt(0x0f70);
 }
 
 }  // namespace
@@ -355,7 +403,9 @@ hipError_t launch_ffn_skinny(const FfnParams& p, hipStream_t stream) {
     const double ksplit = (double)((units + blocks - 1) / blocks) * ((kch + 3) / 4 + 3) * cand;
     const int64_t wblocks = std::min<int64_t>((units + 3) / 4, cap);
     const double whole = (double)((units + 4 * wblocks - 1) / (4 * wblocks)) * kch * cand * 1.15;
-    if (ksplit < best) { best = ksplit; nf = cand; wu = false; }
+    // a gated 64-column unit split over the waves would need 128 KiB of LDS
+    // (weight slots and partial products), leaving one block per CU
+    if (ksplit < best && !(p.act == 2 && cand == 4)) { best = ksplit; nf = cand; wu = false; }
     if (whole < best) { best = whole; nf = cand; wu = true; }
   }
   const int n_slabs = (p.N + nf * 16 - 1) / (nf * 16);
