@@ -15,25 +15,44 @@ namespace moe {
 
 namespace {
 
+// Every expert row is read exactly once, so the loads are non-temporal; each
+// slot's row gets a buffer resource of its own (an empty one for a dropped
+// slot, whose loads then read zeros and move nothing), and a chunk's loads
+// for all slots are issued before the fixed-order accumulation.
+constexpr int kNT = 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float* row, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), (short)0, bytes, 0x00020000);
+}
+
+// KM: slots per token the instance handles (k <= KM)
+template <int KM>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const int64_t t = blockIdx.x;
-  int dst[8];
-  float g[8];
+  const int d = p.d;
+  int dst[KM];
+  float g[KM];
+  __amdgpu_buffer_rsrc_t rs[KM];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
+  for (int s = 0; s < KM; ++s) {
     dst[s] = s < p.k ? p.dest[t * p.k + s] : -1;
     g[s] = s < p.k ? p.gate[t * p.k + s] : 0.f;
+    rs[s] = row_rsrc(p.y_rows + (int64_t)(dst[s] >= 0 ? dst[s] : 0) * d, dst[s] >= 0 ? d * 4 : 0);
   }
-  for (int c = threadIdx.x * 4; c < p.d; c += blockDim.x * 4) {
+  for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < p.S; ++s)
-      acc += *reinterpret_cast<const f32x4*>(p.y_shared + ((int64_t)s * p.T + t) * p.d + c);
+      acc += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                 row_rsrc(p.y_shared + ((int64_t)s * p.T + t) * d, d * 4), (uint32_t)c * 4u, 0, kNT));
+    f32x4 v[KM];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < KM; ++s)
+      v[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs[s], (uint32_t)c * 4u, 0, kNT));
+#pragma unroll
+    for (int s = 0; s < KM; ++s) {
       if (dst[s] < 0) continue;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(p.y_rows + (int64_t)dst[s] * p.d + c);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = fmaf(g[s], v[j], acc[j]);
+      for (int j = 0; j < 4; ++j) acc[j] = fmaf(g[s], v[s][j], acc[j]);
     }
     if (p.out_bf16) {
       uint32_t lo = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
@@ -41,9 +60,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
       uint2 pk;
       pk.x = lo;
       pk.y = hi;
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + t * p.d + c) = pk;
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + t * d + c) = pk;
     } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(p.y) + t * p.d + c) = acc;
+      *reinterpret_cast<f32x4*>(static_cast<float*>(p.y) + t * d + c) = acc;
     }
   }
 }
@@ -102,8 +121,13 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsParams p) {
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   const int threads = p.d >= 1024 ? 256 : (p.d >= 512 ? 128 : 64);
-  if (p.T > 0)
-    hipLaunchKernelGGL(combine_kernel, dim3(p.T), dim3(threads), 0, stream, p);
+  if (p.T > 0) {
+    const dim3 g((unsigned)p.T), b((unsigned)threads);
+    if (p.k <= 1) hipLaunchKernelGGL(combine_kernel<1>, g, b, 0, stream, p);
+    else if (p.k <= 2) hipLaunchKernelGGL(combine_kernel<2>, g, b, 0, stream, p);
+    else if (p.k <= 4) hipLaunchKernelGGL(combine_kernel<4>, g, b, 0, stream, p);
+    else hipLaunchKernelGGL(combine_kernel<8>, g, b, 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -606,12 +606,16 @@ __global__ __launch_bounds__(256) void build_wgrad_tiles_kernel(int groups, int 
 }
 
 // Adds the second-half partials of the split tiles into the float32 output
-// (same plan as the GEMM with P of its blocks).  One block per split tile;
-// runs after the GEMM on the same stream.
+// (same plan as the GEMM with P of its blocks).  kFixParts blocks per split
+// tile, 16 rows each; every thread issues its 4 chunks' loads (partial and
+// output) before adding, so a block waits for memory once.  Runs after the
+// GEMM on the same stream.
+constexpr int kFixParts = 16;
+
 __global__ __launch_bounds__(256) void split_fixup_kernel(FfnParams p, int n_tiles_n, int P) {
   const int n_entries = *p.n_entries;
   const SplitPlan plan = split_plan(n_entries * n_tiles_n, P, (p.K + BK - 1) / BK, p.split_cap);
-  const int j = blockIdx.x;
+  const int j = blockIdx.x / kFixParts, r0 = (blockIdx.x % kFixParts) * (BM / kFixParts);
   if (2 * j >= plan.halves) return;
   int e_idx, n_idx;
   tile_coords(plan.full + j, n_entries, n_tiles_n, e_idx, n_idx);
@@ -620,12 +624,24 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(FfnParams p, int n_til
   float* out = static_cast<float*>(p.out);
   const float* part = p.split + (int64_t)j * (BM * BR);
   constexpr int kChunks = BR / 4;  // float4 chunks per tile row
-  for (int i = threadIdx.x; i < te.rows * kChunks; i += 256) {
-    const int row = i / kChunks, c = (i - row * kChunks) * 4;
-    if (n_out0 + c >= p.N) continue;
-    f32x4* dst = reinterpret_cast<f32x4*>(out + (int64_t)(te.c_row0 + row) * p.N + n_out0 + c);
-    *dst += *reinterpret_cast<const f32x4*>(part + row * BR + c);
+  constexpr int kPer = (BM / kFixParts) * kChunks / 256;
+  f32x4 a[kPer], b[kPer];
+  f32x4* dst[kPer];
+  bool ok[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = threadIdx.x + u * 256;
+    const int row = r0 + i / kChunks, c = (i % kChunks) * 4;
+    ok[u] = row < te.rows && n_out0 + c < p.N;
+    dst[u] = reinterpret_cast<f32x4*>(out + (int64_t)(te.c_row0 + row) * p.N + n_out0 + c);
+    if (ok[u]) {
+      a[u] = *reinterpret_cast<const f32x4*>(part + row * BR + c);
+      b[u] = *dst[u];
+    }
   }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    if (ok[u]) *dst[u] = b[u] + a[u];
 }
 
 }  // namespace
@@ -698,8 +714,8 @@ hipError_t launch_ffn_tiled(const FfnParams& p, hipStream_t stream) {
     if (p.act == -1 && p.split && p.split_cap > 0) {
       const int fix = (int)std::min<int64_t>(p.split_cap, grid / 2);
       if (fix > 0)
-        hipLaunchKernelGGL(split_fixup_kernel, dim3(fix), dim3(256), 0, stream, p, n_tiles_n,
-                           (int)grid);
+        hipLaunchKernelGGL(split_fixup_kernel, dim3(fix * kFixParts), dim3(256), 0, stream, p,
+                           n_tiles_n, (int)grid);
     }
   }
   return hipGetLastError();

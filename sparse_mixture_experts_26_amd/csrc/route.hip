@@ -247,13 +247,23 @@ __global__ __launch_bounds__(kMaxThreads) void route_kernel(RouteParams p) {
 }
 
 // prob_sum[e] = sum over routing blocks: one wave per expert, each lane sums a
-// fixed strided subset in double, then a fixed butterfly; deterministic.
+// fixed strided subset in double, then a fixed butterfly; deterministic.  A
+// lane's loads are issued 8 at a time before their adds (in the same order),
+// so a large batch waits for memory once per 8 partials, not once per partial.
 __global__ __launch_bounds__(256) void prob_reduce_kernel(const float* partial, float* out,
                                                           int nblocks, int E) {
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (e >= E) return;
   double s = 0.0;
-  for (int b = lane; b < nblocks; b += 64) s += (double)partial[(int64_t)b * E + e];
+  int b = lane;
+  for (; b + 7 * 64 < nblocks; b += 8 * 64) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = partial[(int64_t)(b + j * 64) * E + e];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += (double)v[j];
+  }
+  for (; b < nblocks; b += 64) s += (double)partial[(int64_t)b * E + e];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
   if (lane == 0) out[e] = (float)s;
