@@ -922,20 +922,40 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
                                 gr->dw_noise, stream));
   if (cfg->router_bias) MOE_TRY(launch_column_sum(B.dH, (int)c.T, G, gr->db_g, stream));
 
-  // 3. transposed weights: w2t[g] = w2[g]^T [h,d]; w13t[g] = [w1[g]^T | w3[g]^T] [d, Kup]
+  // 3. transposed weights: w2t[g] = w2[g]^T [h,d]; w13t[g] = [w1[g]^T | w3[g]^T] [d, Kup].
+  //    The bf16 tiled GEMMs can read W2, W1 and W3 as stored ([K][N]
+  //    weights) instead.  That form runs about 22% slower (two 8-byte LDS
+  //    transpose reads per operand fragment instead of one 16-byte read),
+  //    while a copy costs both directions of the weight bytes at about
+  //    5 TB/s: per group of d x h weights the copy costs as much as the
+  //    slowdown on about 2000 rows (2 * 2dh / 5e12 = 0.22 * 2 * rows * d * h /
+  //    1.1e15).  Below that many rows per group the stored layout is read.
   const int esz = (int)c.esz;
   const size_t gsz2 = (size_t)c.h * c.d * c.esz, gsz13 = (size_t)c.d * kup * c.esz;
   char* w2t = static_cast<char*>(B.w2t);
   char* w13t = static_cast<char*>(B.w13t);
-  MOE_TRY(launch_transpose(w->w2, G, (int)c.d, (int)c.h, w2t, (int)c.d, 0, esz, stream));
-  MOE_TRY(launch_transpose(w->w1, G, (int)c.h, (int)c.d, w13t, (int)kup, 0, esz, stream));
-  if (swi) MOE_TRY(launch_transpose(w->w3, G, (int)c.h, (int)c.d, w13t, (int)kup, (int)c.h, esz, stream));
-  if (S > 0) {
-    MOE_TRY(launch_transpose(w->ws2, S, (int)c.d, (int)c.h, w2t + G * gsz2, (int)c.d, 0, esz, stream));
-    MOE_TRY(launch_transpose(w->ws1, S, (int)c.h, (int)c.d, w13t + G * gsz13, (int)kup, 0, esz, stream));
-    if (swi)
-      MOE_TRY(launch_transpose(w->ws3, S, (int)c.h, (int)c.d, w13t + G * gsz13, (int)kup, (int)c.h,
-                               esz, stream));
+  FfnParams fp = ffn_params(c, c.E, sv->offsets, c.R, c.C, B.fw);
+  fp.S = S;
+  const bool few_rows = c.R + c.S * c.T < 2000 * (c.E + c.S);
+  const bool bt_down = c.bf16 && few_rows;  // (its input gradient is always tiled)
+  // the up projections' input gradient runs where launch_ffn sends it: the
+  // tiled path unless every group holds at most 32 rows
+  const bool up_tiled = !(fp.group_bound <= 32 && (S == 0 || c.T <= 32));
+  const bool bt_up = c.bf16 && few_rows && up_tiled && (!swi || c.h % 64 == 0);
+  if (!bt_down) {
+    MOE_TRY(launch_transpose(w->w2, G, (int)c.d, (int)c.h, w2t, (int)c.d, 0, esz, stream));
+    if (S > 0)
+      MOE_TRY(launch_transpose(w->ws2, S, (int)c.d, (int)c.h, w2t + G * gsz2, (int)c.d, 0, esz, stream));
+  }
+  if (!bt_up) {
+    MOE_TRY(launch_transpose(w->w1, G, (int)c.h, (int)c.d, w13t, (int)kup, 0, esz, stream));
+    if (swi) MOE_TRY(launch_transpose(w->w3, G, (int)c.h, (int)c.d, w13t, (int)kup, (int)c.h, esz, stream));
+    if (S > 0) {
+      MOE_TRY(launch_transpose(w->ws1, S, (int)c.h, (int)c.d, w13t + G * gsz13, (int)kup, 0, esz, stream));
+      if (swi)
+        MOE_TRY(launch_transpose(w->ws3, S, (int)c.h, (int)c.d, w13t + G * gsz13, (int)kup, (int)c.h,
+                                 esz, stream));
+    }
   }
 
   // 4. input gradient of the down projection with the activation backward:
@@ -945,11 +965,12 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
     MOE_TRY(launch_to_bf16(dy, c.T * c.d, static_cast<uint16_t*>(B.dy_lp), stream));
     dy_op = B.dy_lp;
   }
-  FfnParams fp = ffn_params(c, c.E, sv->offsets, c.R, c.C, B.fw);
-  fp.S = S;
   FfnParams dd = fp;
   dd.a_main = dy_op; dd.a_shared = dy_op; dd.gather = sv->row_token; dd.a_from_c = 0;
   dd.w_main = w2t; dd.w_shared = w2t + G * gsz2; dd.u_main = nullptr; dd.u_shared = nullptr;
+  if (bt_down) {  // W2 [d][h] as stored: K = d rows of N = h
+    dd.w_main = w->w2; dd.w_shared = w->ws2; dd.bt = 1; dd.kh = 0;
+  }
   dd.bias_main = nullptr; dd.bias_shared = nullptr;
   dd.out = B.duv; dd.out_bf16 = c.bf16; dd.accumulate = 0;
   dd.N = (int)c.h; dd.K = (int)c.d; dd.act = kActBwd + c.act;
@@ -960,6 +981,10 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   FfnParams du = fp;
   du.a_main = B.duv; du.a_shared = B.duv; du.gather = nullptr; du.a_from_c = 1;
   du.w_main = w13t; du.w_shared = w13t + G * gsz13; du.u_main = nullptr; du.u_shared = nullptr;
+  if (bt_up) {  // W1 (and W3) [h][d] as stored: K = h (+ h) rows of N = d
+    du.w_main = w->w1; du.w_shared = w->ws1; du.u_main = w->w3; du.u_shared = w->ws3;
+    du.bt = 1; du.kh = swi ? (int)c.h : 0;
+  }
   du.bias_main = nullptr; du.bias_shared = nullptr;
   du.out = B.dxr; du.out_bf16 = 0; du.accumulate = 0;
   du.N = (int)c.d; du.K = (int)kup; du.act = -1;

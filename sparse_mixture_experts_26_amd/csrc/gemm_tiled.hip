@@ -64,6 +64,14 @@ __device__ __forceinline__ int swz(int row) { return (row ^ ((row & 31) >> 3)) &
 
 #define MOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
+// [K][N] weight quarters: 16-byte chunk c of row k sits at slot
+// bt_swz(c) ^ 2 (k mod 4) of its 256-byte row.  A transpose read's 16 lanes
+// take 4 rows x 32 bytes (chunks c, c+1, c even): the 2 (k mod 4) term puts
+// the 4 rows in distinct 32-byte slots of 128 bytes, and bt_swz (chunk bit 1
+// copied into bit 3; an involution) puts the other 16 lanes read with them
+// (chunks c+2, c+3, same rows) into the other 128 bytes.
+__device__ __forceinline__ int bt_swz(int c) { return c ^ (((c >> 1) & 1) << 3); }
+
 // s_waitcnt with vmcnt = N (gfx9 encoding: vmcnt bits [3:0] and [15:14]) and
 // the expcnt / lgkmcnt fields at their maxima, i.e. not waited on.
 template <int N>
@@ -157,10 +165,23 @@ __device__ __forceinline__ SplitPlan split_plan(int tiles, int P, int nk, int ca
 // outputs (act -1) may split the last round's tiles (split_plan): each XCD
 // then also owns a contiguous range of the half-units, run after its whole
 // tiles, and the second halves' partials are added by split_fixup_kernel.
-template <int ACT>
+//
+// BT: the weights are stored [K][N] per group (output columns contiguous:
+// w_main / w_shared of group g hold row k at k*N; with p.kh > 0 rows k >= kh
+// come from the second set u_main / u_shared, row k - kh), as the backward's
+// input gradients find them (W2 for the down projection, W1 and W3 for the up
+// projections), so no transposed copy is made.  A weight quarter then holds
+// 64 rows of k, each 128 columns (256 bytes) wide, loaded as whole lines; the
+// MFMA operand (8 consecutive k of one column per lane) comes from two LDS
+// transpose reads (ds_read_b64_tr_b16: within each 16 lanes, lane j gives 4
+// consecutive columns of row k0 + j/4 at column 4(j%4), and lane i receives
+// column i of rows k0..k0+3).  The 16-byte chunks of row k are XOR-swizzled by
+// 2 (k mod 4), so the 4 rows of a read hit distinct banks.
+template <int ACT, bool BT = false>
 __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int n_tiles_n) {
   constexpr bool GATED = ACT == 2;
   constexpr bool WGRAD = ACT == kActWgrad;
+  static_assert(!BT || (!GATED && !WGRAD), "[K][N] weights: plain or backward forms only");
   __shared__ __attribute__((aligned(16))) char L[kSlots * kQuarter];
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform per wave; say so, or LDS-destination and buffer
@@ -204,6 +225,20 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     qb[ni] = br >> 7;
     rb[ni] = br & 127;
   }
+  // BT: byte offsets, inside a weight quarter and before the sub-step's
+  // 16 rows (s * 4096), of this lane's two transpose reads per fragment
+  int tr_off[2][2];
+  if constexpr (BT) {
+    const int g16 = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int k = 8 * (g16 >> 1) + 4 * t + (j >> 2);   // row inside the sub-step
+        const int n = rb[ni] + 16 * (g16 & 1) + 4 * (j & 3);  // column inside the quarter
+        tr_off[ni][t] = k * 256 + ((bt_swz(n >> 3) ^ (2 * (j >> 2))) << 4) + (n & 7) * 2;
+      }
+  }
 
   for (int it = 0;; ++it) {
     // this block's whole tiles, then its half-units
@@ -236,9 +271,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
       W = static_cast<const uint16_t*>(p.w_main) + (int64_t)N * gd.poff;
       U = W;
     } else {
-      W = static_cast<const uint16_t*>(routed ? p.w_main : p.w_shared) + gw * wstride;
+      // BT with a second weight set: each set holds kh rows of N per group
+      const int64_t gstride = (BT && p.kh > 0) ? (int64_t)N * p.kh : wstride;
+      W = static_cast<const uint16_t*>(routed ? p.w_main : p.w_shared) + gw * gstride;
       U = W;
-      if (GATED) U = static_cast<const uint16_t*>(routed ? p.u_main : p.u_shared) + gw * wstride;
+      if (GATED || (BT && p.kh > 0))
+        U = static_cast<const uint16_t*>(routed ? p.u_main : p.u_shared) + gw * gstride;
       A = static_cast<const uint16_t*>(routed ? p.a_main : p.a_shared);
     }
     const int nk = (K + BK - 1) / BK;
@@ -257,17 +295,26 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     // past K need no branches.
     const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(A), (short)0, 0x7fffffff, 0x00020000);
+    // bytes of one group's weight set (BT with a second set: kh rows each)
+    const int wbytes = (int)((BT && p.kh > 0 ? (int64_t)N * p.kh : wstride) * 2);
     const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(W), (short)0, (int)(wstride * 2), 0x00020000);
+        const_cast<uint16_t*>(W), (short)0, wbytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t u_rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(U), (short)0, (int)(wstride * 2), 0x00020000);
+        const_cast<uint16_t*>(U), (short)0, wbytes, 0x00020000);
     uint32_t off[4][4];  // [quarter][load]
     int l_kc[4];
+    int l_kq[4];  // BT: row (k) inside the stage of this lane's weight loads
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rq = (((wid & 3) + 4 * (j >> 1)) * 2 + (j & 1)) * 8 + (lane >> 3);  // row inside a quarter
       const int kc = (lane & 7) ^ swz(rq);
       l_kc[j] = kc;
+      // BT: load j fills rows 4b .. 4b+3 of the stage, 256 bytes each, b the
+      // same 1 KiB block index; lane i takes row 4b + i/16 and the chunk that
+      // the row's swizzle stores at slot i%16
+      const int kq = ((((wid & 3) + 4 * (j >> 1)) * 2 + (j & 1)) << 2) + (lane >> 4);
+      const int gc = bt_swz((lane & 15) ^ (2 * (kq & 3)));
+      l_kq[j] = kq;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int row = h * 128 + rq;  // tile row
@@ -275,8 +322,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
         int arow = p.a_from_c ? te.c_row0 + row : te.a_row0 + row;
         if (ok && routed && p.gather && !p.a_from_c) arow = p.gather[arow];
         off[2 + h][j] = ok ? ((uint32_t)arow * (uint32_t)K + kc * 8) * 2u : kOOB;
-        const int n = n_out0 + (GATED ? rq : row);
-        off[h][j] = n < N ? ((uint32_t)n * (uint32_t)K + kc * 8) * 2u : kOOB;
+        if constexpr (BT) {
+          const int n = n_out0 + h * 128 + 8 * gc;
+          off[h][j] = n < N ? ((uint32_t)kq * (uint32_t)N + n) * 2u : kOOB;
+        } else {
+          const int n = n_out0 + (GATED ? rq : row);
+          off[h][j] = n < N ? ((uint32_t)n * (uint32_t)K + kc * 8) * 2u : kOOB;
+        }
       }
     }
 
@@ -290,11 +342,21 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     // end read zeros
     auto issue = [&](int slot, int qq, int kt) __attribute__((always_inline)) {
       const int k0 = (kb + kt) * BK;
-      const __amdgpu_buffer_rsrc_t rs = qq >= 2 ? a_rs : (GATED && qq == 1 ? u_rs : w_rs);
+      __amdgpu_buffer_rsrc_t rs = qq >= 2 ? a_rs : (GATED && qq == 1 ? u_rs : w_rs);
+      // BT weight quarters: stage rows k0.. of the set holding them
+      int kset = k0;
+      if (BT && qq < 2 && p.kh > 0 && k0 >= p.kh) {
+        rs = u_rs;
+        kset = k0 - p.kh;
+      }
       if (wid < 4) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t kadd = (k0 + l_kc[j] * 8 < k_end) ? (uint32_t)k0 * 2u : kOOB;
+          uint32_t kadd;
+          if (BT && qq < 2)
+            kadd = (k0 + l_kq[j] < k_end) ? (uint32_t)kset * (uint32_t)N * 2u : kOOB;
+          else
+            kadd = (k0 + l_kc[j] * 8 < k_end) ? (uint32_t)k0 * 2u : kOOB;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               rs, MOE_LDS(L + slot * kQuarter + ((wid + 4 * (j >> 1)) * 2 + (j & 1)) * 1024), 16,
               off[qq][j] + kadd, 0, 0, 0);
@@ -313,8 +375,23 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
       const char* pa = L + (sa >= kSlots ? sa - kSlots : sa) * kQuarter + r;
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) f.a[mi] = *reinterpret_cast<const bf16x8*>(pa + mi * 32 * 128);
-      f.b[0] = *reinterpret_cast<const bf16x8*>(L + (sb0 >= kSlots ? sb0 - kSlots : sb0) * kQuarter + rb[0] * 128 + r);
-      f.b[1] = *reinterpret_cast<const bf16x8*>(L + (sb1 >= kSlots ? sb1 - kSlots : sb1) * kQuarter + rb[1] * 128 + r);
+      if constexpr (BT) {
+        // two transpose reads give the 8 consecutive k of one column
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const int sb = ni == 0 ? sb0 : sb1;
+          const char* qp = L + (sb >= kSlots ? sb - kSlots : sb) * kQuarter + s * 4096;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)MOE_LDS(qp + tr_off[ni][0]));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)MOE_LDS(qp + tr_off[ni][1]));
+          f.b[ni] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      } else {
+        f.b[0] = *reinterpret_cast<const bf16x8*>(L + (sb0 >= kSlots ? sb0 - kSlots : sb0) * kQuarter + rb[0] * 128 + r);
+        f.b[1] = *reinterpret_cast<const bf16x8*>(L + (sb1 >= kSlots ? sb1 - kSlots : sb1) * kQuarter + rb[1] * 128 + r);
+      }
     };
     auto mfma = [&](const Frags& f) __attribute__((always_inline)) {
 #pragma unroll
@@ -339,7 +416,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
   {                                                                      \
     _Pragma("unroll") for (int i = 0; i < 32; ++i) {                     \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 \
-      if ((i & 7) < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); \
+      if ((i & 7) < (BT ? 8 : 6)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); \
       if ((i & 3) == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); \
     }                                                                    \
   }
@@ -692,7 +769,22 @@ hipError_t launch_ffn_tiled(const FfnParams& p, hipStream_t stream) {
   if (wgrad) grid = std::max<int64_t>(grid, 8);
   if (grid > 0) {
     const dim3 g((unsigned)grid), block(kThreads);
-    switch (p.act) {
+    if (p.bt) {  // weights stored [K][N] (backward input gradients)
+      switch (p.act) {
+        case kActBwd + 2:
+          hipLaunchKernelGGL((ffn_tiled_kernel<kActBwd + 2, true>), g, block, 0, stream, p, n_tiles_n);
+          break;
+        case kActBwd + 1:
+          hipLaunchKernelGGL((ffn_tiled_kernel<kActBwd + 1, true>), g, block, 0, stream, p, n_tiles_n);
+          break;
+        case kActBwd:
+          hipLaunchKernelGGL((ffn_tiled_kernel<kActBwd, true>), g, block, 0, stream, p, n_tiles_n);
+          break;
+        default:
+          hipLaunchKernelGGL((ffn_tiled_kernel<-1, true>), g, block, 0, stream, p, n_tiles_n);
+          break;
+      }
+    } else switch (p.act) {
       case kActWgrad:
         hipLaunchKernelGGL(ffn_tiled_kernel<kActWgrad>, g, block, 0, stream, p, n_tiles_n);
         break;

@@ -131,6 +131,12 @@ struct FfnParams {
   // is cut in two (tail split), split_cap tiles of 256 x 256; null = no split
   float* split;
   int split_cap;
+  // tiled path, act -1 or kActBwd + a: the weights are stored [K][N] per
+  // group (output columns contiguous), as W2 and W1 / W3 are for the
+  // backward's input gradients; kh > 0: rows k >= kh come from the second
+  // set (u_main / u_shared), kh rows per group each (kh % 64 == 0)
+  int bt;
+  int kh;
 };
 constexpr int kActBwd = 4;   // act codes 4, 5, 6: GELU, ReLU, SwiGLU backward
 constexpr int kActWgrad = 8;
