@@ -79,18 +79,32 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
   constexpr int kGroups = kCols / 8;          // 8-row groups of a weight slab
   constexpr int kSlot = NB * kGroups * 1024;  // one step of one wave's weights
   constexpr int kRed = WU ? 0 : NFRAG * 1024; // one wave's partial products
+  // output staging: a gated unit's output is the bf16 hidden layer, the
+  // others may be float32; whole-unit waves stage one 16-row fragment at a
+  // time in a tile of their own, split waves the unit's 32 rows once
+  constexpr int kOutB = GATED ? 2 : 4;
+  constexpr int kStage = WU ? 4 * 16 * kCols * kOutB : 32 * kCols * kOutB;
   static_assert(kGroups <= kMaxGroups, "weight slab wider than the descriptor");
-  __shared__ __attribute__((aligned(16))) char lds[4 * (kSlot + kRed)];
+  // (the gated 64-column split form is never launched: it would hold one block per CU)
+  static_assert(4 * (kSlot + kRed) + kStage <= 80 * 1024 || (GATED && NF == 4 && !WU),
+                "two blocks per CU");
+  __shared__ __attribute__((aligned(16))) char lds[4 * (kSlot + kRed) + kStage];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   char* const slot = lds + w * kSlot;
   float* const red = reinterpret_cast<float*>(lds + 4 * kSlot);  // [4][NFRAG][4][64]
+  char* const stage = lds + 4 * (kSlot + kRed) + (WU ? w * 16 * kCols * kOutB : 0);
   const int K = p.K, N = p.N;
   const int64_t wstride = (int64_t)N * K;
-  // a contiguous run of units per block (per wave with WU)
-  const int64_t workers = WU ? (int64_t)gridDim.x * 4 : gridDim.x;
-  const int64_t me = WU ? (int64_t)blockIdx.x * 4 + w : blockIdx.x;
+  // a contiguous run of units per block (per wave with WU), the runs in
+  // order of XCD first: the hardware hands block P to XCD P % 8, so block
+  // P takes run xcd_base + P / 8, and the neighbouring slabs of an expert,
+  // which re-read its operand rows, share one XCD's L2
+  const int xcd = blockIdx.x & 7, nblk = gridDim.x;
+  const int run = (nblk >> 3) * xcd + min(xcd, nblk & 7) + (blockIdx.x >> 3);
+  const int64_t workers = WU ? (int64_t)nblk * 4 : nblk;
+  const int64_t me = WU ? (int64_t)run * 4 + w : run;
   const int u_begin = (int)(me * n_units / workers);
   const int u_end = (int)((me + 1) * n_units / workers);
   // this wave's contiguous reduction range; every wave runs `per` steps
@@ -241,9 +255,9 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
             acc[mf][nf][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 __builtin_bit_cast(bf16x8, sa.a[v][mf]), br.b[v][nf][s], acc[mf][nf][s], 0, 0, 0);
   };
-  // one output element of the unit: bias, pre-activations, activation, store
-  auto emit = [&](const UnitDesc& d, int row, int col, float a, float up)
-      __attribute__((always_inline)) {
+  // one output value of the unit: bias, pre-activations, activation
+  auto value = [&](const UnitDesc& d, int row, int col, float a, float up)
+      __attribute__((always_inline)) -> float {
     const bool routed = d.g < p.G;
     const int gw = routed ? d.g : d.g - p.G;
     const float* bias = routed ? p.bias_main : p.bias_shared;
@@ -254,22 +268,42 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
       pre[0] = f32_to_bf16(a);
       if (GATED) pre[N] = f32_to_bf16(up);
     }
-    float out;
-    if (GATED) {
-      out = silu_f32(a) * up;
-    } else if (ACT == 0) {
-      out = gelu_f32(a);
-    } else if (ACT == 1) {
-      out = fmaxf(a, 0.f);
-    } else {
-      out = a;
-    }
-    const int64_t idx = (int64_t)(d.c_row0 + row) * N + col;
-    if (p.out_bf16) {
-      static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(out);
-    } else {
-      float* dst = static_cast<float*>(p.out) + idx;
-      *dst = p.accumulate ? *dst + out : out;
+    if (GATED) return silu_f32(a) * up;
+    if (ACT == 0) return gelu_f32(a);
+    if (ACT == 1) return fmaxf(a, 0.f);
+    return a;
+  };
+  // Outputs leave through LDS as 16-byte non-temporal stores, whole 64- or
+  // 128-byte row segments per 4 or 8 lanes: the unit's output rows are
+  // written while the weight stream runs, and scattered 2- or 4-byte stores
+  // of the same bytes cost that stream about a sixth of its time (the next
+  // kernel reads them once, so they need not stay in the caches either).
+  // put(): one value into the staging tile (tile row r, unit column c)
+  auto put = [&](int r, int c, float v) __attribute__((always_inline)) {
+    if (GATED || p.out_bf16)
+      reinterpret_cast<uint16_t*>(stage)[r * kCols + c] = f32_to_bf16(v);
+    else
+      reinterpret_cast<float*>(stage)[r * kCols + c] = v;
+  };
+  // drain(): tile rows [0, nrows) to output rows row0 + r (r < rows), by
+  // thread i of n; every 16-byte chunk lies wholly inside or outside N
+  // columns since N is a multiple of 8
+  auto drain = [&](const UnitDesc& d, int u, int row0, int nrows, int i, int n)
+      __attribute__((always_inline)) {
+    const int slab = u - d.g * n_slabs;
+    const bool b16 = GATED || p.out_bf16;
+    const int per_row = kCols * (b16 ? 2 : 4) / 16;
+    for (int c = i; c < nrows * per_row; c += n) {
+      const int r = c / per_row, q = c - r * per_row;
+      const int col = slab * kCols + q * (b16 ? 8 : 4);
+      if (row0 + r >= d.rows || col >= N) continue;
+      // 16-byte aligned: the output is, and N is a multiple of 8
+      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<char*>(p.out) +
+                                            ((int64_t)(d.c_row0 + row0 + r) * N + col) * (b16 ? 2 : 4));
+      u32x4 v = *reinterpret_cast<const u32x4*>(stage + c * 16);
+      if (!b16 && p.accumulate)
+        v = __builtin_bit_cast(u32x4, __builtin_bit_cast(f32x4, v) + __builtin_bit_cast(f32x4, *dst));
+      __builtin_nontemporal_store(v, dst);
     }
   };
   // a group over the limit: NaN in every output row of the group (within
@@ -292,18 +326,26 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
   auto finish = [&](const UnitDesc& d, int u) __attribute__((always_inline)) {
     if constexpr (WU) {
       const int slab = u - d.g * n_slabs;
+      if (d.over) {
+        poison(d, u, lane, 64);
+        return;
+      }
 #pragma unroll
-      for (int mf = 0; mf < 2; ++mf)
+      for (int mf = 0; mf < 2; ++mf) {
+        if (mf * 16 >= d.rows) break;
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int row = mf * 16 + (lane >> 4) * 4 + i;
-            const int col = slab * kCols + nf * 16 + (lane & 15);
-            if (row < d.rows && col < N && !d.over)
-              emit(d, row, col, acc[mf][nf][0][i], GATED ? acc[mf][nf][NB - 1][i] : 0.f);
+            const int r = (lane >> 4) * 4 + i, row = mf * 16 + r;
+            const int c = nf * 16 + (lane & 15), col = slab * kCols + c;
+            if (row < d.rows && col < N)
+              put(r, c, value(d, row, col, acc[mf][nf][0][i], GATED ? acc[mf][nf][NB - 1][i] : 0.f));
           }
-      if (d.over) poison(d, u, lane, 64);
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's tile written
+        drain(d, u, mf * 16, 16, lane, 64);
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // and read, before it is reused
+      }
       return;
     }
     auto R = [&](int wv, int f, int i, int l) -> float& {
@@ -323,17 +365,22 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
       const int mf = o / (NF * 256), rem = o - mf * NF * 256;
       const int nf = rem >> 8, i = (rem >> 6) & 3, l = rem & 63;
       const int row = mf * 16 + (l >> 4) * 4 + i;
-      const int col = slab * kCols + nf * 16 + (l & 15);
+      const int c = nf * 16 + (l & 15), col = slab * kCols + c;
       if (row >= d.rows || col >= N || d.over) continue;
       const int f0 = (mf * NF + nf) * NB;
       const float a = ((R(0, f0, i, l) + R(1, f0, i, l)) + R(2, f0, i, l)) + R(3, f0, i, l);
       float up = 0.f;
       if (GATED)
         up = ((R(0, f0 + 1, i, l) + R(1, f0 + 1, i, l)) + R(2, f0 + 1, i, l)) + R(3, f0 + 1, i, l);
-      emit(d, row, col, a, up);
+      put(row, c, value(d, row, col, a, up));
     }
-    if (d.over) poison(d, u, threadIdx.x, kThreads);
-    lds_barrier();  // the partial products are reused by the next unit
+    if (d.over) {
+      poison(d, u, threadIdx.x, kThreads);
+    } else {
+      lds_barrier();  // the staged tile is complete
+      drain(d, u, 0, 32, threadIdx.x, kThreads);
+    }
+    lds_barrier();  // the partial products and the tile are reused by the next unit
   };
 
   // One continuous pipeline over the block's units.  Step i: wait for its
