@@ -542,7 +542,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
             return o;
           },
           [&](int row, int colc, const u32x4& ch) __attribute__((always_inline)) {
-            *reinterpret_cast<u32x4*>(out + (crow0 + row) * N + colc) = ch;
+            __builtin_nontemporal_store(ch, reinterpret_cast<u32x4*>(out + (crow0 + row) * N + colc));
           });
       if (p.pre) {
         // pre-activations for the backward: u (+ bias), then v when gated
@@ -606,7 +606,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
              f32x4* dst = reinterpret_cast<f32x4*>(out + (crow0 + row) * N + colc);
              f32x4 val = __builtin_bit_cast(f32x4, ch);
              if (p.accumulate) val += *dst;
-             *dst = val;
+             if (WGRAD) *dst = val; else __builtin_nontemporal_store(val, dst);
            });
     }
   }
