@@ -144,15 +144,15 @@ DiagWs carve_diag(Carve& cv, const Cfg& c) {
   w.partial_i = static_cast<int32_t*>(cv.take((size_t)diag_blocks(c.T) * 2 * sizeof(int32_t)));
   return w;
 }
-// Tile schedule of the tiled GEMM, plus the tail-split partials of its float32
-// (N = d) launches.
+// Tile schedule of the tiled GEMM, plus the tail-split partials of its
+// launches (two 256 x 256 float32 blocks per split tile).
 FfnWs carve_ffn(Carve& cv, int64_t rows_bound, int64_t groups, int64_t S, int64_t T, int64_t d) {
   FfnWs w;
   const int64_t ent = ffn_max_entries(rows_bound, (int)groups, (int)S, (int)T);
   w.entries = static_cast<TileEntry*>(cv.take((size_t)ent * sizeof(TileEntry)));
   w.n_entries = static_cast<int32_t*>(cv.take(4));
   w.split_cap = (int)ffn_split_cap(ent, d);
-  w.split = static_cast<float*>(cv.take((size_t)w.split_cap * 256 * 256 * 4));
+  w.split = static_cast<float*>(cv.take((size_t)w.split_cap * 2 * 256 * 256 * 4));
   return w;
 }
 
@@ -321,7 +321,7 @@ BwdWs carve_backward(Carve& cv, const Cfg& c, bool noise) {
   w.fw.entries = static_cast<TileEntry*>(cv.take((size_t)ent * sizeof(TileEntry)));
   w.fw.n_entries = static_cast<int32_t*>(cv.take(4));
   w.fw.split_cap = (int)ffn_split_cap(ffn_max_entries(c.R, (int)c.E, (int)c.S, (int)c.T), c.d);
-  w.fw.split = static_cast<float*>(cv.take((size_t)w.fw.split_cap * 256 * 256 * 4));
+  w.fw.split = static_cast<float*>(cv.take((size_t)w.fw.split_cap * 2 * 256 * 256 * 4));
   w.xcd_bounds = static_cast<int32_t*>(cv.take(16 * 4));
   return w;
 }

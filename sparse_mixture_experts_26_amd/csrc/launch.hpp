@@ -127,8 +127,10 @@ struct FfnParams {
   const GroupDesc* gdesc;    // [G + S]
   void* out_shared;
   int32_t* xcd_bounds;       // [9] scratch: each XCD's tile range
-  // act = -1 on the tiled path: float32 partials of the tiles whose reduction
-  // is cut in two (tail split), split_cap tiles of 256 x 256; null = no split
+  // tiled path, act -1 and 2: float32 partials of the tiles whose reduction
+  // is cut in two (tail split), 2 * split_cap blocks of 256 x 256 (act -1
+  // uses one per split tile, the gated up projection, whose epilogue needs
+  // the whole sum, two); null = no split
   float* split;
   int split_cap;
   // tiled path, act -1 or kActBwd + a: the weights are stored [K][N] per
@@ -141,8 +143,8 @@ struct FfnParams {
 constexpr int kActBwd = 4;   // act codes 4, 5, 6: GELU, ReLU, SwiGLU backward
 constexpr int kActWgrad = 8;
 int64_t ffn_max_entries(int64_t rows_bound, int G, int S, int T);
-// tiles the tail-split scratch of a float32 tiled launch with N output
-// columns holds (each 256 x 256 floats)
+// tiles of a tiled launch with N output columns that its tail split may cut
+// (the scratch holds twice as many blocks of 256 x 256 floats)
 int64_t ffn_split_cap(int64_t max_entries, int64_t N);
 hipError_t launch_ffn(const FfnParams& p, hipStream_t stream);
 

@@ -1,12 +1,15 @@
-"""Tail split of the tiled expert GEMM (float32 down projection).
+"""Tail split of the tiled expert GEMM (float32 down projection and gated up
+projection).
 
 When the last round of 256 x 256 output tiles would leave at least half the
 persistent blocks idle, those tiles are cut into two halves of their reduction
-and the second halves' partials are added afterwards.  These cases pick group
-sizes and row bounds that make the split happen, both after whole rounds of
-tiles (w >= 1) and with fewer tiles than half the launch (w = 0), and compare
-the staged expert FFN with the oracle's expert FFN per group, with biases and
-with accumulation into the output.
+and finished afterwards: the down projection's second halves' partials are
+added to the output; the gated up projection's two halves both write partials
+and a fixup applies silu(gate) * up.  These cases pick group sizes and row
+bounds that make the split happen, both after whole rounds of tiles (w >= 1)
+and with fewer tiles than half the launch (w = 0), and compare the staged
+expert FFN (and the up projection's hidden rows) with the oracle's per group,
+with biases and with accumulation into the output.
 """
 import numpy as np
 import pytest
@@ -24,18 +27,23 @@ pytestmark = pytest.mark.gpu
 BM = BR = 256  # output tile of the tiled kernel
 
 
-def _split_expected(offsets, rows_bound, n_groups, N, K, cus):
-    """Whether the launch splits, from the documented plan (host-side mirror)."""
+def _split_expected(offsets, rows_bound, n_groups, N, K, cus, d=None, gated=False):
+    """Whether the launch splits, from the documented plan (host-side mirror).
+    A gated launch covers 128 output columns per tile; the split scratch is
+    sized by the model width d (its tile count with 256-column tiles)."""
     sizes = np.diff(offsets)
     entries = int(sum((s + BM - 1) // BM for s in sizes))
-    n_tiles_n = (N + BR - 1) // BR
+    cols = BR // 2 if gated else BR
+    n_tiles_n = (N + cols - 1) // cols
     max_entries = (rows_bound + BM - 1) // BM + n_groups
     P = min(cus, max_entries * n_tiles_n)
     tiles = entries * n_tiles_n
     w, r = divmod(tiles, P)
-    cap = min(128, (max_entries * n_tiles_n + 1) // 2)
+    width = N if d is None else d
+    cap = min(128, (max_entries * ((width + BR - 1) // BR) + 1) // 2)
     nk = (K + 63) // 64
-    return r > 0 and 2 * r <= P and r <= cap and nk >= 2, w, r, P
+    min_nk = 48 if gated else 2  # the gated form splits only deep reductions
+    return r > 0 and 2 * r <= P and r <= cap and nk >= min_nk, w, r, P
 
 
 @pytest.mark.parametrize("sizes,rows_bound,d,h", [
@@ -84,3 +92,50 @@ def test_tail_split_matches_oracle(sizes, rows_bound, d, h):
     # the second call adds the same terms onto the first result (in another
     # float32 order for split tiles)
     assert rel_l2(y2, 2 * y1) <= 1e-6
+
+
+@pytest.mark.parametrize("sizes,rows_bound,d,h", [
+    ((4200, 300), 4500, 3072, 2048),  # 19 x 16 tiles on 256 blocks: one whole round, 48 split
+    ((300, 200), 4096, 3072, 384),    # 3 x 3 tiles on a 54-block launch: every tile split
+    # ragged: 200 hidden units (the second column tile is partial) and a
+    # reduction of 3080 (the second half ends in a partial stage)
+    ((700, 50, 333), 4096, 3080, 200),
+])
+def test_gated_up_tail_split_matches_oracle(sizes, rows_bound, d, h):
+    """moe_expert_up (SwiGLU, with b1) at sizes whose launch splits its tail
+    tiles: every hidden row against the oracle's silu(x W1^T + b1) * (x W3^T)."""
+    require_gpu()
+    from tests.gpu_util import worst_row_error
+    G = len(sizes)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows = int(offsets[-1])
+    T = rows_bound
+    cfg = LayerConfig(name="tail_split_up", cfg_id=72, T=T, d=d, E=G, k=1, h=h, act="swiglu",
+                      capacity_factor=0.0, dtype="bf16", ffn_bias=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    split, w, r, P = _split_expected(offsets, rows_bound, G, h, d, cus, d=d, gated=True)
+    banner(f"gated up tail split sizes={sizes} rows_bound={rows_bound} d={d} h={h} w={w} r={r} "
+           f"P={P}")
+    assert split, "case no longer exercises the split"
+    inp = make_inputs(cfg, seed=4)
+    row_token = ((np.arange(rows, dtype=np.int64) * 7919) % T).astype(np.int32)
+    dev = {k: to_torch(v, "cuda") for k, v in inp.tensors().items()}
+    c = config_of(cfg)
+    ws = torch.empty(M.moe_workspace_bytes(c), dtype=torch.uint8, device="cuda")
+    off_d = torch.from_numpy(offsets).cuda()
+    rt_d = torch.from_numpy(row_token).cuda()
+    hidden = torch.full((rows_bound, h), float("nan"), dtype=torch.bfloat16, device="cuda")
+    L.moe_expert_up(c, G, dev["x"], rt_d, off_d, rows_bound, rows_bound, dev["w1"], dev["w3"],
+                    dev["b1"], hidden, ws)
+    torch.cuda.synchronize()
+    got = host(hidden)[:rows].astype(np.float64)
+    want = np.zeros((rows, h))
+    for g in range(G):
+        sl = slice(int(offsets[g]), int(offsets[g + 1]))
+        xr = O.to_f64(inp.x[row_token[sl]])
+        a = xr @ O.to_f64(inp.w1[g]).T + O.to_f64(inp.b1[g])
+        u = xr @ O.to_f64(inp.w3[g]).T
+        want[sl] = O.activation("swiglu", a, u)
+    assert np.all(np.isfinite(got))
+    assert rel_l2(got, want) <= 2e-2
+    assert worst_row_error(got, want) <= 5e-2
