@@ -387,7 +387,7 @@ moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w,
  * part out of the scratch, so they raise the largest layer that fits.
  * Returns MOE_ERR_WORKSPACE_TOO_SMALL, before anything is enqueued, when the
  * layer needs more than the scratch holds (a decode batch of the Mixtral
- * shape needs about 21 MiB, the Switch-shaped layer about 70 MiB; prefill
+ * shape needs about 39 MiB, the Switch-shaped layer about 102 MiB; prefill
  * shapes do not fit).  All calls on one device share its scratch: calls that
  * overlap on one device (on different streams, or from several host threads
  * without ordering) race and give undefined results.  Nothing in the scratch
