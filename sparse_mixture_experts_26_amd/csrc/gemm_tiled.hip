@@ -625,14 +625,15 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
              *reinterpret_cast<u32x4*>(part + row * BR + (colc - n_out0)) = ch;
            });
     } else {
-      // float32 rows (down projection, input gradients) or weight gradients
+      // float32 rows (down projection, input gradients) or weight gradients,
+      // all written once for a later launch (or the caller): non-temporal
       float* out = static_cast<float*>(WGRAD && !routed ? p.out_shared : p.out);
       emit(F32{}, [&](int mi, int nj, int v) __attribute__((always_inline)) { return acc[mi][nj][v] + bcol[nj]; },
            [&](int row, int colc, const u32x4& ch) __attribute__((always_inline)) {
              f32x4* dst = reinterpret_cast<f32x4*>(out + (crow0 + row) * N + colc);
              f32x4 val = __builtin_bit_cast(f32x4, ch);
              if (p.accumulate) val += *dst;
-             if (WGRAD) *dst = val; else __builtin_nontemporal_store(val, dst);
+             __builtin_nontemporal_store(val, dst);
            });
     }
   }
