@@ -142,27 +142,31 @@ __device__ __forceinline__ void tile_coords(int t, int n_entries, int n_tiles_n,
 
 // Tail split.  With tiles = w P + r on P persistent blocks, the last round
 // holds only r tiles and leaves P - r blocks idle.  When 2r <= P each of those
-// tiles is cut into two halves of its reduction that run on different blocks,
-// so the launch takes w + 1/2 tile times instead of w + 1.  Tiles [0, full)
-// run whole; half-unit u (0 <= u < halves) is tile full + u/2, half u%2.
-// Float32 outputs: the first half writes the output, the second float32
-// partials that split_fixup_kernel adds.  The gated up projection (whose
-// epilogue needs the whole sum): both halves write float32 partials and
-// split_act_fixup_kernel adds them and applies bias and activation.
+// tiles is cut into parts (2, or 3 when 3r <= P) of its reduction that run on
+// different blocks, so the launch takes w + 1/2 (1/3) tile times instead of
+// w + 1.  Tiles [0, full) run whole; unit u (0 <= u < units) is part u % parts
+// of tile full + u / parts, part q covering stages [q nk / parts, (q+1) nk /
+// parts).  Float32 outputs: part 0 writes the output, the others float32
+// partials that split_fixup_kernel adds in part order.  The gated up
+// projection (whose epilogue needs the whole sum) uses two parts, both writing
+// float32 partials, which split_act_fixup_kernel adds before bias and
+// activation.  The scratch holds two partial blocks per split tile.
 // The gated form writes and re-reads two float32 partial blocks per split
 // tile, four times the bytes of its bf16 output, so it splits only tiles of
 // at least 48 reduction stages, where half a tile saves more than that
 // traffic costs (a 2048-deep reduction measured 0.6% slower split, a
 // 4096-deep one 0.8% faster).
 struct SplitPlan {
-  int full, halves;
+  int full, units, parts;
 };
 constexpr int kGatedSplitStages = 48;
 __device__ __forceinline__ SplitPlan split_plan(int tiles, int P, int nk, int cap, bool gated) {
   const int w = tiles / P, r = tiles - w * P;
-  if (r > 0 && 2 * r <= P && r <= cap && nk >= (gated ? kGatedSplitStages : 2))
-    return {w * P, 2 * r};
-  return {tiles, 0};
+  if (r > 0 && 2 * r <= P && r <= cap && nk >= (gated ? kGatedSplitStages : 2)) {
+    const int parts = (!gated && 3 * r <= P && nk >= 3) ? 3 : 2;
+    return {w * P, parts * r, parts};
+  }
+  return {tiles, 0, 1};
 }
 
 // ACT: moe_act_t for the up projection (2 = gated SwiGLU), -1 for none
@@ -176,7 +180,7 @@ __device__ __forceinline__ SplitPlan split_plan(int tiles, int P, int nk, int ca
 // an equal share of real tiles and neighbouring tiles share an L2.  Float32
 // outputs (act -1) and the gated up projection may split the last round's
 // tiles (split_plan): each XCD then also owns a contiguous range of the
-// half-units, run after its whole tiles, and a fixup kernel finishes them.
+// split units, run after its whole tiles, and a fixup kernel finishes them.
 //
 // BT: the weights are stored [K][N] per group (output columns contiguous:
 // w_main / w_shared of group g hold row k at k*N; with p.kh > 0 rows k >= kh
@@ -210,12 +214,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
   constexpr bool SPLITS = ACT == -1 || ACT == 2;
   const SplitPlan plan = SPLITS && p.split
                              ? split_plan(tiles, gridDim.x, (p.K + BK - 1) / BK, p.split_cap, GATED)
-                             : SplitPlan{tiles, 0};
+                             : SplitPlan{tiles, 0, 1};
   const int per = (plan.full + 7) >> 3;
   const int t_begin = WGRAD ? p.xcd_bounds[xcd] : xcd * per;
   const int t_end = WGRAD ? p.xcd_bounds[xcd + 1] : min(plan.full, (xcd + 1) * per);
-  const int per_h = (plan.halves + 7) >> 3;
-  const int h_begin = xcd * per_h, h_end = min(plan.halves, (xcd + 1) * per_h);
+  const int per_h = (plan.units + 7) >> 3;
+  const int h_begin = xcd * per_h, h_end = min(plan.units, (xcd + 1) * per_h);
   const int n_whole = t_begin + q < t_end ? (t_end - t_begin - q + nq - 1) / nq : 0;
   const int N = p.N;
   constexpr uint32_t kOOB = 0x80000000u;
@@ -254,15 +258,15 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
   }
 
   for (int it = 0;; ++it) {
-    // this block's whole tiles, then its half-units
-    int t, half = -1;  // -1: whole tile; 0 / 1: first / second half of its reduction
+    // this block's whole tiles, then its split units
+    int t, half = -1;  // -1: whole tile; else the part of its reduction
     if (it < n_whole) {
       t = t_begin + q + it * nq;
     } else {
       const int u = h_begin + q + (it - n_whole) * nq;
       if (u >= h_end) break;
-      t = plan.full + (u >> 1);
-      half = u & 1;
+      t = plan.full + u / plan.parts;
+      half = u - (t - plan.full) * plan.parts;
     }
     int e_idx, n_idx;
     tile_coords(t, n_entries, n_tiles_n, e_idx, n_idx);
@@ -294,9 +298,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     }
     const int nk = (K + BK - 1) / BK;
     // stages [kb, kb + nks) of the reduction; chunks at or past k_end read zeros
-    const int kb = half == 1 ? nk / 2 : 0;
-    const int nks = half < 0 ? nk : (half == 0 ? nk / 2 : nk - nk / 2);
-    const int k_end = half == 0 ? (nk / 2) * BK : K;
+    const int kb = half < 0 ? 0 : half * nk / plan.parts;
+    const int ke = half < 0 ? nk : (half + 1) * nk / plan.parts;
+    const int nks = ke - kb;
+    const int k_end = ke == nk ? K : ke * BK;
     const int n_out0 = n_idx * (GATED ? BR / 2 : BR);
 
     // ---- direct-to-LDS loads.  A quarter is 16 loads of 1 KiB (8 rows x 128
@@ -616,10 +621,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
                *reinterpret_cast<u32x2*>(out + r * ld + N + colc) = o;
              }
            });
-    } else if (SPLITS && half == 1) {
-      // second half of a split tile: float32 partials (no bias), tile-local
+    } else if (SPLITS && half >= 1) {
+      // a later part of a split tile: float32 partials (no bias), tile-local
       // rows of BR values
-      float* part = p.split + (int64_t)(t - plan.full) * (BM * BR);
+      float* part = p.split + ((int64_t)(t - plan.full) * 2 + half - 1) * (BM * BR);
       emit(F32{}, [&](int mi, int nj, int v) __attribute__((always_inline)) { return acc[mi][nj][v]; },
            [&](int row, int colc, const u32x4& ch) __attribute__((always_inline)) {
              *reinterpret_cast<u32x4*>(part + row * BR + (colc - n_out0)) = ch;
@@ -709,27 +714,28 @@ __global__ __launch_bounds__(256) void build_wgrad_tiles_kernel(int groups, int 
   if (tiles == 0 && tid >= 1 && tid < 8) xcd_bounds[tid] = 0;
 }
 
-// Adds the second-half partials of the split tiles into the float32 output
-// (same plan as the GEMM with P of its blocks).  kFixParts blocks per split
-// tile, 16 rows each; every thread issues its 4 chunks' loads (partial and
-// output) before adding, so a block waits for memory once.  Runs after the
-// GEMM on the same stream.
+// Adds the later parts' partials of the split tiles into the float32 output,
+// in part order (same plan as the GEMM with P of its blocks).  kFixParts
+// blocks per split tile, 16 rows each; every thread issues its 4 chunks'
+// loads (partials and output) before adding, so a block waits for memory
+// once.  Runs after the GEMM on the same stream.
 constexpr int kFixParts = 16;
 
 __global__ __launch_bounds__(256) void split_fixup_kernel(FfnParams p, int n_tiles_n, int P) {
   const int n_entries = *p.n_entries;
   const SplitPlan plan = split_plan(n_entries * n_tiles_n, P, (p.K + BK - 1) / BK, p.split_cap, false);
   const int j = blockIdx.x / kFixParts, r0 = (blockIdx.x % kFixParts) * (BM / kFixParts);
-  if (2 * j >= plan.halves) return;
+  if (j * plan.parts >= plan.units) return;
   int e_idx, n_idx;
   tile_coords(plan.full + j, n_entries, n_tiles_n, e_idx, n_idx);
   const TileEntry te = p.entries[e_idx];
   const int n_out0 = n_idx * BR;
   float* out = static_cast<float*>(p.out);
-  const float* part = p.split + (int64_t)j * (BM * BR);
+  const float* part = p.split + (int64_t)(2 * j) * (BM * BR);
+  const bool third = plan.parts == 3;
   constexpr int kChunks = BR / 4;  // float4 chunks per tile row
   constexpr int kPer = (BM / kFixParts) * kChunks / 256;
-  f32x4 a[kPer], b[kPer];
+  f32x4 a[kPer], c3[kPer], b[kPer];
   f32x4* dst[kPer];
   bool ok[kPer];
 #pragma unroll
@@ -740,12 +746,13 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(FfnParams p, int n_til
     dst[u] = reinterpret_cast<f32x4*>(out + (int64_t)(te.c_row0 + row) * p.N + n_out0 + c);
     if (ok[u]) {
       a[u] = *reinterpret_cast<const f32x4*>(part + row * BR + c);
+      if (third) c3[u] = *reinterpret_cast<const f32x4*>(part + BM * BR + row * BR + c);
       b[u] = *dst[u];
     }
   }
 #pragma unroll
   for (int u = 0; u < kPer; ++u)
-    if (ok[u]) *dst[u] = b[u] + a[u];
+    if (ok[u]) *dst[u] = third ? (b[u] + a[u]) + c3[u] : b[u] + a[u];
 }
 
 // The split tiles of the gated up projection: out = silu(gate) * up in bf16
@@ -759,7 +766,7 @@ __global__ __launch_bounds__(256) void split_act_fixup_kernel(FfnParams p, int n
   const int n_entries = *p.n_entries;
   const SplitPlan plan = split_plan(n_entries * n_tiles_n, P, (p.K + BK - 1) / BK, p.split_cap, true);
   const int j = blockIdx.x / kFixParts, r0 = (blockIdx.x % kFixParts) * (BM / kFixParts);
-  if (2 * j >= plan.halves) return;
+  if (j * plan.parts >= plan.units) return;
   int e_idx, n_idx;
   tile_coords(plan.full + j, n_entries, n_tiles_n, e_idx, n_idx);
   const TileEntry te = p.entries[e_idx];

@@ -2,10 +2,10 @@
 projection).
 
 When the last round of 256 x 256 output tiles would leave at least half the
-persistent blocks idle, those tiles are cut into two halves of their reduction
-and finished afterwards: the down projection's second halves' partials are
-added to the output; the gated up projection's two halves both write partials
-and a fixup applies silu(gate) * up.  These cases pick group sizes and row
+persistent blocks idle, those tiles are cut into parts of their reduction and
+finished afterwards: the down projection's later parts' partials (two or
+three parts) are added to the output; the gated up projection's two halves
+both write partials and a fixup applies silu(gate) * up.  These cases pick group sizes and row
 bounds that make the split happen, both after whole rounds of tiles (w >= 1)
 and with fewer tiles than half the launch (w = 0), and compare the staged
 expert FFN (and the up projection's hidden rows) with the oracle's per group,
@@ -43,12 +43,15 @@ def _split_expected(offsets, rows_bound, n_groups, N, K, cus, d=None, gated=Fals
     cap = min(128, (max_entries * ((width + BR - 1) // BR) + 1) // 2)
     nk = (K + 63) // 64
     min_nk = 48 if gated else 2  # the gated form splits only deep reductions
-    return r > 0 and 2 * r <= P and r <= cap and nk >= min_nk, w, r, P
+    split = r > 0 and 2 * r <= P and r <= cap and nk >= min_nk
+    parts = (3 if (not gated and 3 * r <= P and nk >= 3) else 2) if split else 1
+    return split, w, r, P, parts
 
 
 @pytest.mark.parametrize("sizes,rows_bound,d,h", [
-    ((4200, 300), 4500, 4096, 256),   # 19 x 16 tiles on 256 blocks: one whole round, 48 split
-    ((300, 200), 4096, 512, 192),     # 3 x 2 tiles on a 36-block launch: every tile split
+    ((4200, 300), 4500, 4096, 256),   # 19 x 16 tiles on 256 blocks: one whole round, 48 in 3 parts
+    ((5000, 400), 5400, 4096, 256),   # 22 x 16 tiles: one whole round, 96 in 2 parts
+    ((300, 200), 4096, 512, 192),     # 3 x 2 tiles on a 36-block launch: every tile in 3 parts
     # ragged everywhere: 640 columns (2.5 column tiles) and a reduction of 200
     # (the second half ends in a partial stage)
     ((700, 50, 333), 4096, 640, 200),
@@ -63,8 +66,9 @@ def test_tail_split_matches_oracle(sizes, rows_bound, d, h):
     cfg = LayerConfig(name="tail_split", cfg_id=71, T=T, d=d, E=G, k=1, h=h, act="swiglu",
                       capacity_factor=0.0, dtype="bf16", ffn_bias=True)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    split, w, r, P = _split_expected(offsets, rows_bound, G, d, h, cus)
-    banner(f"tail split sizes={sizes} rows_bound={rows_bound} d={d} h={h} w={w} r={r} P={P}")
+    split, w, r, P, parts = _split_expected(offsets, rows_bound, G, d, h, cus)
+    banner(f"tail split sizes={sizes} rows_bound={rows_bound} d={d} h={h} w={w} r={r} P={P} "
+           f"parts={parts}")
     assert split, "case no longer exercises the split"
     inp = make_inputs(cfg, seed=3)
     # rows gather tokens in a scrambled order
@@ -113,7 +117,7 @@ def test_gated_up_tail_split_matches_oracle(sizes, rows_bound, d, h):
     cfg = LayerConfig(name="tail_split_up", cfg_id=72, T=T, d=d, E=G, k=1, h=h, act="swiglu",
                       capacity_factor=0.0, dtype="bf16", ffn_bias=True)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    split, w, r, P = _split_expected(offsets, rows_bound, G, h, d, cus, d=d, gated=True)
+    split, w, r, P, _ = _split_expected(offsets, rows_bound, G, h, d, cus, d=d, gated=True)
     banner(f"gated up tail split sizes={sizes} rows_bound={rows_bound} d={d} h={h} w={w} r={r} "
            f"P={P}")
     assert split, "case no longer exercises the split"
