@@ -195,6 +195,110 @@ def test_backward_full_size(name):
         assert abs(db.sum()) <= 1e-4 * np.abs(db).sum() + 1e-6
 
 
+def _rel_l2_gpu(got, want) -> float:
+    """Relative L2 of a device float32 tensor against a float64 host array."""
+    w = torch.from_numpy(np.asarray(want, np.float64)).to(got.device)
+    g = got.to(torch.float64)
+    return float(torch.linalg.vector_norm(g - w) / max(float(torch.linalg.vector_norm(w)), 1e-300))
+
+
+@pytest.mark.parametrize("name", FULL_TC)
+def test_backward_full_size_sparse_upstream(name):
+    """Every gradient at full size, exactly: the upstream gradient is zero
+    except on a sample S of tokens and the loss weights are zero, so only S
+    carries gradient (B1, B2).  The oracle then needs only S's tokens: their
+    expert rows (one-row FFN backwards summed per expert, which is how the
+    full backward sums an expert's rows), their gates and logit gradients and
+    the router's share.  Checked: dx of S per token (every other row exactly
+    0); dW_g, db_g, dW_noise whole; every expert's weight gradients whole
+    (experts S does not reach exactly 0); the shared experts' whole."""
+    require_gpu()
+    from workloads import FULL
+    cfg = FULL[name]
+    T, E, k, d = cfg.T, cfg.E, cfg.k, cfg.d
+    inp = make_inputs(cfg, 0)
+    H = O.router_logits(inp.x, inp.w_g, inp.b_g, inp.w_noise, inp.eps)
+    idx = O.select_top_k(H, k)
+    g = O.selected_gates(H, idx)
+    C = O.capacity(cfg.capacity_factor, T, k, E)
+    disp = (O.dispatch_reroute(idx, H, E, min(C, T)) if cfg.overflow == "reroute"
+            else O.dispatch(idx, E, C))
+    offsets, dest = disp["offsets"], disp["dest"]
+    rng = np.random.default_rng(cfg.cfg_id + 17)
+    lost = np.flatnonzero((dest < 0).any(axis=1))
+    pick = [0, T - 1] + ([int(lost[0])] if lost.size else []) + list(rng.choice(T, 9, replace=False))
+    S = np.unique(np.asarray(pick, np.int64))
+    banner(f"backward full {name}: sparse upstream gradient on {S.size} tokens")
+    dy = np.zeros((T, d), np.float32)
+    dy[S] = make_upstream_grad(cfg, 0)[S]
+
+    dev = upload(inp)
+    layer = MoeLayer(cfg, weights_of(dev))
+    layer.forward_train(dev["x"], dev.get("eps"), torch.from_numpy(H).cuda())
+    got = layer.backward(dev["x"], torch.from_numpy(dy).cuda(), dev.get("eps"), 0.0, 0.0)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(layer.out["offsets"]), offsets)
+    tol = y_tol(cfg)
+
+    # the oracle on S: expert rows grouped by expert, shared experts, gates
+    dx = np.zeros((S.size, d))
+    dg = np.zeros((S.size, k))
+    rows_of = {}
+    for i, t in enumerate(S):
+        for sl in range(k):
+            r = int(dest[t, sl])
+            if r >= 0:
+                e = int(np.searchsorted(offsets, r, side="right") - 1)
+                rows_of.setdefault(e, []).append((i, int(t), sl))
+    for e in range(E):
+        names = ["dw1", "dw2"] + (["dw3"] if cfg.act == "swiglu" else [])
+        if e not in rows_of:
+            for n in names:
+                assert int(torch.count_nonzero(got[n][e])) == 0, (n, e)
+            continue
+        ii = np.array([a for a, _, _ in rows_of[e]])
+        tt = np.array([b for _, b, _ in rows_of[e]])
+        ss = np.array([c for _, _, c in rows_of[e]])
+        res = O.expert_ffn_backward(inp.x[tt], inp.w1[e], inp.w2[e], cfg.act,
+                                    g[tt, ss][:, None] * dy[tt].astype(np.float64),
+                                    None if inp.w3 is None else inp.w3[e],
+                                    None if inp.b1 is None else inp.b1[e],
+                                    None if inp.b2 is None else inp.b2[e])
+        np.add.at(dx, ii, res["dx"])
+        dg[ii, ss] = (dy[tt].astype(np.float64) * res["y"]).sum(axis=1)
+        for n in names:
+            assert _rel_l2_gpu(got[n][e], res[n]) <= tol, (n, e)
+        if "db1" in got:
+            assert rel_l2(host(got["db1"][e]), res["db1"]) <= tol, ("db1", e)
+            assert rel_l2(host(got["db2"][e]), res["db2"]) <= tol, ("db2", e)
+    for sh in range(cfg.n_shared):
+        res = O.expert_ffn_backward(inp.x[S], inp.ws1[sh], inp.ws2[sh], cfg.act,
+                                    dy[S].astype(np.float64),
+                                    None if inp.ws3 is None else inp.ws3[sh])
+        dx += res["dx"]
+        assert _rel_l2_gpu(got["dws1"][sh], res["dw1"]) <= tol, ("dws1", sh)
+        assert _rel_l2_gpu(got["dws2"][sh], res["dw2"]) <= tol, ("dws2", sh)
+        if cfg.act == "swiglu":
+            assert _rel_l2_gpu(got["dws3"][sh], res["dw3"]) <= tol, ("dws3", sh)
+    dH = np.zeros((S.size, E))
+    np.put_along_axis(dH, idx[S], O.gate_softmax_backward(g[S], dg), axis=1)
+    rt = O.router_backward(inp.x[S], inp.w_g, dH, inp.w_noise,
+                           None if inp.eps is None else inp.eps[S])
+    dx += rt["dx"]
+
+    gdx = got["dx"]
+    for i, t in enumerate(S):
+        assert rel_l2(host(gdx[t]), dx[i]) <= tol, ("dx", int(t))
+    rest = torch.ones(T, dtype=torch.bool, device=gdx.device)
+    rest[torch.from_numpy(S).to(gdx.device)] = False
+    assert int(torch.count_nonzero(gdx[rest])) == 0
+    assert rel_l2(host(got["dw_g"]), rt["dw_g"]) <= tol
+    if "db_g" in got:
+        assert rel_l2(host(got["db_g"]), rt["db_g"]) <= tol
+    if rt["dw_noise"] is not None:
+        assert rel_l2(host(got["dw_noise"]), rt["dw_noise"]) <= tol
+
+
 def test_backward_full_size_expert_choice():
     """The full-size expert-choice layer (Mixtral prefill shape, capacity
     factor 1): expert weight-gradient rows and columns of the busiest and of
