@@ -320,7 +320,7 @@ BwdWs carve_backward(Carve& cv, const Cfg& c, bool noise) {
                                         wgrad_entries((int)groups, (int)std::max(c.d, c.h)));
   w.fw.entries = static_cast<TileEntry*>(cv.take((size_t)ent * sizeof(TileEntry)));
   w.fw.n_entries = static_cast<int32_t*>(cv.take(4));
-  w.fw.split_cap = (int)ffn_split_cap(ffn_max_entries(c.R, (int)c.E, (int)c.S, (int)c.T), c.d);
+  w.fw.split_cap = (int)ffn_split_cap(ffn_max_entries(c.R, (int)c.E, (int)c.S, (int)c.T), c.d, true);
   w.fw.split = static_cast<float*>(cv.take((size_t)w.fw.split_cap * 2 * 256 * 256 * 4));
   w.xcd_bounds = static_cast<int32_t*>(cv.take(16 * 4));
   return w;
@@ -938,10 +938,11 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   fp.S = S;
   const bool few_rows = c.R + c.S * c.T < 2000 * (c.E + c.S);
   const bool bt_down = c.bf16 && few_rows;  // (its input gradient is always tiled)
-  // the up projections' input gradient runs where launch_ffn sends it: the
-  // tiled path unless every group holds at most 32 rows
-  const bool up_tiled = !(fp.group_bound <= 32 && (S == 0 || c.T <= 32));
-  const bool bt_up = c.bf16 && few_rows && up_tiled && (!swi || c.h % 64 == 0);
+  // the up projections' input gradient then runs on the tiled kernel too,
+  // even where every group holds at most 32 rows: the weight-streaming
+  // kernel would need the transposed copies (decode: 1.9 GB of weights
+  // copied both ways per call)
+  const bool bt_up = c.bf16 && few_rows && (!swi || c.h % 64 == 0);
   if (!bt_down) {
     MOE_TRY(launch_transpose(w->w2, G, (int)c.d, (int)c.h, w2t, (int)c.d, 0, esz, stream));
     if (S > 0)
@@ -988,7 +989,7 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   du.bias_main = nullptr; du.bias_shared = nullptr;
   du.out = B.dxr; du.out_bf16 = 0; du.accumulate = 0;
   du.N = (int)c.d; du.K = (int)kup; du.act = -1;
-  MOE_TRY(launch_ffn(du, stream));
+  MOE_TRY(bt_up ? launch_ffn_tiled(du, stream) : launch_ffn(du, stream));
 
   // 6. dx = expert rows of the token + shared rows + router share
   MOE_TRY(launch_dx(bp, w->w_g, noise ? w->w_noise : nullptr, c.bf16, stream));

@@ -831,10 +831,12 @@ __global__ __launch_bounds__(256) void split_act_fixup_kernel(FfnParams p, int n
 
 }  // namespace
 
-int64_t ffn_split_cap(int64_t max_entries, int64_t N) {
-  // never more than half of a 256-block launch; never more than half the tiles
+int64_t ffn_split_cap(int64_t max_entries, int64_t N, bool wide) {
+  // never more than half of a 256-block launch; never more than half the
+  // tiles, or than all of them for a launch that may run on twice as many
+  // blocks as tiles (and so split every tile)
   const int64_t tiles = max_entries * ((N + BR - 1) / BR);
-  return std::min<int64_t>(128, (tiles + 1) / 2);
+  return std::min<int64_t>(128, wide ? tiles : (tiles + 1) / 2);
 }
 
 int64_t ffn_max_entries(int64_t rows_bound, int G, int S, int T) {
@@ -871,9 +873,13 @@ hipError_t launch_ffn_tiled(const FfnParams& p, hipStream_t stream) {
                        p.T, p.rows_bound, (int)max_entries, p.entries, p.n_entries);
   }
   // one resident block per CU (160 KiB of LDS each), never more blocks than
-  // tiles; the weight gradients' work-balanced XCD ranges need a block on
-  // every XCD (block P serves XCD P % 8), so at least 8 there
-  int64_t grid = std::min<int64_t>(device_cus(), max_entries * n_tiles_n);
+  // tiles; the backward's [K][N] input gradients, whose launches at decode
+  // and Switch sizes hold fewer tiles than CUs (each a deep reduction), take
+  // up to twice that, so the tail split cuts every tile in two on the idle
+  // CUs; the weight gradients' work-balanced XCD ranges need a block on every
+  // XCD (block P serves XCD P % 8), so at least 8 there
+  const bool wide = p.bt && p.act == -1 && p.split && p.split_cap > 0;
+  int64_t grid = std::min<int64_t>(device_cus(), max_entries * n_tiles_n * (wide ? 2 : 1));
   if (wgrad) grid = std::max<int64_t>(grid, 8);
   if (grid > 0) {
     const dim3 g((unsigned)grid), block(kThreads);

@@ -144,8 +144,9 @@ constexpr int kActBwd = 4;   // act codes 4, 5, 6: GELU, ReLU, SwiGLU backward
 constexpr int kActWgrad = 8;
 int64_t ffn_max_entries(int64_t rows_bound, int G, int S, int T);
 // tiles of a tiled launch with N output columns that its tail split may cut
-// (the scratch holds twice as many blocks of 256 x 256 floats)
-int64_t ffn_split_cap(int64_t max_entries, int64_t N);
+// (the scratch holds twice as many blocks of 256 x 256 floats); wide: the
+// backward's [K][N] input gradients, which may split every tile
+int64_t ffn_split_cap(int64_t max_entries, int64_t N, bool wide = false);
 hipError_t launch_ffn(const FfnParams& p, hipStream_t stream);
 
 // ---- expert-choice routing ---------------------------------------------------------

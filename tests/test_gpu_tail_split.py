@@ -40,7 +40,7 @@ def _split_expected(offsets, rows_bound, n_groups, N, K, cus, d=None, gated=Fals
     tiles = entries * n_tiles_n
     w, r = divmod(tiles, P)
     width = N if d is None else d
-    cap = min(128, (max_entries * ((width + BR - 1) // BR) + 1) // 2)
+    cap = min(128, max_entries * ((width + BR - 1) // BR))
     nk = (K + 63) // 64
     min_nk = 48 if gated else 2  # the gated form splits only deep reductions
     split = r > 0 and 2 * r <= P and r <= cap and nk >= min_nk
