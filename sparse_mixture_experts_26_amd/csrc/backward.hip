@@ -445,7 +445,10 @@ __global__ __launch_bounds__(256) void dx_kernel(BwdParams p, const TW* w_g, con
     shn[tt][e] = ok && p.dHn ? p.dHn[(t0 + tt) * p.E + e] : 0.f;
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < p.d; c += 256) {
+  // one column per thread: blocks cover 8 tokens x 256 columns, so even a
+  // decode batch spreads over many CUs (the per-column order is fixed)
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  if (c < p.d) {
     float acc[kDxTokens];
 #pragma unroll
     for (int tt = 0; tt < kDxTokens; ++tt) acc[tt] = 0.f;
@@ -607,12 +610,14 @@ hipError_t launch_wgrad_f32(const float* At, const float* Bt, const GroupDesc* d
 hipError_t launch_dx(const BwdParams& p, const void* w_g, const void* w_noise, int bf16,
                      hipStream_t stream) {
   const unsigned blocks = (unsigned)((p.T + kDxTokens - 1) / kDxTokens);
-  if (blocks == 0) return hipGetLastError();
+  const unsigned col_blocks = (unsigned)((p.d + 255) / 256);
+  if (blocks == 0 || col_blocks == 0) return hipGetLastError();
+  const dim3 g(blocks, col_blocks);
   if (bf16)
-    hipLaunchKernelGGL(dx_kernel<uint16_t>, dim3(blocks), dim3(256), 0, stream, p,
+    hipLaunchKernelGGL(dx_kernel<uint16_t>, g, dim3(256), 0, stream, p,
                        static_cast<const uint16_t*>(w_g), static_cast<const uint16_t*>(w_noise));
   else
-    hipLaunchKernelGGL(dx_kernel<float>, dim3(blocks), dim3(256), 0, stream, p,
+    hipLaunchKernelGGL(dx_kernel<float>, g, dim3(256), 0, stream, p,
                        static_cast<const float*>(w_g), static_cast<const float*>(w_noise));
   return hipGetLastError();
 }
