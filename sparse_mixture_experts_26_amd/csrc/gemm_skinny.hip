@@ -432,6 +432,9 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
 int device_cus();
 
 hipError_t launch_ffn_skinny(const FfnParams& p, hipStream_t stream) {
+  // the gated form stages the bf16 hidden layer (the only output it has:
+  // the kernel serves bf16 layers)
+  if (p.act == 2 && !p.out_bf16) return hipErrorInvalidValue;
   // Unit width and work split from a cost model in wave-steps of one
   // 16-column fragment: the busiest worker's units times their steps (the
   // K-split pays about 3 more steps per unit for its LDS reduction), times
