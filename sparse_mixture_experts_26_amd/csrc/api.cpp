@@ -938,10 +938,9 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   fp.S = S;
   const bool few_rows = c.R + c.S * c.T < 2000 * (c.E + c.S);
   const bool bt_down = c.bf16 && few_rows;  // (its input gradient is always tiled)
-  // the up projections' input gradient then runs on the tiled kernel too,
-  // even where every group holds at most 32 rows: the weight-streaming
-  // kernel would need the transposed copies (decode: 1.9 GB of weights
-  // copied both ways per call)
+  // the up projections' input gradient reads W1 (and W3) as stored too, on
+  // the kernel the forward's down projection uses (tiled, or weight streaming
+  // where every group holds at most 32 rows)
   const bool bt_up = c.bf16 && few_rows && (!swi || c.h % 64 == 0);
   if (!bt_down) {
     MOE_TRY(launch_transpose(w->w2, G, (int)c.d, (int)c.h, w2t, (int)c.d, 0, esz, stream));
@@ -989,7 +988,7 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   du.bias_main = nullptr; du.bias_shared = nullptr;
   du.out = B.dxr; du.out_bf16 = 0; du.accumulate = 0;
   du.N = (int)c.d; du.K = (int)kup; du.act = -1;
-  MOE_TRY(bt_up ? launch_ffn_tiled(du, stream) : launch_ffn(du, stream));
+  MOE_TRY(launch_ffn(du, stream));
 
   // 6. dx = expert rows of the token + shared rows + router share
   MOE_TRY(launch_dx(bp, w->w_g, noise ? w->w_noise : nullptr, c.bf16, stream));

@@ -49,6 +49,7 @@ struct UnitDesc {
   int over;  // rows of a group that exceeds the 32-row limit (0 otherwise)
   uint32_t a_off[2];
   uint32_t b_row[kMaxGroups];  // byte offset of this lane's weight row in group j
+  uint32_t b_col;              // BT: byte offset of this lane's 16-byte column chunk
   const uint16_t* W;
   const uint16_t* U;
   const void* A;
@@ -69,9 +70,19 @@ __device__ __forceinline__ void* uniform_ptr(const void* q) {
 // WU: every wave owns whole units (the full reduction axis, no LDS reduction,
 // no barriers), for short reductions with units enough for every wave;
 // otherwise the block's 4 waves split each unit's reduction axis.
-template <int ACT, int NF, bool WU>
+// BT: the weights are stored [K][N] per group (output columns contiguous),
+// as W1 / W3 are for the backward's input gradient of the up projections;
+// with p.kh > 0 rows k >= kh come from the second set (u_main / u_shared),
+// kh rows per group each (kh % 64 == 0).  A step's 64 rows of k, each the
+// unit's 64 columns (128 bytes), are loaded as whole lines like the stored
+// rows are otherwise, and each MFMA operand fragment comes from two LDS
+// transpose reads (ds_read_b64_tr_b16: within each 16 lanes, lane j gives 4
+// consecutive columns of row k0 + j/4 at column 4(j%4), and lane i receives
+// column i of rows k0..k0+3).  Plain (act -1) 64-column units only.
+template <int ACT, int NF, bool WU, bool BT = false>
 __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n_slabs,
                                                               int n_units) {
+  static_assert(!BT || (ACT == -1 && NF == 4), "[K][N] weights: plain 64-column units only");
   constexpr int kCols = NF * 16;
   constexpr bool GATED = ACT == 2;
   constexpr int NB = GATED ? 2 : 1;           // weight sets (w1 and w3 when gated)
@@ -96,7 +107,8 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
   float* const red = reinterpret_cast<float*>(lds + 4 * kSlot);  // [4][NFRAG][4][64]
   char* const stage = lds + 4 * (kSlot + kRed) + (WU ? w * 16 * kCols * kOutB : 0);
   const int K = p.K, N = p.N;
-  const int64_t wstride = (int64_t)N * K;
+  // elements of one group's weight set (BT with a second set: kh rows each)
+  const int64_t wstride = (BT && p.kh > 0) ? (int64_t)N * p.kh : (int64_t)N * K;
   // a contiguous run of units per block (per wave with WU), the runs in
   // order of XCD first: the hardware hands block P to XCD P % 8, so block
   // P takes run xcd_base + P / 8, and the neighbouring slabs of an expert,
@@ -125,6 +137,22 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
   for (int v = 0; v < UNR; ++v) {
     const int n = lane & 15, q = lane >> 4;
     rd_off[v] = (n >> 3) * 1024 + (n & 7) * 128 + ((((4 * v + q) ^ (n & 7)) & 7) << 4);
+  }
+  // BT: transpose reads of sub-step v, half t (rows k0 + 4t ..) for column
+  // fragment 0: lane j of 16-lane group q reads row 32v + 8q + 4t + j/4 (row
+  // r = 4t + j/4 of 8-row group 4v + q) at column 4(j%4), in 16-byte chunk
+  // c = (j/2)%2, which the load's swizzle keeps at slot c ^ r.  Fragment nf
+  // adds chunk 2 nf, which xors into the slot bits 1-2 (offset ^ nf << 5).
+  int tr_off[UNR][2];
+  if constexpr (BT) {
+    const int j = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int v = 0; v < UNR; ++v)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int r = 4 * t + (j >> 2);
+        tr_off[v][t] = (4 * v + q) * 1024 + r * 128 + ((((j >> 1) & 1) ^ r) << 4) + (j & 1) * 8;
+      }
   }
 
   // Unit descriptor.  The expert's row range and gathered rows are re-read
@@ -171,13 +199,22 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
     d.a_off[0] = cached_a[0];
     d.a_off[1] = cached_a[1];
     d.W = static_cast<const uint16_t*>(routed ? p.w_main : p.w_shared) + gw * wstride;
-    d.U = GATED ? static_cast<const uint16_t*>(routed ? p.u_main : p.u_shared) + gw * wstride : d.W;
+    d.U = (GATED || (BT && p.kh > 0))
+              ? static_cast<const uint16_t*>(routed ? p.u_main : p.u_shared) + gw * wstride
+              : d.W;
     d.A = routed ? p.a_main : p.a_shared;
+    if constexpr (BT) {
+      // the unit's columns are this lane's chunk of each k-row; an expert
+      // with no rows reads no weights
+      const int n = slab * kCols + ld_chunk * 8;
+      d.b_col = (n < N && cached_rows > 0) ? (uint32_t)n * 2u : kOOB;
+    } else {
 #pragma unroll
-    for (int j = 0; j < kGroups; ++j) {
-      const int n = slab * kCols + j * 8 + ld_row;
-      // an expert with no rows reads no weights: every offset is out of range
-      d.b_row[j] = (n < N && cached_rows > 0) ? (uint32_t)n * (uint32_t)K * 2u : kOOB;
+      for (int j = 0; j < kGroups; ++j) {
+        const int n = slab * kCols + j * 8 + ld_row;
+        // an expert with no rows reads no weights: every offset is out of range
+        d.b_row[j] = (n < N && cached_rows > 0) ? (uint32_t)n * (uint32_t)K * 2u : kOOB;
+      }
     }
   };
 
@@ -212,14 +249,30 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
     const __amdgpu_buffer_rsrc_t u_rs = __builtin_amdgcn_make_buffer_rsrc(
         uniform_ptr(d.U), (short)0, (int)(wstride * 2), 0x00020000);
     const int k0 = kb + st * kStep;
-    const uint32_t bk = (k0 + ld_chunk * 8 < ke ? (uint32_t)(k0 + ld_chunk * 8) * 2u : kOOB) | past;
+    if constexpr (BT) {
+      // 64 rows of k, 8 per load; a step lies wholly in one weight set
+      // (k0 and kh are multiples of 64)
+      const bool second = p.kh > 0 && k0 >= p.kh;
+      const int kr0 = second ? k0 - p.kh : k0;
 #pragma unroll
-    for (int s = 0; s < NB; ++s)
+      for (int j = 0; j < kGroups; ++j) {
+        const int kk = k0 + j * 8 + ld_row;
+        const uint32_t off = (kk < ke && d.b_col != kOOB)
+                                 ? (uint32_t)(kr0 + j * 8 + ld_row) * (uint32_t)N * 2u + d.b_col
+                                 : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? u_rs : w_rs,
+                                                 MOE_LDS(slot + j * 1024), 16, off | past, 0, 0, kNT);
+      }
+    } else {
+      const uint32_t bk = (k0 + ld_chunk * 8 < ke ? (uint32_t)(k0 + ld_chunk * 8) * 2u : kOOB) | past;
 #pragma unroll
-      for (int j = 0; j < kGroups; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(s == 0 ? w_rs : u_rs,
-                                                 MOE_LDS(slot + (s * kGroups + j) * 1024), 16,
-                                                 (d.b_row[j] + bk) | past, 0, 0, kNT);
+      for (int s = 0; s < NB; ++s)
+#pragma unroll
+        for (int j = 0; j < kGroups; ++j)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(s == 0 ? w_rs : u_rs,
+                                                   MOE_LDS(slot + (s * kGroups + j) * 1024), 16,
+                                                   (d.b_row[j] + bk) | past, 0, 0, kNT);
+    }
 #pragma unroll
     for (int v = 0; v < UNR; ++v) {
       const int kk = k0 + v * 32 + kl;
@@ -232,14 +285,28 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
   struct BRegs { bf16x8 b[UNR][NF][NB]; };
   // this step's weight fragments, from the wave's slot into registers
   auto fetch = [&](BRegs& br) __attribute__((always_inline)) {
+    if constexpr (BT) {
+      typedef short v4i16 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int v = 0; v < UNR; ++v)
+      for (int v = 0; v < UNR; ++v)
 #pragma unroll
-      for (int nf = 0; nf < NF; ++nf)
+        for (int nf = 0; nf < NF; ++nf) {
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)MOE_LDS(slot + (tr_off[v][0] ^ (nf << 5))));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)MOE_LDS(slot + (tr_off[v][1] ^ (nf << 5))));
+          br.b[v][nf][0] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    } else {
 #pragma unroll
-        for (int s = 0; s < NB; ++s)
-          br.b[v][nf][s] = *reinterpret_cast<const bf16x8*>(
-              slot + (s * kGroups + 2 * nf) * 1024 + rd_off[v]);
+      for (int v = 0; v < UNR; ++v)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+          for (int s = 0; s < NB; ++s)
+            br.b[v][nf][s] = *reinterpret_cast<const bf16x8*>(
+                slot + (s * kGroups + 2 * nf) * 1024 + rd_off[v]);
+    }
   };
   // Both row fragments are always multiplied: the second reads zeros when the
   // expert holds 16 rows or fewer (MFMA time is negligible here).
@@ -446,7 +513,8 @@ hipError_t launch_ffn_skinny(const FfnParams& p, hipStream_t stream) {
   int nf = 2;
   bool wu = false;
   double best = 1e300;
-  for (int cand = 4; cand >= 2; cand -= 2) {
+  if (p.bt && p.act != -1) return hipErrorInvalidValue;  // [K][N] weights: plain form only
+  for (int cand = 4; cand >= (p.bt ? 4 : 2); cand -= 2) {
     const int64_t units = groups * ((p.N + cand * 16 - 1) / (cand * 16));
     if (units == 0) continue;
     const int64_t blocks = std::min<int64_t>(units, cap);
@@ -473,7 +541,12 @@ hipError_t launch_ffn_skinny(const FfnParams& p, hipStream_t stream) {
     case 0: hipLaunchKernelGGL((ffn_skinny_kernel<0, NFV, WUV>), g, block, 0, stream, p, n_slabs, nu); break;  \
     default: hipLaunchKernelGGL((ffn_skinny_kernel<-1, NFV, WUV>), g, block, 0, stream, p, n_slabs, nu); break; \
   }
-    if (nf == 4 && wu) {
+    if (p.bt) {
+      if (wu)
+        hipLaunchKernelGGL((ffn_skinny_kernel<-1, 4, true, true>), g, block, 0, stream, p, n_slabs, nu);
+      else
+        hipLaunchKernelGGL((ffn_skinny_kernel<-1, 4, false, true>), g, block, 0, stream, p, n_slabs, nu);
+    } else if (nf == 4 && wu) {
       MOE_SKINNY_LAUNCH(4, true)
     } else if (nf == 4) {
       MOE_SKINNY_LAUNCH(4, false)

@@ -133,10 +133,11 @@ struct FfnParams {
   // the whole sum, two); null = no split
   float* split;
   int split_cap;
-  // tiled path, act -1 or kActBwd + a: the weights are stored [K][N] per
-  // group (output columns contiguous), as W2 and W1 / W3 are for the
-  // backward's input gradients; kh > 0: rows k >= kh come from the second
-  // set (u_main / u_shared), kh rows per group each (kh % 64 == 0)
+  // tiled path (act -1 or kActBwd + a) and weight-streaming path (act -1):
+  // the weights are stored [K][N] per group (output columns contiguous), as
+  // W2 and W1 / W3 are for the backward's input gradients; kh > 0: rows
+  // k >= kh come from the second set (u_main / u_shared), kh rows per group
+  // each (kh % 64 == 0)
   int bt;
   int kh;
 };
