@@ -975,7 +975,9 @@ moe_status_t moe_layer_backward(const moe_config_t* cfg, const moe_weights_t* w,
   dd.out = B.duv; dd.out_bf16 = c.bf16; dd.accumulate = 0;
   dd.N = (int)c.h; dd.K = (int)c.d; dd.act = kActBwd + c.act;
   dd.pre = sv->pre; dd.row_gate = B.row_gate;
-  MOE_TRY(c.bf16 ? launch_ffn_tiled(dd, stream) : launch_ffn_f32(dd, stream));
+  // (where every group holds at most 32 rows this streams W2 on the
+  // weight-streaming kernel, which then reads it as stored)
+  MOE_TRY(c.bf16 ? launch_ffn(dd, stream) : launch_ffn_f32(dd, stream));
 
   // 5. input gradient of the up projection(s): dx_rows = duv [w1 | w3]
   FfnParams du = fp;

@@ -82,7 +82,11 @@ __device__ __forceinline__ void* uniform_ptr(const void* q) {
 template <int ACT, int NF, bool WU, bool BT = false>
 __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n_slabs,
                                                               int n_units) {
-  static_assert(!BT || (ACT == -1 && NF == 4), "[K][N] weights: plain 64-column units only");
+  // act-backward forms (down projection's input gradient): du (dv) from the
+  // gated sum and the saved pre-activations, bf16 rows of ld = N (2N SwiGLU)
+  constexpr bool BWD = ACT >= kActBwd && ACT <= kActBwd + 2;
+  static_assert(!BT || ((ACT == -1 || BWD) && NF == 4), "[K][N] weights: 64-column units only");
+  static_assert(!BWD || BT, "act-backward forms read [K][N] weights");
   constexpr int kCols = NF * 16;
   constexpr bool GATED = ACT == 2;
   constexpr int NB = GATED ? 2 : 1;           // weight sets (w1 and w3 when gated)
@@ -322,6 +326,45 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
             acc[mf][nf][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 __builtin_bit_cast(bf16x8, sa.a[v][mf]), br.b[v][nf][s], acc[mf][nf][s], 0, 0, 0);
   };
+  // act-backward: du (dv) of one output from its sum a: the row's gate
+  // (routed rows; shared rows 1), the saved pre-activations u (v), the
+  // activation's backward; staged as bf16 at (r, c) of the du tile and of
+  // the dv tile that follows it (tile_rows rows each)
+  auto put_bwd = [&](const UnitDesc& d, int r, int c, int row, int col, float a, int tile_rows)
+      __attribute__((always_inline)) {
+    const bool routed = d.g < p.G;
+    const int64_t ra = d.c_row0 + row;
+    const int64_t ld = ACT == kActBwd + 2 ? 2 * (int64_t)N : N;
+    const uint16_t* pre = static_cast<const uint16_t*>(p.pre);
+    const float g = routed ? p.row_gate[ra] : 1.f;
+    const float uu = bf16_to_f32(pre[ra * ld + col]);
+    const float vv = ACT == kActBwd + 2 ? bf16_to_f32(pre[ra * ld + N + col]) : 0.f;
+    float du, dv;
+    act_backward(ACT - kActBwd, a * g, uu, vv, du, dv);
+    uint16_t* st = reinterpret_cast<uint16_t*>(stage);
+    st[r * kCols + c] = f32_to_bf16(du);
+    if (ACT == kActBwd + 2) st[(tile_rows + r) * kCols + c] = f32_to_bf16(dv);
+  };
+  // act-backward: tile rows [0, nrows) of the du tile (and the dv tile after
+  // it) to output rows row0 + r, columns col (du) and N + col (dv) of rows
+  // of ld bf16 elements, as 16-byte non-temporal stores; thread i of n
+  auto drain_bwd = [&](const UnitDesc& d, int u, int row0, int nrows, int tile_rows, int i, int n)
+      __attribute__((always_inline)) {
+    const int slab = u - d.g * n_slabs;
+    const int64_t ld = ACT == kActBwd + 2 ? 2 * (int64_t)N : N;
+    constexpr int per_row = kCols * 2 / 16;
+    constexpr int sets = ACT == kActBwd + 2 ? 2 : 1;
+    for (int c = i; c < sets * nrows * per_row; c += n) {
+      const int set = c / (nrows * per_row), cc = c - set * nrows * per_row;
+      const int r = cc / per_row, q = cc - r * per_row;
+      const int col = slab * kCols + q * 8;
+      if (row0 + r >= d.rows || col >= N) continue;
+      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) +
+                                            (d.c_row0 + row0 + r) * ld + set * N + col);
+      __builtin_nontemporal_store(
+          *reinterpret_cast<const u32x4*>(stage + ((set * tile_rows + r) * per_row + q) * 16), dst);
+    }
+  };
   // one output value of the unit: bias, pre-activations, activation
   auto value = [&](const UnitDesc& d, int row, int col, float a, float up)
       __attribute__((always_inline)) -> float {
@@ -382,6 +425,13 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
     for (int o = i; o < rows * kCols; o += n) {
       const int row = o / kCols, col = slab * kCols + (o - row * kCols);
       if (col >= N) continue;
+      if constexpr (BWD) {  // du (and dv) rows of ld elements
+        const int64_t ld = ACT == kActBwd + 2 ? 2 * (int64_t)N : N;
+        uint16_t* o16 = static_cast<uint16_t*>(p.out) + (d.c_row0 + row) * ld + col;
+        o16[0] = 0x7fc0u;
+        if (ACT == kActBwd + 2) o16[N] = 0x7fc0u;
+        continue;
+      }
       const int64_t idx = (int64_t)(d.c_row0 + row) * N + col;
       if (p.out_bf16) static_cast<uint16_t*>(p.out)[idx] = 0x7fc0u;
       else static_cast<float*>(p.out)[idx] = __builtin_nanf("");
@@ -406,11 +456,14 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
           for (int i = 0; i < 4; ++i) {
             const int r = (lane >> 4) * 4 + i, row = mf * 16 + r;
             const int c = nf * 16 + (lane & 15), col = slab * kCols + c;
-            if (row < d.rows && col < N)
-              put(r, c, value(d, row, col, acc[mf][nf][0][i], GATED ? acc[mf][nf][NB - 1][i] : 0.f));
+            if (row < d.rows && col < N) {
+              if constexpr (BWD) put_bwd(d, r, c, row, col, acc[mf][nf][0][i], 16);
+              else put(r, c, value(d, row, col, acc[mf][nf][0][i], GATED ? acc[mf][nf][NB - 1][i] : 0.f));
+            }
           }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's tile written
-        drain(d, u, mf * 16, 16, lane, 64);
+        if constexpr (BWD) drain_bwd(d, u, mf * 16, 16, 16, lane, 64);
+        else drain(d, u, mf * 16, 16, lane, 64);
         __builtin_amdgcn_s_waitcnt(0xc07f);  // and read, before it is reused
       }
       return;
@@ -439,13 +492,15 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
       float up = 0.f;
       if (GATED)
         up = ((R(0, f0 + 1, i, l) + R(1, f0 + 1, i, l)) + R(2, f0 + 1, i, l)) + R(3, f0 + 1, i, l);
-      put(row, c, value(d, row, col, a, up));
+      if constexpr (BWD) put_bwd(d, row, c, row, col, a, 32);
+      else put(row, c, value(d, row, col, a, up));
     }
     if (d.over) {
       poison(d, u, threadIdx.x, kThreads);
     } else {
       lds_barrier();  // the staged tile is complete
-      drain(d, u, 0, 32, threadIdx.x, kThreads);
+      if constexpr (BWD) drain_bwd(d, u, 0, 32, 32, threadIdx.x, kThreads);
+      else drain(d, u, 0, 32, threadIdx.x, kThreads);
     }
     lds_barrier();  // the partial products and the tile are reused by the next unit
   };
@@ -513,7 +568,10 @@ hipError_t launch_ffn_skinny(const FfnParams& p, hipStream_t stream) {
   int nf = 2;
   bool wu = false;
   double best = 1e300;
-  if (p.bt && p.act != -1) return hipErrorInvalidValue;  // [K][N] weights: plain form only
+  // [K][N] weights: the plain and the act-backward forms only; the
+  // act-backward forms only with [K][N] weights
+  const bool bwd = p.act >= kActBwd && p.act <= kActBwd + 2;
+  if (p.bt ? !(p.act == -1 || bwd) : bwd) return hipErrorInvalidValue;
   for (int cand = 4; cand >= (p.bt ? 4 : 2); cand -= 2) {
     const int64_t units = groups * ((p.N + cand * 16 - 1) / (cand * 16));
     if (units == 0) continue;
@@ -542,10 +600,16 @@ hipError_t launch_ffn_skinny(const FfnParams& p, hipStream_t stream) {
     default: hipLaunchKernelGGL((ffn_skinny_kernel<-1, NFV, WUV>), g, block, 0, stream, p, n_slabs, nu); break; \
   }
     if (p.bt) {
-      if (wu)
-        hipLaunchKernelGGL((ffn_skinny_kernel<-1, 4, true, true>), g, block, 0, stream, p, n_slabs, nu);
-      else
-        hipLaunchKernelGGL((ffn_skinny_kernel<-1, 4, false, true>), g, block, 0, stream, p, n_slabs, nu);
+#define MOE_SKINNY_BT(A)                                                                          \
+  if (wu) hipLaunchKernelGGL((ffn_skinny_kernel<A, 4, true, true>), g, block, 0, stream, p, n_slabs, nu); \
+  else hipLaunchKernelGGL((ffn_skinny_kernel<A, 4, false, true>), g, block, 0, stream, p, n_slabs, nu);
+      switch (p.act) {
+        case kActBwd + 2: MOE_SKINNY_BT(kActBwd + 2) break;
+        case kActBwd + 1: MOE_SKINNY_BT(kActBwd + 1) break;
+        case kActBwd: MOE_SKINNY_BT(kActBwd) break;
+        default: MOE_SKINNY_BT(-1) break;
+      }
+#undef MOE_SKINNY_BT
     } else if (nf == 4 && wu) {
       MOE_SKINNY_LAUNCH(4, true)
     } else if (nf == 4) {
