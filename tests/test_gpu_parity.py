@@ -232,6 +232,46 @@ def test_edge_configs(kw):
     _check_y(cfg, want, got)
 
 
+def test_large_batch_many_chunks():
+    """The largest batch tested, 262,144 tokens: 16,384 routing blocks and
+    their P partials, a 512-chunk dispatch scan, 64 experts of about 8,000
+    rows with drops, a 262K-token combine.  Replay first (everything exact
+    against the oracle, outputs on a sample of tokens), then the GPU's own
+    router (logit bar, flips bounded, and every later step exact against the
+    oracle re-run on the GPU's logits, outputs on the same sample)."""
+    require_gpu()
+    cfg = _cfg(name="large_batch", cfg_id=907, T=262144, d=128, E=64, k=2, h=128,
+               act="swiglu", capacity_factor=1.25)
+    banner(f"{cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} h={cfg.h}")
+    inp = make_inputs(cfg)
+    rng = np.random.default_rng(3)
+    toks = np.unique(np.concatenate([[0, 1023, 1024, cfg.T - 1],
+                                     rng.choice(cfg.T, 60, replace=False)]))
+    want = oracle_forward(inp, tokens=toks)
+    assert want["drop_rate"] > 0
+    dev = upload(inp)
+    layer = MoeLayer(cfg, weights_of(dev))
+    fill_sentinels(layer)
+    got = layer.forward(dev["x"], None, torch.from_numpy(want["logits"]).cuda())
+    torch.cuda.synchronize()
+    _check_routing_exact(cfg, want, got)
+    _check_stats(cfg, want, got)
+    _check_y(cfg, want, got)
+    fill_sentinels(layer)
+    got = layer.forward(dev["x"])
+    torch.cuda.synchronize()
+    H = host(got["logits"])
+    assert rel_l2(H, want["logits"]) <= 1e-5
+    err = float(np.abs(H.astype(np.float64) - want["logits"]).max())
+    diff, gaps = topk_flips(want["logits"], H, cfg.k)
+    banner(f"{cfg.name}: routing flips {diff.size} of {cfg.T}")
+    assert np.all(gaps <= 2 * err), (diff, gaps, err)
+    mine = oracle_forward(inp, logits=H, tokens=toks)
+    _check_routing_exact(cfg, mine, got)
+    _check_stats(cfg, mine, got)
+    _check_y(cfg, mine, got)
+
+
 def test_capacity_zero_drops_everything():
     cfg = _cfg(name="cap0", T=64, capacity_factor=1e-6)
     inp, want, layer, got = _run(cfg, replay=True)
