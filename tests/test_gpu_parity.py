@@ -272,6 +272,22 @@ def test_large_batch_many_chunks():
     _check_y(cfg, mine, got)
 
 
+@pytest.mark.parametrize("cf", [1.0, 0.5])
+def test_toy_fp32_with_drops(cf):
+    """The float32 toy layer again at capacity factors 1.0 and 0.5 (C = 32
+    and 16), where drops certainly occur: replay exact, then the GPU's own
+    router with every later step exact against the oracle on its logits."""
+    from workloads import FULL
+    cfg = FULL["toy_fp32"].with_(name=f"toy_fp32_cf{cf}", capacity_factor=cf)
+    inp, want, layer, got = _run(cfg, replay=True)
+    assert want["drop_rate"] > 0
+    _check_routing_exact(cfg, want, got)
+    _check_stats(cfg, want, got)
+    _check_y(cfg, want, got)
+    inp, want, layer, got = _run(cfg, replay=False, inp=inp)
+    _check_own_router(cfg, inp, want, got)
+
+
 def test_capacity_zero_drops_everything():
     cfg = _cfg(name="cap0", T=64, capacity_factor=1e-6)
     inp, want, layer, got = _run(cfg, replay=True)

@@ -215,6 +215,29 @@ def test_capacity_formula_values():
     assert O.capacity(1.5, 100, 1, 4) == int(100 / 4 * 1.5)
 
 
+def test_toy_layer_at_binding_capacities():
+    """The toy layer again at capacity factors 1.0 and 0.5: C = 32 and 16 by
+    the capacity formula, so with 128 assignments over 4 experts some must
+    drop; the definitional arrival-order walk and the vectorised dispatch
+    agree on which, every kept load is at most C, and a factor-0.5 layer
+    keeps exactly 4 C rows (every expert is over-subscribed)."""
+    for cf, C in ((1.0, 32), (0.5, 16)):
+        cfg = FULL["toy_fp32"].with_(name=f"toy_cf{cf}", capacity_factor=cf)
+        assert O.capacity(cf, cfg.T, cfg.k, cfg.E) == C
+        inp = make_inputs(cfg, 0)
+        H = O.router_logits(inp.x, inp.w_g, inp.b_g)
+        idx = O.select_top_k(H, cfg.k)
+        walk = O.dispatch_in_arrival_order(idx, cfg.E, C)
+        vec = O.dispatch(idx, cfg.E, C)
+        kept = np.diff(vec["offsets"])
+        assert np.all(kept <= C)
+        assert int(kept.sum()) < cfg.T * cfg.k
+        assert np.array_equal(walk["slot_rank"] >= 0, vec["dest"] >= 0)
+        assert np.array_equal(walk["kept"], kept)
+        if cf == 0.5:
+            assert int(kept.sum()) == 4 * C
+
+
 def _all_idx_patterns(T, E, k):
     choices = list(itertools.permutations(range(E), k))
     for combo in itertools.product(choices, repeat=T):
