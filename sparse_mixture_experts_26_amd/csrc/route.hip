@@ -18,7 +18,10 @@
 // on (value desc, index asc) pick the experts, and the same registers yield
 // the full softmax, whose per-expert sums over the block's tokens are written
 // per block and reduced in a fixed order by a second kernel (no atomics, so
-// results are deterministic).
+// results are deterministic).  Phase 2's wave reductions run within 16-lane
+// rows on DPP lane permutations (register-speed, where a general shuffle
+// goes through the LDS crossbar and costs a round trip per step), and the
+// four row results are read as scalars and combined in a fixed order.
 #include <algorithm>
 
 #include "launch.hpp"
@@ -30,6 +33,72 @@ namespace {
 constexpr int kMaxWaves = 16;
 constexpr int kMaxThreads = 64 * kMaxWaves;
 constexpr uint32_t kOOB = 0x80000000u;
+
+// DPP lane permutations within each 16-lane row: swap neighbours (quad
+// permutation [1,0,3,2]), swap pairs ([2,3,0,1]), reverse each half row,
+// reverse the row.  Applied in that order they leave every lane of a row
+// combined with all 16 lanes of its row.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);  // every source lane exists
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// Maximum and sum over the wave, the same value in every lane.  The sum's
+// order is fixed: pairs, quads, half rows, rows, then (row 0 + row 1) +
+// (row 2 + row 3).
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)),
+               fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+// (value desc, index asc): the candidate (ov, oi) beats (bv, bi).  A strict
+// total order on distinct indices, so any reduction order picks the same one.
+__device__ __forceinline__ void take_better(float& bv, int& bi, float ov, int oi) {
+  const bool win = (ov > bv) | ((ov == bv) & (oi < bi));  // both sides evaluated: no branch
+  bv = win ? ov : bv;
+  bi = win ? oi : bi;
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& bv, int& bi) {
+  take_better(bv, bi, dpp<CTRL>(bv), dpp<CTRL>(bi));
+}
+// the wave's best (value, index), the same in every lane
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+  argmax_step<kDppXor1>(bv, bi);
+  argmax_step<kDppXor2>(bv, bi);
+  argmax_step<kDppHalfMirror>(bv, bi);
+  argmax_step<kDppMirror>(bv, bi);
+  float v = lane_value(bv, 0);
+  int i = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16)
+    take_better(v, i, lane_value(bv, r), __builtin_amdgcn_readlane(bi, r));
+  bv = v;
+  bi = i;
+}
 
 // Phase 1, bf16: this wave's partial products over its model-width range into
 // part[m*ldh + n] (gate columns, then noise columns).  The block's waves form
@@ -55,16 +124,24 @@ __device__ void router_tile_bf16(const RouteParams& p, float* part, int ldh, int
   const int steps = (d + 31) / 32, per = (steps + nk - 1) / nk;
   const int kb = w * per * 32, ke = min(d, (w + 1) * per * 32);
   for (int nb = wc * 64; nb < ncols; nb += nc * 64) {
-    uint32_t b_base[4];
-    bool noise_col[4];
+    // Column n < E is gate row n, E <= n < 2E noise row n - E.  Each lane
+    // has an offset into both sets (out of range where its column belongs to
+    // the other set); a 16-column group loads from the set(s) it touches, so
+    // every load's buffer resource is the same for the whole wave.
+    uint32_t g_off[4], n_off[4];
+    bool g_grp[4], n_grp[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int n = nb + j * 16 + (lane & 15);
-      noise_col[j] = n >= p.E;
-      const int nn = noise_col[j] ? n - p.E : n;
-      b_base[j] = n < ncols ? (uint32_t)nn * (uint32_t)d * 2u : kOOB;
+      const int n = nb + j * 16 + (lane & 15), n0 = nb + j * 16;
+      g_off[j] = n < p.E ? (uint32_t)n * (uint32_t)d * 2u : kOOB;
+      n_off[j] = (n >= p.E && n < ncols) ? (uint32_t)(n - p.E) * (uint32_t)d * 2u : kOOB;
+      g_grp[j] = n0 < p.E;
+      n_grp[j] = ncols > p.E && n0 + 15 >= p.E && n0 < ncols;
     }
     f32x4 acc[4] = {};
+    // 16-column groups that hold columns (narrow tiles skip the rest: no
+    // loads, no MFMAs)
+    const int njc = min(4, (ncols - nb + 15) >> 4);
     // batches of 3 steps: all of a batch's loads are issued before its MFMAs
     // (steps past the range read zeros), so a wave waits for memory once per
     // batch rather than once per step
@@ -74,20 +151,29 @@ __device__ void router_tile_bf16(const RouteParams& p, float* part, int ldh, int
       u32x4 bv[kBatch][4];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
+        // past the range every offset is out of range (no sum of two
+        // out-of-range offsets, which could wrap into range)
         const int kk = k0 + u * 32 + kofs;
-        const uint32_t kadd = kk < ke ? (uint32_t)kk * 2u : kOOB;
-        a[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, a_base + kadd, 0, 0));
+        const bool kin = kk < ke;
+        const uint32_t kk2 = (uint32_t)kk * 2u;
+        a[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+            xr, kin ? a_base + kk2 : kOOB, 0, 0));
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bv[u][j] = noise_col[j] ? __builtin_amdgcn_raw_buffer_load_b128(nr, b_base[j] + kadd, 0, 0)
-                                  : __builtin_amdgcn_raw_buffer_load_b128(gr, b_base[j] + kadd, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          if (j >= njc) continue;
+          u32x4 b = {0u, 0u, 0u, 0u};
+          if (g_grp[j]) b = __builtin_amdgcn_raw_buffer_load_b128(gr, kin ? g_off[j] + kk2 : kOOB, 0, 0);
+          if (n_grp[j]) b |= __builtin_amdgcn_raw_buffer_load_b128(nr, kin ? n_off[j] + kk2 : kOOB, 0, 0);
+          bv[u][j] = b;
+        }
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], __builtin_bit_cast(bf16x8, bv[u][j]),
-                                                          acc[j], 0, 0, 0);
+          if (j < njc)
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], __builtin_bit_cast(bf16x8, bv[u][j]),
+                                                            acc[j], 0, 0, 0);
     }
     // 16x16 result layout: lane holds column lane%16, rows 4*(lane/16) + i.
 #pragma unroll
@@ -115,6 +201,69 @@ __device__ void router_tile_f32(const RouteParams& p, float* sH, int ldh, int t_
     float s = 0.0f;
     for (int c = 0; c < p.d; ++c) s = fmaf(xr[c], wr[c], s);
     sH[m * ldh + n] = s;
+  }
+}
+
+// Phase 2 for the block's tokens, NJ logits per lane (expert lane + 64 j; E
+// <= 64 NJ).  A lane's slot that holds no expert, or whose expert has been
+// selected, reads (-inf, kNone), which loses to every expert still
+// selectable (a tie on -inf goes to the lower index), so each of the k
+// rounds is a plain wave-wide argmax.  The gates' normaliser sums
+// exp(logit - best) in slot order.
+constexpr int kNone = 0x7fffffff;
+
+template <int NJ>
+__device__ __forceinline__ void route_tokens(const RouteParams& p, const float* sH, int ldh,
+                                             int t_base, int w, int nw, int lane,
+                                             float (&pacc)[4]) {
+  for (int m = w; m < kRouteTokens; m += nw) {
+    const int t = t_base + m;
+    if (t >= p.T) break;
+    float v[NJ];
+    int id[NJ];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int e = lane + 64 * j;
+      const bool ok = e < p.E;
+      v[j] = ok ? sH[m * ldh + e] : -INFINITY;
+      id[j] = ok ? e : kNone;
+      mx = fmaxf(mx, v[j]);
+    }
+    mx = wave_max_dpp(mx);
+    float ex[NJ], s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      ex[j] = id[j] != kNone ? expf(v[j] - mx) : 0.f;
+      s += ex[j];
+    }
+    s = wave_sum_dpp(s);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) pacc[j] += ex[j] / s;
+
+    float v0 = 0.f, z = 0.f, my_v = 0.f;
+    int my_i = 0;
+    for (int sl = 0; sl < p.k; ++sl) {
+      float bv = v[0];
+      int bi = id[0];
+#pragma unroll
+      for (int j = 1; j < NJ; ++j) take_better(bv, bi, v[j], id[j]);
+      wave_argmax(bv, bi);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const bool mine = id[j] == bi;
+        v[j] = mine ? -INFINITY : v[j];
+        id[j] = mine ? kNone : id[j];
+      }
+      v0 = sl == 0 ? bv : v0;
+      z += expf(bv - v0);
+      my_v = lane == sl ? bv : my_v;
+      my_i = lane == sl ? bi : my_i;
+    }
+    if (lane < p.k) {
+      p.idx[(int64_t)t * p.k + lane] = my_i;
+      p.gate[(int64_t)t * p.k + lane] = expf(my_v - v0) / z;
+    }
   }
 }
 
@@ -171,68 +320,11 @@ __global__ __launch_bounds__(kMaxThreads) void route_kernel(RouteParams p) {
   // Phase 2: one token per wave iteration; lane owns experts lane + 64*j.
   // Wave w takes tokens w, w + nw, w + 2nw, ... of the block, so every one of
   // the 16 tokens is handled whatever the wave count (which need not divide 16).
-  const int nj = (p.E + 63) >> 6;
   float pacc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int m = w; m < kRouteTokens; m += nw) {
-    const int t = t_base + m;
-    if (t >= p.T) break;
-    float v[4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      v[j] = (j < nj && e < p.E) ? sH[m * ldh + e] : -INFINITY;
-      mx = fmaxf(mx, v[j]);
-    }
-    mx = wave_max(mx);
-    float ex[4], s = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      ex[j] = (j < nj && e < p.E) ? expf(v[j] - mx) : 0.f;
-      s += ex[j];
-    }
-    s = wave_sum(s);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pacc[j] += ex[j] / s;
-
-    unsigned taken = 0;
-    float v0 = 0.f, z = 0.f;
-    float my_v = 0.f;
-    int my_i = 0;
-    for (int sl = 0; sl < p.k; ++sl) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = lane + 64 * j;
-        if (j < nj && e < p.E && !((taken >> j) & 1u) && (v[j] > bv || bi == 0x7fffffff)) {
-          bv = v[j];
-          bi = e;
-        }
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, kWave);
-        const int oi = __shfl_xor(bi, o, kWave);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (sl == 0) v0 = bv;
-      z += expf(bv - v0);
-      if (lane == sl) {
-        my_v = bv;
-        my_i = bi;
-      }
-    }
-    if (lane < p.k) {
-      p.idx[(int64_t)t * p.k + lane] = my_i;
-      p.gate[(int64_t)t * p.k + lane] = expf(my_v - v0) / z;
-    }
-  }
+  const int nj = (p.E + 63) >> 6;
+  if (nj == 1) route_tokens<1>(p, sH, ldh, t_base, w, nw, lane, pacc);
+  else if (nj == 2) route_tokens<2>(p, sH, ldh, t_base, w, nw, lane, pacc);
+  else route_tokens<4>(p, sH, ldh, t_base, w, nw, lane, pacc);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;

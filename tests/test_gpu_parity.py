@@ -313,10 +313,11 @@ def test_dense_equivalence_E1_k1(dtype):
 
 def test_ties_and_signed_zero_replay():
     """Integer-valued logits with many exact ties and both zeros: the GPU's
-    top-k must pick lowest indices among equals, exactly as the oracle."""
+    top-k must pick lowest indices among equals, exactly as the oracle (one,
+    two and up to four logits per lane of the router's selection)."""
     require_gpu()
     rng = np.random.default_rng(3)
-    for E, k in ((4, 2), (8, 3), (64, 6), (130, 5), (256, 8)):
+    for E, k in ((4, 2), (8, 3), (64, 6), (100, 4), (130, 5), (256, 8)):
         cfg = _cfg(name=f"ties_E{E}", T=300, E=E, k=k, capacity_factor=1.0)
         inp = make_inputs(cfg)
         H = rng.integers(-1, 2, size=(cfg.T, E)).astype(np.float32)
