@@ -360,8 +360,8 @@ def main():
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU (every figure is a single "
-                                   "MI355X's); run with --gpus 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only (every figure is a "
+                                   "single MI355X's); run with --gpus 1"}))
         sys.exit(2)
 
     import torch
