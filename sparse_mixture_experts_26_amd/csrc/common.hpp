@@ -87,6 +87,46 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// DPP lane permutations within each 16-lane row: swap neighbours (quad
+// permutation [1,0,3,2]), swap pairs ([2,3,0,1]), reverse each half row,
+// reverse the row.  Applied in that order they leave every lane of a row
+// combined with all 16 lanes of its row.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);  // every source lane exists
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// Maximum and sum over the wave, the same value in every lane.  The sum's
+// order is fixed: pairs, quads, half rows, rows, then (row 0 + row 1) +
+// (row 2 + row 3).
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)),
+               fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
 // One entry of the grouped-GEMM tile schedule: `rows` (<= tile height) rows
 // of weight group `group`, reading operand rows from a_row0 and writing
 // output rows from c_row0.

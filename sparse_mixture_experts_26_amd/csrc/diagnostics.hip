@@ -7,11 +7,13 @@
 // The z-loss is read as the mean over tokens of the squared log-partition of
 // the float32 logits; entropy is in nats.
 //
-// Per-token terms: one wave per token (lane owns experts lane + 64 j), 16
-// tokens per block, partial sums per block in double in a fixed order; a
-// one-block kernel reduces the partials in a fixed order (strided per thread,
-// then over the threads) and adds the count-based metrics.  No atomics:
-// results are deterministic.
+// Per-token terms: one wave per token (lane owns experts lane + 64 j; wave
+// reductions on DPP row permutations, the token's lost slots by one ballot),
+// 16 tokens per block, partial sums per block in double in a fixed order; a
+// one-block kernel reduces the partials (strided per thread, then a fixed
+// pairwise tree over the threads) and adds the count-based metrics, whose
+// sums over experts use the same tree.  No atomics: results are
+// deterministic.
 #include "launch.hpp"
 
 namespace moe {
@@ -26,41 +28,48 @@ __global__ __launch_bounds__(256) void diag_token_kernel(DiagParams p) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   double zsum = 0.0, hsum = 0.0;
   int full = 0, part = 0;
-  for (int i = 0; i < kDiagTokens / 4; ++i) {
-    const int64_t t = (int64_t)blockIdx.x * kDiagTokens + w * (kDiagTokens / 4) + i;
-    if (t >= p.T) break;
-    const float* h = p.logits + t * p.E;
-    float v[4], mx = -INFINITY;
+  // the wave's 4 tokens: every logit load is issued before any is used
+  constexpr int kPer = kDiagTokens / 4;
+  const int64_t t0 = (int64_t)blockIdx.x * kDiagTokens + w * kPer;
+  float v[kPer][4];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = lane + 64 * j;
-      v[j] = e < p.E ? h[e] : -INFINITY;
-      mx = fmaxf(mx, v[j]);
+      v[i][j] = (t0 + i < p.T && e < p.E) ? p.logits[(t0 + i) * p.E + e] : -INFINITY;
     }
-    mx = wave_max(mx);
+  int lost[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    lost[i] = __popcll(__ballot(t0 + i < p.T && lane < p.k && p.dest[(t0 + i) * p.k + lane] < 0));
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (t0 + i >= p.T) break;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, v[i][j]);
+    mx = wave_max_dpp(mx);
     float ex[4], s = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = lane + 64 * j;
-      ex[j] = e < p.E ? expf(v[j] - mx) : 0.f;
+      ex[j] = e < p.E ? expf(v[i][j] - mx) : 0.f;
       s += ex[j];
     }
-    s = wave_sum(s);
+    s = wave_sum_dpp(s);
     const float lse = mx + logf(s);
     float ph = 0.f;  // sum_e p_e h_e
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = lane + 64 * j;
-      if (e < p.E) ph += (ex[j] / s) * v[j];
+      if (e < p.E) ph += (ex[j] / s) * v[i][j];
     }
-    ph = wave_sum(ph);
-    int lost = lane < p.k && p.dest[t * p.k + lane] < 0 ? 1 : 0;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) lost += __shfl_xor(lost, o, kWave);
+    ph = wave_sum_dpp(ph);
     zsum += (double)lse * (double)lse;
     hsum += (double)lse - (double)ph;
-    full += lost == p.k;
-    part += lost > 0 && lost < p.k;
+    full += lost[i] == p.k;
+    part += lost[i] > 0 && lost[i] < p.k;
   }
   if (lane == 0) {
     s_z[w] = zsum;
@@ -79,67 +88,76 @@ __global__ __launch_bounds__(256) void diag_token_kernel(DiagParams p) {
   }
 }
 
+
 __global__ __launch_bounds__(256) void diag_final_kernel(DiagParams p, int nblocks) {
-  __shared__ double s_ov[256];
+  __shared__ double s_a[256], s_b[256], s_c[256], s_d[256];
+  __shared__ long long s_full[256], s_part[256];
+  __shared__ int s_mx[256];
   const int e = threadIdx.x;
   const double tk = (double)p.T * (double)p.k;
-  double mean = 0.0;
-  int mx = 0;
-  for (int i = 0; i < p.E; ++i) {
-    mean += (double)p.counts[i];
-    mx = max(mx, p.counts[i]);
-  }
-  mean /= (double)p.E;
-  if (e < p.E) {
-    const int c = p.counts[e];
-    const int kept = c < p.C ? c : p.C;
+  const bool ex = e < p.E;
+  const int c = ex ? p.counts[e] : 0;
+  const int kept = c < p.C ? c : p.C;
+  if (ex) {
     p.diag[8 + e] = (float)(c - kept);
     p.diag[8 + p.E + e] = p.C > 0 ? (float)((double)kept / (double)p.C) : 0.f;
-    s_ov[e] = (double)(c - kept);
   }
-  // partials: thread e sums blocks e, e+256, ... (fixed order), then thread 0
-  // sums the 256 thread sums in order
-  __shared__ double s_zs[256], s_hs[256];
-  __shared__ long long s_full[256], s_part[256];
-  {
-    double zs = 0.0, hs = 0.0;
-    long long full = 0, part = 0;
-    for (int b = e; b < nblocks; b += 256) {
-      zs += p.partial_d[2 * b];
-      hs += p.partial_d[2 * b + 1];
-      full += p.partial_i[2 * b];
-      part += p.partial_i[2 * b + 1];
-    }
-    s_zs[e] = zs;
-    s_hs[e] = hs;
-    s_full[e] = full;
-    s_part[e] = part;
+  // per-token partials: thread e sums blocks e, e + 256, ... in order
+  double zs = 0.0, hs = 0.0;
+  long long full = 0, part = 0;
+  for (int b = e; b < nblocks; b += 256) {
+    zs += p.partial_d[2 * b];
+    hs += p.partial_d[2 * b + 1];
+    full += p.partial_i[2 * b];
+    part += p.partial_i[2 * b + 1];
   }
+  s_a[e] = (double)c;
+  s_b[e] = zs;
+  s_c[e] = hs;
+  s_d[e] = (double)(c - kept);
+  s_full[e] = full;
+  s_part[e] = part;
+  s_mx[e] = c;
   __syncthreads();
+  // pairwise trees over the 256 slots, all seven in step (slot 0 ends with
+  // each total; the same pairing every call)
+  for (int o = 128; o > 0; o >>= 1) {
+    if (e < o) {
+      s_a[e] += s_a[e + o];
+      s_b[e] += s_b[e + o];
+      s_c[e] += s_c[e + o];
+      s_d[e] += s_d[e + o];
+      s_full[e] += s_full[e + o];
+      s_part[e] += s_part[e + o];
+      s_mx[e] = max(s_mx[e], s_mx[e + o]);
+    }
+    __syncthreads();
+  }
+  const double mean = s_a[0] / (double)p.E;
+  const double z_sum = s_b[0], h_sum = s_c[0], ov = s_d[0];
+  const long long n_full = s_full[0], n_part = s_part[0];
+  const int mx = s_mx[0];
+  __syncthreads();  // every thread has read the totals before the slots are reused
+  s_a[e] = ex ? ((double)c - mean) * ((double)c - mean) : 0.0;
+  s_b[e] = ex ? fabs((double)c - tk / (double)p.E) : 0.0;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (e < o) {
+      s_a[e] += s_a[e + o];
+      s_b[e] += s_b[e + o];
+    }
+    __syncthreads();
+  }
   if (e == 0) {
-    double zs = 0.0, hs = 0.0, var = 0.0, dev = 0.0, ov = 0.0;
-    long long full = 0, part = 0;
-    for (int b = 0; b < 256; ++b) {
-      zs += s_zs[b];
-      hs += s_hs[b];
-      full += s_full[b];
-      part += s_part[b];
-    }
-    for (int i = 0; i < p.E; ++i) {
-      const double c = (double)p.counts[i];
-      var += (c - mean) * (c - mean);
-      dev += fabs(c - tk / (double)p.E);
-      ov += s_ov[i];
-    }
-    var /= (double)p.E;
-    p.diag[0] = (float)(zs / (double)p.T);
-    p.diag[1] = (float)(hs / (double)p.T);
+    const double var = s_a[0] / (double)p.E;
+    p.diag[0] = (float)(z_sum / (double)p.T);
+    p.diag[1] = (float)(h_sum / (double)p.T);
     p.diag[2] = mean > 0.0 ? (float)(sqrt(var) / mean) : 0.f;
-    p.diag[3] = (float)dev;
+    p.diag[3] = (float)s_b[0];
     p.diag[4] = mean > 0.0 ? (float)((double)mx / mean) : 0.f;
     p.diag[5] = (float)ov;
-    p.diag[6] = (float)((double)full / (double)p.T);
-    p.diag[7] = (float)((double)part / (double)p.T);
+    p.diag[6] = (float)((double)n_full / (double)p.T);
+    p.diag[7] = (float)((double)n_part / (double)p.T);
   }
 }
 
