@@ -67,12 +67,17 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   }
 }
 
-// stats = [f (E), P (E), L_aux, drop_rate]; one block, fixed summation order.
+// stats = [f (E), P (E), L_aux, drop_rate]; one block, fixed summation order
+// (a pairwise tree over the 256 threads for the sums over experts and over
+// the slots left unplaced).
 __global__ __launch_bounds__(256) void stats_kernel(StatsParams p) {
   __shared__ double prod[256];
   __shared__ long long kept[256];
+  __shared__ int lost[256];
   const int e = threadIdx.x;
   const double tk = (double)p.T * (double)p.k;
+  prod[e] = 0.0;
+  kept[e] = 0;
   if (e < p.E) {
     const int c = p.counts[e];
     const double f = (double)c / tk;
@@ -82,9 +87,8 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsParams p) {
     prod[e] = f * P;
     kept[e] = c < p.C ? c : p.C;
   }
-  __syncthreads();
-  // slots left unplaced (re-routing): counted over dest in a fixed order
-  __shared__ int lost[256];
+  // slots left unplaced (re-routing): counted over dest, each thread a fixed
+  // strided subset
   int my_lost = 0;
   if (p.dest) {
     const int64_t n = (int64_t)p.T * p.k, n4 = n >> 2;
@@ -104,16 +108,17 @@ __global__ __launch_bounds__(256) void stats_kernel(StatsParams p) {
   }
   lost[e] = my_lost;
   __syncthreads();
-  if (e == 0) {
-    double s = 0.0;
-    long long ks = 0, ls = 0;
-    for (int i = 0; i < p.E; ++i) {
-      s += prod[i];
-      ks += kept[i];
+  for (int o = 128; o > 0; o >>= 1) {
+    if (e < o) {
+      prod[e] += prod[e + o];
+      kept[e] += kept[e + o];
+      lost[e] += lost[e + o];
     }
-    for (int i = 0; i < 256; ++i) ls += lost[i];
-    p.stats[2 * p.E] = (float)((double)p.E * s);
-    p.stats[2 * p.E + 1] = p.dest ? (float)((double)ls / tk) : (float)(1.0 - (double)ks / tk);
+    __syncthreads();
+  }
+  if (e == 0) {
+    p.stats[2 * p.E] = (float)((double)p.E * prod[0]);
+    p.stats[2 * p.E + 1] = p.dest ? (float)((double)lost[0] / tk) : (float)(1.0 - (double)kept[0] / tk);
   }
 }
 
