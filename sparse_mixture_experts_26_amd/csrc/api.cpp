@@ -782,6 +782,10 @@ static moe_status_t layer_forward(const moe_config_t* cfg, const moe_weights_t* 
   dn.bias_main = cfg->ffn_bias ? w->b2 : nullptr; dn.bias_shared = nullptr;
   dn.out = L.y_rows; dn.out_bf16 = 0; dn.accumulate = 0;
   dn.N = (int)c.d; dn.K = (int)c.h; dn.act = -1;
+  // the two projections pick the same kernel (same dtype, group bound, S
+  // and T) over the same groups, so a tiled down projection finds its row
+  // tiles already in the schedule scratch the up projection built
+  dn.tiles_built = 1;
   if ((st = hip_status(launch_ffn(dn, stream))) != MOE_OK) return st;
 
   // 5. combine (+ statistics)

@@ -868,7 +868,7 @@ hipError_t launch_ffn_tiled(const FfnParams& p, hipStream_t stream) {
   if (wgrad) {
     hipLaunchKernelGGL(build_wgrad_tiles_kernel, dim3(1), dim3(256), 0, stream, p.G + p.S, p.G,
                        p.M, n_tiles_n, p.gdesc, p.entries, p.n_entries, p.xcd_bounds);
-  } else {
+  } else if (!p.tiles_built) {
     hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, stream, p.offsets, p.G, p.S,
                        p.T, p.rows_bound, (int)max_entries, p.entries, p.n_entries);
   }

@@ -113,6 +113,11 @@ struct FfnParams {
   int bf16;                  // operand dtype
   TileEntry* entries;        // scratch for the tiled path
   int32_t* n_entries;        // scratch
+  // nonzero: entries / n_entries already hold this launch's row-tile
+  // schedule, built by an earlier tiled launch on the same stream with the
+  // same offsets, G, S, T and rows_bound (the forward's down projection
+  // reuses the up projection's); the launch then does not rebuild it
+  int tiles_built;
   // forward (act 0..2): when set, the pre-activations are stored too: row r
   // holds u = a W^T (+ bias) in [0, N) and, gated, v = a U^T in [N, 2N)
   void* pre;
