@@ -17,10 +17,12 @@ hipError_t launch_ffn_f32(const FfnParams& p, hipStream_t stream);
 
 // float32 -> plain kernel; <= 32 rows in every group (shared groups hold T
 // rows) -> weight-streaming kernel; otherwise the tiled MFMA kernel.
+bool ffn_uses_skinny(const FfnParams& p) {
+  return p.bf16 && p.group_bound <= 32 && (p.S == 0 || p.T <= 32);
+}
 hipError_t launch_ffn(const FfnParams& p, hipStream_t stream) {
   if (!p.bf16) return launch_ffn_f32(p, stream);
-  const bool small = p.group_bound <= 32 && (p.S == 0 || p.T <= 32);
-  return small ? launch_ffn_skinny(p, stream) : launch_ffn_tiled(p, stream);
+  return ffn_uses_skinny(p) ? launch_ffn_skinny(p, stream) : launch_ffn_tiled(p, stream);
 }
 }  // namespace moe
 
@@ -725,6 +727,20 @@ static moe_status_t layer_forward(const moe_config_t* cfg, const moe_weights_t* 
   rp.idx = L.idx; rp.gate = L.gate; rp.prob_partial = L.rw.prob_partial; rp.prob_sum = L.prob_sum;
   rp.noise_pre = nullptr;
   rp.T = (int)c.T; rp.d = (int)c.d; rp.E = (int)c.E; rp.k = (int)c.k; rp.bf16 = c.bf16;
+  // Top-1 layers without shared experts whose down projection streams the
+  // weights: every kept row is its token's only expert output, so that
+  // launch stores gate * row straight into the token's output row and there
+  // is no combine pass; the router zeroes every output row first, so the
+  // dropped tokens' rows stay zero.  Not when the caller wants the float32
+  // expert rows.
+  FfnParams fp = ffn_params(c, c.E, L.offsets, c.R, c.C, L.fw);
+  fp.S = (int)c.S;
+  const bool direct = !c.ec && !c.rr && c.k == 1 && c.S == 0 && ffn_uses_skinny(fp) &&
+                      !(aux && aux->y_rows);
+  if (direct) {
+    rp.zero_rows = y;
+    rp.row_bytes = (int)(c.d * 2);
+  }
   if ((st = hip_status(launch_route(rp, stream))) != MOE_OK) return st;
 
   // 3. counts, capacity, dispatch tables (expert choice: every expert takes
@@ -766,8 +782,6 @@ static moe_status_t layer_forward(const moe_config_t* cfg, const moe_weights_t* 
 
   // 4. grouped expert FFN: routed groups gathered through row_token, then the
   //    shared experts over all tokens, in one launch per projection
-  FfnParams fp = ffn_params(c, c.E, L.offsets, c.R, c.C, L.fw);
-  fp.S = (int)c.S;
   FfnParams up = fp;
   up.a_main = x; up.a_shared = x; up.gather = L.row_token; up.a_from_c = 0;
   up.w_main = w->w1; up.u_main = w->w3; up.w_shared = w->ws1; up.u_shared = w->ws3;
@@ -786,6 +800,10 @@ static moe_status_t layer_forward(const moe_config_t* cfg, const moe_weights_t* 
   // and T) over the same groups, so a tiled down projection finds its row
   // tiles already in the schedule scratch the up projection built
   dn.tiles_built = 1;
+  if (direct) {
+    dn.out = y; dn.out_bf16 = 1;
+    dn.direct_token = L.row_token; dn.direct_gate = L.gate;
+  }
   if ((st = hip_status(launch_ffn(dn, stream))) != MOE_OK) return st;
 
   // 5. combine (+ statistics)
@@ -804,12 +822,14 @@ static moe_status_t layer_forward(const moe_config_t* cfg, const moe_weights_t* 
     }
     return MOE_OK;
   }
-  CombineParams cp;
-  cp.y_rows = L.y_rows; cp.dest = L.dest; cp.gate = L.gate;
-  cp.y_shared = c.S > 0 ? L.y_rows + (size_t)c.R * c.d : nullptr;
-  cp.y = y; cp.T = (int)c.T; cp.d = (int)c.d; cp.k = (int)c.k; cp.S = (int)c.S;
-  cp.out_bf16 = c.bf16;
-  if ((st = hip_status(launch_combine(cp, stream))) != MOE_OK) return st;
+  if (!direct) {
+    CombineParams cp;
+    cp.y_rows = L.y_rows; cp.dest = L.dest; cp.gate = L.gate;
+    cp.y_shared = c.S > 0 ? L.y_rows + (size_t)c.R * c.d : nullptr;
+    cp.y = y; cp.T = (int)c.T; cp.d = (int)c.d; cp.k = (int)c.k; cp.S = (int)c.S;
+    cp.out_bf16 = c.bf16;
+    if ((st = hip_status(launch_combine(cp, stream))) != MOE_OK) return st;
+  }
   if (aux && aux->stats) {
     StatsParams sp;
     sp.counts = L.counts; sp.prob_sum = L.prob_sum; sp.stats = aux->stats;

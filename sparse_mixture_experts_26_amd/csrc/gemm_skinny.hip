@@ -381,7 +381,17 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
     if (GATED) return silu_f32(a) * up;
     if (ACT == 0) return gelu_f32(a);
     if (ACT == 1) return fmaxf(a, 0.f);
+    // top-1 direct store: the gate times the row, formed as the combine
+    // forms it (fma onto zero), so the stored bf16 value is the same
+    if constexpr (ACT == -1 && !BT)
+      if (p.direct_token) a = fmaf(p.direct_gate[p.direct_token[d.c_row0 + row]], a, 0.f);
     return a;
+  };
+  // output row of unit row `row` (the token's row for a top-1 direct store)
+  auto out_row = [&](const UnitDesc& d, int row) __attribute__((always_inline)) -> int64_t {
+    if constexpr (ACT == -1 && !BT)
+      if (p.direct_token) return p.direct_token[d.c_row0 + row];
+    return (int64_t)d.c_row0 + row;
   };
   // Outputs leave through LDS as 16-byte non-temporal stores, whole 64- or
   // 128-byte row segments per 4 or 8 lanes: the unit's output rows are
@@ -409,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
       if (row0 + r >= d.rows || col >= N) continue;
       // 16-byte aligned: the output is, and N is a multiple of 8
       u32x4* dst = reinterpret_cast<u32x4*>(static_cast<char*>(p.out) +
-                                            ((int64_t)(d.c_row0 + row0 + r) * N + col) * (b16 ? 2 : 4));
+                                            (out_row(d, row0 + r) * N + col) * (b16 ? 2 : 4));
       u32x4 v = *reinterpret_cast<const u32x4*>(stage + c * 16);
       if (!b16 && p.accumulate)
         v = __builtin_bit_cast(u32x4, __builtin_bit_cast(f32x4, v) + __builtin_bit_cast(f32x4, *dst));
@@ -432,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void ffn_skinny_kernel(FfnParams p, int n
         if (ACT == kActBwd + 2) o16[N] = 0x7fc0u;
         continue;
       }
-      const int64_t idx = (int64_t)(d.c_row0 + row) * N + col;
+      const int64_t idx = out_row(d, row) * N + col;
       if (p.out_bf16) static_cast<uint16_t*>(p.out)[idx] = 0x7fc0u;
       else static_cast<float*>(p.out)[idx] = __builtin_nanf("");
     }

@@ -24,6 +24,12 @@ struct RouteParams {
   float* noise_pre;         // [T,E] out: x W_noise^T before softplus, or null
   int T, d, E, k;
   int bf16;
+  // when set, each block also zeroes its tokens' rows (row_bytes bytes, a
+  // multiple of 16) of this [T, row_bytes] buffer: the output rows of a
+  // top-1 layer whose down projection stores straight into the kept
+  // tokens' rows (the dropped tokens' rows stay zero); null = nothing
+  void* zero_rows = nullptr;
+  int row_bytes = 0;
 };
 constexpr int kRouteTokens = 16;  // tokens per routing block
 inline int route_blocks(int64_t T) { return (int)((T + kRouteTokens - 1) / kRouteTokens); }
@@ -145,6 +151,12 @@ struct FfnParams {
   // each (kh % 64 == 0)
   int bt;
   int kh;
+  // weight-streaming path, act -1, top-1 layers without shared experts: each
+  // routed row r is its token's only expert output, so the epilogue stores
+  // direct_gate[t] * row (bias included) as bf16 into row t = direct_token[r]
+  // of `out` ([T, N], the layer output) instead of row r; null = row r
+  const int32_t* direct_token;
+  const float* direct_gate;
 };
 constexpr int kActBwd = 4;   // act codes 4, 5, 6: GELU, ReLU, SwiGLU backward
 constexpr int kActWgrad = 8;
@@ -154,6 +166,8 @@ int64_t ffn_max_entries(int64_t rows_bound, int G, int S, int T);
 // backward's [K][N] input gradients, which may split every tile
 int64_t ffn_split_cap(int64_t max_entries, int64_t N, bool wide = false);
 hipError_t launch_ffn(const FfnParams& p, hipStream_t stream);
+// whether launch_ffn runs p on the weight-streaming kernel
+bool ffn_uses_skinny(const FfnParams& p);
 
 // ---- expert-choice routing ---------------------------------------------------------
 struct EcParams {

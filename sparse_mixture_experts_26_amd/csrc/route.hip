@@ -296,6 +296,16 @@ __global__ __launch_bounds__(kMaxThreads) void route_kernel(RouteParams p) {
     for (int q = 1; q < nw; ++q) v += (double)sP[q][e];  // fixed order, double
     p.prob_partial[(int64_t)blockIdx.x * p.E + e] = (float)v;
   }
+  // the block's tokens' output rows, zeroed last (nothing is loaded after)
+  if (p.zero_rows) {
+    const int chunks = p.row_bytes >> 4;
+    const int rows = min(kRouteTokens, p.T - t_base);
+    for (int c = threadIdx.x; c < rows * chunks; c += nt) {
+      const int m = c / chunks, q = c - m * chunks;
+      reinterpret_cast<uint4*>(static_cast<char*>(p.zero_rows) +
+                               (int64_t)(t_base + m) * p.row_bytes)[q] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
 }
 
 // prob_sum[e] = sum over routing blocks: one wave per expert, each lane sums a

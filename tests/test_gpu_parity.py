@@ -189,6 +189,40 @@ def test_staged_entry_points_match_layer_forward(name):
         assert rel_l2(a, b) <= 1e-4
 
 
+@pytest.mark.parametrize("kw", [
+    # capacity 18 < the mean load: many drops; ReLU, no biases
+    dict(name="top1_direct", T=600, d=256, E=32, k=1, h=384, act="relu", capacity_factor=1.0),
+    # capacity 29; noisy router, GELU with both biases, a ragged model width
+    dict(name="top1_direct_noise_bias", T=700, d=136, E=24, k=1, h=200, act="gelu",
+         capacity_factor=1.0, router_noise=True, ffn_bias=True),
+])
+def test_top1_direct_store(kw):
+    """A top-1 layer without shared experts whose groups hold at most 32 rows:
+    the single call's down projection stores gate * row straight into each
+    token's output row and the dispatch zeroes the dropped tokens' rows (no
+    float32 expert rows, no combine pass).  Its output must equal the staged
+    path's (expert rows, then the combine) bit for bit, every dropped token's
+    row must be exactly zero, and both must match the oracle."""
+    cfg = _cfg(**kw)
+    # the weight-streaming down projection (capacity at most 32 rows)
+    assert O.capacity(cfg.capacity_factor, cfg.T, cfg.k, cfg.E) <= 32
+    inp, want, layer, got = _run(cfg, replay=True)
+    assert want["drop_rate"] > 0
+    _check_routing_exact(cfg, want, got)
+    _check_stats(cfg, want, got)
+    _check_y(cfg, want, got)
+    y1 = host(got["y"]).copy()
+    dropped = want["dest"].reshape(cfg.T) < 0
+    assert dropped.any() and not dropped.all()
+    assert np.all(y1[dropped] == 0) and not np.signbit(y1[dropped]).any()
+    dev = upload(inp)
+    layer2 = MoeLayer(cfg, weights_of(dev))
+    fill_sentinels(layer2)
+    got2 = layer2.staged(dev["x"], dev.get("eps"), torch.from_numpy(want["logits"]).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(got2["y"].view(torch.int16), got["y"].view(torch.int16))
+
+
 def test_bitwise_determinism():
     cfg = SMALL["finegrained_small"]
     inp, want, layer, got = _run(cfg, replay=False)
