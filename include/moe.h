@@ -367,6 +367,11 @@ moe_status_t moe_combine_expert_choice(const moe_config_t* cfg, const float* y_r
  * topk_gate, dest and diag are then not written).  With token choice,
  * aux->diag != NULL also runs moe_router_diagnostics on the layer's routing,
  * and cfg->overflow == MOE_OVERFLOW_REROUTE uses moe_dispatch_reroute.
+ * A top-1 layer without shared experts (token choice, dropping) whose groups
+ * hold at most 32 rows, called without aux->y_rows, skips the float32 expert
+ * rows and the combine: the down projection stores gate * row straight into
+ * each kept token's row of y (the same bf16 values the combine would form)
+ * and the router zeroes y's rows first, so dropped tokens read zero.
  * Intermediates live in `ws` unless `aux` names a buffer for them.
  */
 moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w,
