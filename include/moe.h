@@ -150,7 +150,10 @@ size_t moe_workspace_bytes(const moe_config_t* cfg);
  * GPU call: `waves` (host) receives the wavefronts per 16-token block and
  * `lds_bytes` (host) the block's LDS (dynamic plus static).  `device_logits`
  * nonzero describes the bf16 path that computes the logits on the device,
- * zero the replay or float32 path.  A block's waves take its 16 tokens in
+ * zero the replay or float32 path.  A bf16 batch of 1024 tokens or more
+ * whose router has 32 logit columns or more (E, or 2E with noise) computes its
+ * logits in a kernel of its own (64-token blocks) and the router kernel
+ * replays them, so it has the replay shape either way.  A block's waves take its 16 tokens in
  * turn (token m to wave m mod waves) for the top-k step, so every token is
  * routed whatever the count.  For tests and capacity planning; returns
  * MOE_OK, or the status moe_route would return for an invalid config. */

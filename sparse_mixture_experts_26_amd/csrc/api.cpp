@@ -405,7 +405,10 @@ moe_status_t moe_route_launch_shape(const moe_config_t* cfg, int device_logits, 
   moe_status_t st = check_cfg(cfg, &c);
   if (st != MOE_OK) return st;
   if (!waves || !lds_bytes) return MOE_ERR_INVALID_ARGUMENT;
-  const RoutePlan rp = route_plan((int)c.E, cfg->router_noise != 0, c.bf16 && device_logits);
+  // large bf16 batches compute their logits in a kernel of their own; the
+  // router kernel then has its replay shape
+  const bool fused = c.bf16 && device_logits && !route_split_logits(c.T, c.E, cfg->router_noise != 0);
+  const RoutePlan rp = route_plan((int)c.E, fused && cfg->router_noise != 0, fused);
   *waves = rp.waves;
   *lds_bytes = rp.lds_bytes + rp.static_lds_bytes;
   return MOE_OK;

@@ -15,8 +15,9 @@
 //   2. scan:   one block turns the chunk histograms into per-chunk bases (chunk
 //              order), counts, kept = min(counts, C) and the offsets.
 //   3. assign: rank = base + local rank; kept iff rank < C; dest and row_token.
-// A batch of at most one chunk (decode-sized) runs all three steps in a single
-// block of 16 waves, one slice per wave, with the tables kept in LDS.
+// A batch of at most four chunks (decode- and Switch-sized) runs all three
+// steps in a single block of 16 waves, one to four slices per wave, with the
+// tables kept in LDS.
 // Every step is ordered, so the integer outputs are exact and deterministic.
 #include "launch.hpp"
 
@@ -41,32 +42,47 @@ __device__ __forceinline__ int slice_rank(int e, int lane, int& count) {
   return __popcll(peers & ((1ull << lane) - 1ull));
 }
 
-// n <= kDispatchChunk: rank, scan and assign in one block; wave w = slice w.
+// n <= NS * kDispatchChunk: rank, scan and assign in one block of 16 waves;
+// wave w takes slices w, w + 16, ..., w + 16 (NS - 1), and the slices are
+// prefix-summed per expert in slice (= arrival) order.
+template <int NS>
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchParams p) {
-  __shared__ int hist[kSlices][256];
+  __shared__ int hist[NS * kSlices][256];
   __shared__ int sscan[256];
   __shared__ int soff[256];
-  const int lane = threadIdx.x & 63, s = threadIdx.x >> 6, x = threadIdx.x;
-  for (int i = x; i < kSlices * 256; i += 1024) (&hist[0][0])[i] = 0;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, x = threadIdx.x;
+  for (int i = x; i < NS * kSlices * 256; i += 1024) (&hist[0][0])[i] = 0;
   __syncthreads();
-  const int i = s * 64 + lane;
-  int e = kInvalid;
-  if (i < p.n) {
-    e = p.idx[i];
-    if (e < 0 || e >= p.E) e = kInvalid;
+  int my_e[NS], my_r[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int s = w + kSlices * j;
+    const int i = s * 64 + lane;
+    int e = kInvalid;
+    if (i < p.n) {
+      e = p.idx[i];
+      if (e < 0 || e >= p.E) e = kInvalid;
+    }
+    int cnt;
+    const int r = slice_rank(e, lane, cnt);
+    if (e != kInvalid && r == 0) hist[s][e] = cnt;
+    my_e[j] = e;
+    my_r[j] = r;
   }
-  int cnt;
-  const int r = slice_rank(e, lane, cnt);
-  if (e != kInvalid && r == 0) hist[s][e] = cnt;
   __syncthreads();
   int kept = 0;
   if (x < 256) {
     if (x < p.E) {
+      // the expert's slice counts, read together, then their exclusive
+      // prefix in slice order
+      int c[NS * kSlices];
+#pragma unroll
+      for (int q = 0; q < NS * kSlices; ++q) c[q] = hist[q][x];
       int run = 0;
-      for (int q = 0; q < kSlices; ++q) {
-        const int c = hist[q][x];
+#pragma unroll
+      for (int q = 0; q < NS * kSlices; ++q) {
         hist[q][x] = run;
-        run += c;
+        run += c[q];
       }
       p.counts[x] = run;
       kept = run < p.C ? run : p.C;
@@ -86,16 +102,22 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchParams p) 
     if (x == p.E - 1) p.offsets[p.E] = sscan[x];
   }
   __syncthreads();
-  if (i < p.n) {
-    int d = -1;
-    if (e != kInvalid) {
-      const int rank = hist[s][e] + r;
-      if (rank < p.C) {
-        d = soff[e] + rank;
-        p.row_token[d] = i / p.k;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int s = w + kSlices * j;
+    const int i = s * 64 + lane;
+    if (i < p.n) {
+      const int e = my_e[j];
+      int d = -1;
+      if (e != kInvalid) {
+        const int rank = hist[s][e] + my_r[j];
+        if (rank < p.C) {
+          d = soff[e] + rank;
+          p.row_token[d] = i / p.k;
+        }
       }
+      p.dest[i] = d;
     }
-    p.dest[i] = d;
   }
 }
 
@@ -215,7 +237,11 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* x, const int3
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t stream) {
   const int chunks = dispatch_chunks(p.n);
   if (chunks == 1) {
-    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, stream, p);
+    hipLaunchKernelGGL(dispatch_small_kernel<1>, dim3(1), dim3(1024), 0, stream, p);
+    return hipGetLastError();
+  }
+  if (chunks <= 4) {  // (a 64 KiB slice table in LDS)
+    hipLaunchKernelGGL(dispatch_small_kernel<4>, dim3(1), dim3(1024), 0, stream, p);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(dispatch_rank_kernel, dim3(chunks), dim3(256), 0, stream, p);

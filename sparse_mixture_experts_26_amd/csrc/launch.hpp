@@ -34,6 +34,17 @@ struct RouteParams {
 constexpr int kRouteTokens = 16;  // tokens per routing block
 inline int route_blocks(int64_t T) { return (int)((T + kRouteTokens - 1) / kRouteTokens); }
 hipError_t launch_route(const RouteParams& p, hipStream_t stream);
+// bf16 batches of at least this many tokens, with at least 32 logit columns
+// (gate plus noise), compute their logits in a kernel of their own (64-token
+// blocks, so the router matrix is read from L2 once per 64 tokens instead of
+// once per 16) and route_kernel replays them.  A narrower router matrix is
+// cheap to re-read, and there the single fused launch is faster.
+#ifndef MOE_ROUTE_SPLIT_MIN_T
+#define MOE_ROUTE_SPLIT_MIN_T 1024
+#endif
+inline bool route_split_logits(int64_t T, int64_t E, bool noise) {
+  return T >= MOE_ROUTE_SPLIT_MIN_T && E * (noise ? 2 : 1) >= 32;
+}
 // Launch shape of route_kernel: waves per block, dynamic and static LDS bytes
 // (mma: bf16 logits computed on the device; otherwise float32 or replay).
 struct RoutePlan { int waves; size_t lds_bytes; size_t static_lds_bytes; };

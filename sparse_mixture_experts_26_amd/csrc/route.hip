@@ -64,7 +64,11 @@ __device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
 // part[m*ldh + n] (gate columns, then noise columns).  The block's waves form
 // nk x nc: nk contiguous model-width ranges, and nc interleaved sets of
 // 64-column groups (wide tiles: the column groups run in parallel instead of
-// one after another); wave w takes range w % nk and set w / nk.
+// one after another); wave w takes range w % nk and set w / nk.  NJ: 16-column
+// groups per 64-column set that can hold columns (narrow tiles skip the rest);
+// NOISE: the tile has noise columns, so each group loads from both sets (a
+// lane's offset into the set its column is not in reads zeros) and ORs them.
+template <int NJ, bool NOISE>
 __device__ void router_tile_bf16(const RouteParams& p, float* part, int ldh, int t_base,
                                  int ncols, int nk, int nc) {
   const int lane = threadIdx.x & 63;
@@ -75,7 +79,7 @@ __device__ void router_tile_bf16(const RouteParams& p, float* part, int ldh, int
       const_cast<void*>(p.x), (short)0, 0x7fffffff, 0x00020000);
   const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(p.w_g), (short)0, (int)((int64_t)p.E * d * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t nr = p.w_noise ? __builtin_amdgcn_make_buffer_rsrc(
+  const __amdgpu_buffer_rsrc_t nr = NOISE ? __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(p.w_noise), (short)0, (int)((int64_t)p.E * d * 2), 0x00020000) : gr;
   const int row = t_base + (lane & 15);
   const int kofs = (lane >> 4) * 8;
@@ -84,31 +88,24 @@ __device__ void router_tile_bf16(const RouteParams& p, float* part, int ldh, int
   const int steps = (d + 31) / 32, per = (steps + nk - 1) / nk;
   const int kb = w * per * 32, ke = min(d, (w + 1) * per * 32);
   for (int nb = wc * 64; nb < ncols; nb += nc * 64) {
-    // Column n < E is gate row n, E <= n < 2E noise row n - E.  Each lane
-    // has an offset into both sets (out of range where its column belongs to
-    // the other set); a 16-column group loads from the set(s) it touches, so
-    // every load's buffer resource is the same for the whole wave.
-    uint32_t g_off[4], n_off[4];
-    bool g_grp[4], n_grp[4];
+    // Column n < E is gate row n, E <= n < 2E noise row n - E: each lane has
+    // an offset into both sets, out of range in the set its column is not in.
+    uint32_t g_off[NJ], n_off[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = nb + j * 16 + (lane & 15), n0 = nb + j * 16;
+    for (int j = 0; j < NJ; ++j) {
+      const int n = nb + j * 16 + (lane & 15);
       g_off[j] = n < p.E ? (uint32_t)n * (uint32_t)d * 2u : kOOB;
-      n_off[j] = (n >= p.E && n < ncols) ? (uint32_t)(n - p.E) * (uint32_t)d * 2u : kOOB;
-      g_grp[j] = n0 < p.E;
-      n_grp[j] = ncols > p.E && n0 + 15 >= p.E && n0 < ncols;
+      n_off[j] = (NOISE && n >= p.E && n < ncols) ? (uint32_t)(n - p.E) * (uint32_t)d * 2u : kOOB;
     }
-    f32x4 acc[4] = {};
-    // 16-column groups that hold columns (narrow tiles skip the rest: no
-    // loads, no MFMAs)
-    const int njc = min(4, (ncols - nb + 15) >> 4);
-    // batches of 3 steps: all of a batch's loads are issued before its MFMAs
-    // (steps past the range read zeros), so a wave waits for memory once per
-    // batch rather than once per step
-    constexpr int kBatch = 3;
+    f32x4 acc[NJ] = {};
+    // batches of 3 steps (2 for 4 groups with noise, within the 16-wave
+    // block's 128 registers): all of a batch's loads are issued before its
+    // MFMAs (steps past the range read zeros), so a wave waits for memory once
+    // per batch rather than once per step
+    constexpr int kBatch = (NOISE && NJ == 4) ? 2 : 3;
     for (int k0 = kb; k0 < ke; k0 += 32 * kBatch) {
       bf16x8 a[kBatch];
-      u32x4 bv[kBatch][4];
+      u32x4 bg[kBatch][NJ], bn[kBatch][NJ];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         // past the range every offset is out of range (no sum of two
@@ -119,31 +116,154 @@ __device__ void router_tile_bf16(const RouteParams& p, float* part, int ldh, int
         a[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
             xr, kin ? a_base + kk2 : kOOB, 0, 0));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j >= njc) continue;
-          u32x4 b = {0u, 0u, 0u, 0u};
-          if (g_grp[j]) b = __builtin_amdgcn_raw_buffer_load_b128(gr, kin ? g_off[j] + kk2 : kOOB, 0, 0);
-          if (n_grp[j]) b |= __builtin_amdgcn_raw_buffer_load_b128(nr, kin ? n_off[j] + kk2 : kOOB, 0, 0);
-          bv[u][j] = b;
+        for (int j = 0; j < NJ; ++j) {
+          bg[u][j] = __builtin_amdgcn_raw_buffer_load_b128(
+              gr, kin && g_off[j] != kOOB ? g_off[j] + kk2 : kOOB, 0, 0);
+          if constexpr (NOISE)
+            bn[u][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                nr, kin && n_off[j] != kOOB ? n_off[j] + kk2 : kOOB, 0, 0);
         }
       }
+      // keep the batch's loads ahead of its MFMAs (the scheduler would
+      // otherwise pair each load with its use and wait on it)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (j < njc)
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], __builtin_bit_cast(bf16x8, bv[u][j]),
-                                                            acc[j], 0, 0, 0);
+        for (int j = 0; j < NJ; ++j) {
+          u32x4 b = bg[u][j];
+          if constexpr (NOISE) b |= bn[u][j];
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], __builtin_bit_cast(bf16x8, b),
+                                                          acc[j], 0, 0, 0);
+        }
     }
     // 16x16 result layout: lane holds column lane%16, rows 4*(lane/16) + i.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int n = nb + j * 16 + (lane & 15);
       if (n < ncols) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) part[((lane >> 4) * 4 + i) * ldh + n] = acc[j][i];
       }
     }
+  }
+}
+
+// Router logits of a large bf16 batch, ahead of route_kernel's replay form.
+// The fused kernel's 16-token blocks each read the whole router matrix, so a
+// batch of T tokens reads it T/16 times from L2 (a 128-expert noisy router
+// over 4096 tokens: 100 MB; 64 experts over 16384 tokens: 268 MB).  Here a
+// block takes 64 tokens and one block of columns: EB experts' gate rows (and,
+// with noise, the same experts' noise rows), 16 NG weight rows in all.  Its 4
+// waves split the model width into contiguous ranges and each computes the
+// whole 64 x 16NG tile over its range (4 x NG tiles of
+// v_mfma_f32_16x16x32_bf16, float32 accumulate), so no operand is loaded
+// twice within a block; the 4 partial tiles are summed in LDS in wave order
+// (fixed, deterministic), then bias and noise are applied as in the fused
+// kernel and the logits (and the pre-softplus noise sums) written out.
+// Columns: gate expert e0 + c for c < EB; with noise, noise expert e0 + c - EB
+// for EB <= c < 2 EB (EB = 8 NG with noise, 16 NG without).
+constexpr int kLogitRows = 64;
+template <int NG, bool NOISE>
+__global__ __launch_bounds__(256) void router_logits_kernel(RouteParams p) {
+  constexpr int NC = 16 * NG, EB = NOISE ? NC / 2 : NC, LD = NC + 1;
+  __shared__ float part[4][kLogitRows * LD];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t0 = blockIdx.x * kLogitRows, e0 = blockIdx.y * EB;
+  const int d = p.d;
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.x), (short)0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.w_g), (short)0, (int)((int64_t)p.E * d * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t nr = NOISE ? __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.w_noise), (short)0, (int)((int64_t)p.E * d * 2), 0x00020000) : gr;
+  const int kofs = (lane >> 4) * 8;
+  uint32_t a_off[4], b_off[NG];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int t = t0 + 16 * m + (lane & 15);
+    a_off[m] = t < p.T ? (uint32_t)t * (uint32_t)d * 2u : kOOB;
+  }
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const int e = e0 + (16 * j) % EB + (lane & 15);
+    b_off[j] = e < min(p.E, e0 + EB) ? (uint32_t)e * (uint32_t)d * 2u : kOOB;
+  }
+  // this wave's contiguous model-width range, in steps of 32
+  const int steps = (d + 31) / 32, per = (steps + 3) / 4;
+  const int kb = w * per * 32, ke = min(d, (w + 1) * per * 32);
+  f32x4 acc[4][NG] = {};
+  // batches of kBatch steps: all of a batch's loads are issued before its
+  // MFMAs, so a wave waits for memory once per batch
+  constexpr int kBatch = NG >= 4 ? 4 : 6;
+  for (int k0 = kb; k0 < ke; k0 += 32 * kBatch) {
+    bf16x8 a[kBatch][4], b[kBatch][NG];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int kk = k0 + u * 32 + kofs;
+      const bool kin = kk < ke;
+      const uint32_t kk2 = (uint32_t)kk * 2u;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        a[u][m] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+            xr, kin && a_off[m] != kOOB ? a_off[m] + kk2 : kOOB, 0, 0));
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        // gate rows, then (with noise) the noise rows of the same experts
+        const bool from_noise = NOISE && j >= NG / 2;
+        b[u][j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+            from_noise ? nr : gr, kin && b_off[j] != kOOB ? b_off[j] + kk2 : kOOB, 0, 0));
+      }
+    }
+    // keep the batch's loads ahead of its MFMAs (the scheduler would otherwise
+    // pair each load with its use and wait on it, one load in flight at a time)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < NG; ++j)
+          acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][m], b[u][j], acc[m][j], 0, 0, 0);
+  }
+  // 16x16 result layout: lane holds column lane%16, rows 4*(lane/16) + i
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int j = 0; j < NG; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        part[w][(16 * m + 4 * (lane >> 4) + i) * LD + 16 * j + (lane & 15)] = acc[m][j][i];
+  __syncthreads();
+  // thread -> column c = tid % EB, rows tid / EB + (256 / EB) i: the bias is
+  // loaded once and every eps load of the thread is issued before any is used
+  constexpr int RS = 256 / EB, NR = kLogitRows / RS;
+  const int c = threadIdx.x % EB, r0 = threadIdx.x / EB, e = e0 + c;
+  const bool col_ok = e < p.E;
+  const float bias = (p.b_g && col_ok) ? p.b_g[e] : 0.f;
+  float eps[NR];
+  if constexpr (NOISE) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int t = t0 + r0 + RS * i;
+      eps[i] = (col_ok && t < p.T) ? p.eps[(int64_t)t * p.E + e] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int r = r0 + RS * i, t = t0 + r;
+    if (!col_ok || t >= p.T) continue;
+    const int o = r * LD + c;
+    float v = ((part[0][o] + part[1][o]) + part[2][o]) + part[3][o];  // wave order
+    v += bias;
+    if constexpr (NOISE) {
+      const int on = o + EB;
+      const float n = ((part[0][on] + part[1][on]) + part[2][on]) + part[3][on];
+      v += eps[i] * softplus_f32(n);
+      if (p.noise_pre) p.noise_pre[(int64_t)t * p.E + e] = n;
+    }
+    p.logits[(int64_t)t * p.E + e] = v;
   }
 }
 
@@ -245,7 +365,18 @@ __global__ __launch_bounds__(kMaxThreads) void route_kernel(RouteParams p) {
       // the model width; every (range, column) partial lands in tile w % nk
       const int nc = ncols > 64 ? min(4, min(nw, (ncols + 63) / 64)) : 1;
       const int nk = nw / nc;
-      router_tile_bf16(p, lds + (w % nk) * tile, ldh, t_base, ncols, nk, nc);
+      float* part = lds + (w % nk) * tile;
+      // 16-column groups a 64-column set can hold: 1, 2 or 4
+      const int nj = ncols > 32 ? 4 : (ncols > 16 ? 2 : 1);
+      if (noise) {
+        if (nj == 4) router_tile_bf16<4, true>(p, part, ldh, t_base, ncols, nk, nc);
+        else if (nj == 2) router_tile_bf16<2, true>(p, part, ldh, t_base, ncols, nk, nc);
+        else router_tile_bf16<1, true>(p, part, ldh, t_base, ncols, nk, nc);
+      } else {
+        if (nj == 4) router_tile_bf16<4, false>(p, part, ldh, t_base, ncols, nk, nc);
+        else if (nj == 2) router_tile_bf16<2, false>(p, part, ldh, t_base, ncols, nk, nc);
+        else router_tile_bf16<1, false>(p, part, ldh, t_base, ncols, nk, nc);
+      }
       __syncthreads();
       for (int i = threadIdx.x; i < tile; i += nt) {
         float v = lds[i];
@@ -256,23 +387,49 @@ __global__ __launch_bounds__(kMaxThreads) void route_kernel(RouteParams p) {
       router_tile_f32(p, sH, ldh, t_base, ncols);
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < kRouteTokens * p.E; i += nt) {
-      const int m = i / p.E, e = i - m * p.E, t = t_base + m;
-      if (t >= p.T) continue;
-      float v = sH[m * ldh + e];
-      if (p.b_g) v += p.b_g[e];
-      if (noise) {
-        const float n = sH[m * ldh + p.E + e];
-        v += p.eps[(int64_t)t * p.E + e] * softplus_f32(n);
-        if (p.noise_pre) p.noise_pre[(int64_t)t * p.E + e] = n;
+    // the block's 16 x E logits, 4 per thread per pass: a pass issues its
+    // bias and eps loads before it uses any of them
+    for (int i0 = 0; i0 < kRouteTokens * p.E; i0 += 4 * nt) {
+      float bias[4], ep[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * nt + threadIdx.x;
+        const int m = i / p.E, e = i - m * p.E, t = t_base + m;
+        const bool ok = i < kRouteTokens * p.E && t < p.T;
+        bias[u] = (ok && p.b_g) ? p.b_g[e] : 0.f;
+        ep[u] = (ok && noise) ? p.eps[(int64_t)t * p.E + e] : 0.f;
       }
-      sH[m * ldh + e] = v;
-      p.logits[(int64_t)t * p.E + e] = v;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * nt + threadIdx.x;
+        const int m = i / p.E, e = i - m * p.E, t = t_base + m;
+        if (i >= kRouteTokens * p.E || t >= p.T) continue;
+        float v = sH[m * ldh + e] + bias[u];
+        if (noise) {
+          const float n = sH[m * ldh + p.E + e];
+          v += ep[u] * softplus_f32(n);
+          if (p.noise_pre) p.noise_pre[(int64_t)t * p.E + e] = n;
+        }
+        sH[m * ldh + e] = v;
+        p.logits[(int64_t)t * p.E + e] = v;
+      }
     }
   } else {
-    for (int i = threadIdx.x; i < kRouteTokens * p.E; i += nt) {
-      const int m = i / p.E, e = i - m * p.E, t = t_base + m;
-      if (t < p.T) sH[m * ldh + e] = p.logits[(int64_t)t * p.E + e];
+    // replay: 4 loads per thread in flight per pass
+    for (int i0 = 0; i0 < kRouteTokens * p.E; i0 += 4 * nt) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * nt + threadIdx.x;
+        const int m = i / p.E, e = i - m * p.E, t = t_base + m;
+        v[u] = (i < kRouteTokens * p.E && t < p.T) ? p.logits[(int64_t)t * p.E + e] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * nt + threadIdx.x;
+        const int m = i / p.E, e = i - m * p.E;
+        if (i < kRouteTokens * p.E) sH[m * ldh + e] = v[u];
+      }
     }
   }
   __syncthreads();
@@ -356,8 +513,29 @@ RoutePlan route_plan(int E, bool noise, bool mma) {
 
 hipError_t launch_route(const RouteParams& p, hipStream_t stream) {
   const int blocks = route_blocks(p.T);
-  const RoutePlan rp = route_plan(p.E, p.w_noise != nullptr, p.bf16 && p.x);
-  hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(64 * rp.waves), rp.lds_bytes, stream, p);
+  if (p.bf16 && p.x && route_split_logits(p.T, p.E, p.w_noise != nullptr)) {
+    // logits first (bias and noise applied), then the router kernel replays them
+    const bool noise = p.w_noise != nullptr;
+    // (at least 32 columns: two groups of 16, or four past 32 columns)
+    const int ng = (noise ? 2 * p.E : p.E) > 32 ? 4 : 2;
+    const int eb = noise ? 8 * ng : 16 * ng;
+    const dim3 g((unsigned)((p.T + kLogitRows - 1) / kLogitRows), (unsigned)((p.E + eb - 1) / eb));
+#define MOE_LOGITS(NGV, NZ) hipLaunchKernelGGL((router_logits_kernel<NGV, NZ>), g, dim3(256), 0, stream, p)
+    if (noise) {
+      if (ng == 4) MOE_LOGITS(4, true); else MOE_LOGITS(2, true);
+    } else {
+      if (ng == 4) MOE_LOGITS(4, false); else MOE_LOGITS(2, false);
+    }
+#undef MOE_LOGITS
+    RouteParams q = p;
+    q.x = nullptr; q.w_g = nullptr; q.b_g = nullptr; q.w_noise = nullptr; q.eps = nullptr;
+    q.noise_pre = nullptr;
+    const RoutePlan rp = route_plan(p.E, false, false);
+    hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(64 * rp.waves), rp.lds_bytes, stream, q);
+  } else {
+    const RoutePlan rp = route_plan(p.E, p.w_noise != nullptr, p.bf16 && p.x);
+    hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(64 * rp.waves), rp.lds_bytes, stream, p);
+  }
   hipLaunchKernelGGL(prob_reduce_kernel, dim3((p.E + 3) / 4), dim3(256), 0, stream,
                      (const float*)p.prob_partial, p.prob_sum, blocks, p.E);
   return hipGetLastError();

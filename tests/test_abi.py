@@ -299,6 +299,17 @@ def test_router_launch_shape_routes_every_token():
                     seen.add(waves)
     # the shapes that exposed the old contiguous split are among those checked
     assert 15 in seen and 16 in seen
+    # large bf16 batches with 32 logit columns or more replay logits computed
+    # by a kernel of their own: the router kernel then has its 4-wave shape
+    for E, noise, split in ((8, False, False), (16, True, True), (31, False, False),
+                            (32, False, True), (64, False, True), (128, True, True)):
+        for T, big in ((1023, False), (1024, True), (16384, True)):
+            c = M.make_config(T, 2048, E, 1, 64, router_noise=noise)
+            waves, lds = M.moe_route_launch_shape(c, True)
+            if split and big:
+                assert waves == 4, (E, noise, T, waves)
+            else:
+                assert waves >= 8, (E, noise, T, waves)
 
 
 def test_noalloc_rejects_layers_beyond_its_scratch():

@@ -132,6 +132,46 @@ def test_router_wave_counts(E, noise):
     _check_own_router(cfg, inp, want, got)
 
 
+@pytest.mark.parametrize("E,noise,d", [(1, False, 256), (8, False, 264), (13, True, 256),
+                                       (16, True, 200), (17, False, 256), (33, True, 264),
+                                       (40, False, 264),
+                                       (64, False, 256), (100, True, 200), (128, True, 264),
+                                       (256, False, 256)])
+def test_router_logits_kernel(E, noise, d):
+    """Batches of 1024 tokens or more with 32 logit columns or more compute
+    their logits in a kernel of their own (64-token blocks, one to four
+    16-column groups, gate and noise columns of the same experts in one block)
+    before the top-k step replays them; narrower routers keep the fused
+    kernel.  T = 1101 ends in a partial 64-token block; expert counts that are
+    not multiples of the column block and model widths that are not multiples
+    of 32 leave ragged column and reduction tails."""
+    import sparse_mixture_experts_26_amd as M
+    k = min(2, E)
+    cfg = _cfg(name=f"router_logits_E{E}_{'noisy' if noise else 'plain'}_d{d}", T=1101, d=d,
+               E=E, k=k, h=64, act="relu", capacity_factor=1.25, router_noise=noise,
+               router_bias="normal", router_bias_std=0.5)
+    waves, _ = M.moe_route_launch_shape(M.make_config(cfg.T, cfg.d, E, k, 64,
+                                                      router_noise=noise), True)
+    if E * (2 if noise else 1) >= 32:
+        assert waves == 4  # the router kernel replays the logits kernel's output
+    inp, want, layer, got = _run(cfg, replay=False)
+    assert np.all(host(got["topk_idx"]) >= 0)
+    _check_own_router(cfg, inp, want, got)
+
+
+@pytest.mark.parametrize("T,k,E,cf", [(1500, 2, 8, 1.0), (4096, 1, 128, 1.0), (2049, 2, 16, 1.25),
+                                      (1024, 4, 64, 0.0)])
+def test_dispatch_single_block_sizes(T, k, E, cf):
+    """Dispatch of 1025 to 4096 assignments runs in one block (four 1024-
+    assignment chunks); 4098 assignments take the three-launch path.  Exact
+    against the oracle with the oracle's logits replayed, drops included."""
+    cfg = _cfg(name=f"dispatch_T{T}_k{k}_E{E}", T=T, d=64, E=E, k=k, h=32, act="relu",
+               capacity_factor=cf, router_bias="normal", router_bias_std=1.0)
+    inp, want, layer, got = _run(cfg, replay=True)
+    _check_routing_exact(cfg, want, got)
+    _check_stats(cfg, want, got)
+
+
 def test_dispatch_permuted_copy():
     """moe_dispatch with x and x_perm: row r of x_perm is row row_token[r] of
     x, bit for bit, for every kept row; rows past the kept total are left
