@@ -807,6 +807,14 @@ static moe_status_t layer_forward(const moe_config_t* cfg, const moe_weights_t* 
     dn.out = y; dn.out_bf16 = 1;
     dn.direct_token = L.row_token; dn.direct_gate = L.gate;
   }
+  // A bf16 layer whose combine gathers 4 or more rows per token (k routed
+  // plus the shared experts) keeps its own expert rows in bf16, rounded once
+  // like every other bf16 activation: half the bytes the down projection
+  // writes and the combine reads.  Not when the caller wants the float32
+  // rows, and not with fewer rows per token, where the float32 down
+  // projection's tail split is worth more than the traffic.
+  const bool rows_bf16 = c.bf16 && !c.ec && !direct && !(aux && aux->y_rows) && c.k + c.S >= 4;
+  if (rows_bf16) dn.out_bf16 = 1;
   if ((st = hip_status(launch_ffn(dn, stream))) != MOE_OK) return st;
 
   // 5. combine (+ statistics)
@@ -828,9 +836,11 @@ static moe_status_t layer_forward(const moe_config_t* cfg, const moe_weights_t* 
   if (!direct) {
     CombineParams cp;
     cp.y_rows = L.y_rows; cp.dest = L.dest; cp.gate = L.gate;
-    cp.y_shared = c.S > 0 ? L.y_rows + (size_t)c.R * c.d : nullptr;
+    cp.y_shared = c.S > 0 ? static_cast<const char*>(static_cast<const void*>(L.y_rows)) +
+                                (size_t)c.R * c.d * (rows_bf16 ? 2 : 4)
+                          : nullptr;
     cp.y = y; cp.T = (int)c.T; cp.d = (int)c.d; cp.k = (int)c.k; cp.S = (int)c.S;
-    cp.out_bf16 = c.bf16;
+    cp.out_bf16 = c.bf16; cp.rows_bf16 = rows_bf16;
     if ((st = hip_status(launch_combine(cp, stream))) != MOE_OK) return st;
   }
   if (aux && aux->stats) {

@@ -7,8 +7,9 @@
 // dropped assignment contributes nothing.  Shared experts add with weight 1.
 //
 // One block per token gathers its <= k expert rows (each contiguous, 16-byte
-// loads) and accumulates in float32 in a fixed order: shared experts first,
-// then slot 0, 1, ...; the result is stored in the layer dtype.
+// loads; float32 rows, or the bf16 rows a bf16 layer call keeps) and
+// accumulates in float32 in a fixed order: shared experts first, then slot 0,
+// 1, ...; the result is stored in the layer dtype.
 #include "launch.hpp"
 
 namespace moe {
@@ -21,15 +22,34 @@ namespace {
 // for all slots are issued before the fixed-order accumulation.
 constexpr int kNT = 2;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float* row, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), (short)0, bytes, 0x00020000);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0, bytes, 0x00020000);
 }
 
-// KM: slots per token the instance handles (k <= KM)
-template <int KM>
+// the VW values of one 16-byte load: float32, or bf16 pairs.  (The element
+// is copied to a scalar first: a bit cast applied to a vector element
+// expression itself reads element 0 whatever the index.)
+template <bool RB>
+__device__ __forceinline__ float lane_val(const u32x4& v, int j) {
+  if constexpr (RB) {
+    const uint32_t w = v[j >> 1];
+    return __builtin_bit_cast(float, (j & 1) ? (w & 0xffff0000u) : (w << 16));
+  } else {
+    const uint32_t w = v[j];
+    return __builtin_bit_cast(float, w);
+  }
+}
+
+// KM: slots per token the instance handles (k <= KM); RB: expert rows (and
+// shared rows) in bf16, 8 columns per 16-byte load instead of 4
+template <int KM, bool RB>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  constexpr int VW = RB ? 8 : 4;   // columns per 16-byte load
+  constexpr int ES = RB ? 2 : 4;   // bytes per row element
   const int64_t t = blockIdx.x;
   const int d = p.d;
+  const char* rows = static_cast<const char*>(p.y_rows);
+  const char* shared = static_cast<const char*>(p.y_shared);
   int dst[KM];
   float g[KM];
   __amdgpu_buffer_rsrc_t rs[KM];
@@ -37,32 +57,44 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   for (int s = 0; s < KM; ++s) {
     dst[s] = s < p.k ? p.dest[t * p.k + s] : -1;
     g[s] = s < p.k ? p.gate[t * p.k + s] : 0.f;
-    rs[s] = row_rsrc(p.y_rows + (int64_t)(dst[s] >= 0 ? dst[s] : 0) * d, dst[s] >= 0 ? d * 4 : 0);
+    rs[s] = row_rsrc(rows + (int64_t)(dst[s] >= 0 ? dst[s] : 0) * d * ES, dst[s] >= 0 ? d * ES : 0);
   }
-  for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < p.S; ++s)
-      acc += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                 row_rsrc(p.y_shared + ((int64_t)s * p.T + t) * d, d * 4), (uint32_t)c * 4u, 0, kNT));
-    f32x4 v[KM];
+  for (int c = threadIdx.x * VW; c < d; c += blockDim.x * VW) {
+    float acc[VW];
 #pragma unroll
-    for (int s = 0; s < KM; ++s)
-      v[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs[s], (uint32_t)c * 4u, 0, kNT));
+    for (int j = 0; j < VW; ++j) acc[j] = 0.f;
+    for (int s = 0; s < p.S; ++s) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+          row_rsrc(shared + ((int64_t)s * p.T + t) * d * ES, d * ES), (uint32_t)c * ES, 0, kNT);
+#pragma unroll
+      for (int j = 0; j < VW; ++j) acc[j] += lane_val<RB>(v, j);
+    }
+    u32x4 v[KM];
+#pragma unroll
+    for (int s = 0; s < KM; ++s) v[s] = __builtin_amdgcn_raw_buffer_load_b128(rs[s], (uint32_t)c * ES, 0, kNT);
 #pragma unroll
     for (int s = 0; s < KM; ++s) {
       if (dst[s] < 0) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = fmaf(g[s], v[s][j], acc[j]);
+      for (int j = 0; j < VW; ++j) acc[j] = fmaf(g[s], lane_val<RB>(v[s], j), acc[j]);
     }
     if (p.out_bf16) {
-      uint32_t lo = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-      uint32_t hi = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
-      uint2 pk;
-      pk.x = lo;
-      pk.y = hi;
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + t * d + c) = pk;
+      uint32_t w[VW / 2];
+#pragma unroll
+      for (int j = 0; j < VW / 2; ++j)
+        w[j] = (uint32_t)f32_to_bf16(acc[2 * j]) | ((uint32_t)f32_to_bf16(acc[2 * j + 1]) << 16);
+      uint16_t* o = static_cast<uint16_t*>(p.y) + t * d + c;
+      if constexpr (RB) {
+        *reinterpret_cast<u32x4*>(o) = u32x4{w[0], w[1], w[2], w[3]};
+      } else {
+        uint2 pk;
+        pk.x = w[0];
+        pk.y = w[1];
+        *reinterpret_cast<uint2*>(o) = pk;
+      }
     } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(p.y) + t * d + c) = acc;
+      *reinterpret_cast<f32x4*>(static_cast<float*>(p.y) + t * d + c) =
+          f32x4{acc[0], acc[1], acc[2], acc[3]};
     }
   }
 }
@@ -128,10 +160,15 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   const int threads = p.d >= 1024 ? 256 : (p.d >= 512 ? 128 : 64);
   if (p.T > 0) {
     const dim3 g((unsigned)p.T), b((unsigned)threads);
-    if (p.k <= 1) hipLaunchKernelGGL(combine_kernel<1>, g, b, 0, stream, p);
-    else if (p.k <= 2) hipLaunchKernelGGL(combine_kernel<2>, g, b, 0, stream, p);
-    else if (p.k <= 4) hipLaunchKernelGGL(combine_kernel<4>, g, b, 0, stream, p);
-    else hipLaunchKernelGGL(combine_kernel<8>, g, b, 0, stream, p);
+#define MOE_COMBINE(RBV)                                                                   \
+  if (p.k <= 1) hipLaunchKernelGGL((combine_kernel<1, RBV>), g, b, 0, stream, p);         \
+  else if (p.k <= 2) hipLaunchKernelGGL((combine_kernel<2, RBV>), g, b, 0, stream, p);    \
+  else if (p.k <= 4) hipLaunchKernelGGL((combine_kernel<4, RBV>), g, b, 0, stream, p);    \
+  else hipLaunchKernelGGL((combine_kernel<8, RBV>), g, b, 0, stream, p);
+    // bf16 rows only feed a bf16 output
+    if (p.rows_bf16 && !p.out_bf16) return hipErrorInvalidValue;
+    if (p.rows_bf16) { MOE_COMBINE(true) } else { MOE_COMBINE(false) }
+#undef MOE_COMBINE
   }
   return hipGetLastError();
 }

@@ -211,8 +211,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
   // weight gradients: tiles differ in depth, so the XCD ranges balance work
   // (computed with the schedule); otherwise equal tile counts
   // (the GELU / ReLU forms would spill registers with a split epilogue)
+  // (a bf16 down projection does not split: its partials would need a
+  // converting fixup)
   constexpr bool SPLITS = ACT == -1 || ACT == 2;
-  const SplitPlan plan = SPLITS && p.split
+  const SplitPlan plan = SPLITS && p.split && !(ACT == -1 && p.out_bf16)
                              ? split_plan(tiles, gridDim.x, (p.K + BK - 1) / BK, p.split_cap, GATED)
                              : SplitPlan{tiles, 0, 1};
   const int per = (plan.full + 7) >> 3;
@@ -629,6 +631,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
            [&](int row, int colc, const u32x4& ch) __attribute__((always_inline)) {
              *reinterpret_cast<u32x4*>(part + row * BR + (colc - n_out0)) = ch;
            });
+    } else if (ACT == -1 && p.out_bf16) {
+      // bf16 rows of a down projection (a layer call's expert outputs, read
+      // once by its combine), bias added before the one rounding
+      uint16_t* out = static_cast<uint16_t*>(p.out);
+      emit(Bf16{}, [&](int mi, int nj, int v) __attribute__((always_inline)) { return acc[mi][nj][v] + bcol[nj]; },
+           [&](int row, int colc, const u32x4& ch) __attribute__((always_inline)) {
+             __builtin_nontemporal_store(ch, reinterpret_cast<u32x4*>(out + (crow0 + row) * N + colc));
+           });
     } else {
       // float32 rows (down projection, input gradients) or weight gradients,
       // all written once for a later launch (or the caller): non-temporal
@@ -917,7 +927,7 @@ hipError_t launch_ffn_tiled(const FfnParams& p, hipStream_t stream) {
       default: hipLaunchKernelGGL(ffn_tiled_kernel<-1>, g, block, 0, stream, p, n_tiles_n); break;
     }
     // the split tiles of a tail split (the plan is made on the device)
-    const bool splits = p.act == -1 || p.act == 2;
+    const bool splits = (p.act == -1 && !p.out_bf16) || p.act == 2;
     if (splits && p.split && p.split_cap > 0) {
       const int fix = (int)std::min<int64_t>(p.split_cap, grid / 2);
       const dim3 fg((unsigned)(fix * kFixParts)), fb(256);

@@ -227,13 +227,14 @@ hipError_t launch_diagnostics(const DiagParams& p, hipStream_t stream);
 
 // ---- combine -------------------------------------------------------------------
 struct CombineParams {
-  const float* y_rows;       // [*, d]
+  const void* y_rows;        // [*, d] float32, or bf16 with rows_bf16
   const int32_t* dest;       // [T,k]
   const float* gate;         // [T,k]
-  const float* y_shared;     // [S,T,d] or null
+  const void* y_shared;      // [S,T,d] (the dtype of y_rows) or null
   void* y;                   // [T,d]
   int T, d, k, S;
   int out_bf16;
+  int rows_bf16 = 0;         // expert rows in bf16 (a bf16 layer call's own rows)
 };
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 

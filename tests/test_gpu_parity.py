@@ -223,10 +223,26 @@ def test_staged_entry_points_match_layer_forward(name):
     else:
         # the staged path runs the shared experts as launches of their own, so
         # the tail split of the down projection may cut other tiles (float32
-        # partial sums in another order): equal up to the output's last bit
+        # partial sums in another order); and the single call of a bf16 layer
+        # whose tokens gather 4 or more expert rows (k routed plus shared)
+        # keeps those rows in bf16, one more rounding per row.  Per element
+        # the two outputs then differ by at most a bf16 rounding (2^-8
+        # relative) of each output and of every gated term, the terms' sizes
+        # taken from the staged float32 rows, plus float32 slack.
         a, b = host(got2["y"]).astype(np.float64), host(y1).astype(np.float64)
-        assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 1e-30)
-        assert rel_l2(a, b) <= 1e-4
+        rows = host(layer2.y_rows).astype(np.float64)
+        R, T = layer2.rows_bound, cfg.T
+        mag = np.zeros_like(a)
+        for s in range(cfg.n_shared):
+            mag += np.abs(rows[R + s * T:R + (s + 1) * T])
+        dest = host(got2["dest"])
+        gate = host(got2["topk_gate"]).astype(np.float64)
+        for slot in range(cfg.k):
+            ok = dest[:, slot] >= 0
+            mag[ok] += np.abs(gate[ok, slot, None] * rows[dest[ok, slot]])
+        bound = 1.1 * 2.0 ** -8 * (np.abs(a) + np.abs(b) + mag) + 1e-5 * mag + 1e-30
+        assert np.all(np.abs(a - b) <= bound)
+        assert rel_l2(a, b) <= 1e-2
 
 
 @pytest.mark.parametrize("kw", [
