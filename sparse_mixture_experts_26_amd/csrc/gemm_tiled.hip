@@ -222,7 +222,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
   const int t_end = WGRAD ? p.xcd_bounds[xcd + 1] : min(plan.full, (xcd + 1) * per);
   const int per_h = (plan.units + 7) >> 3;
   const int h_begin = xcd * per_h, h_end = min(plan.units, (xcd + 1) * per_h);
-  const int n_whole = t_begin + q < t_end ? (t_end - t_begin - q + nq - 1) / nq : 0;
+  // Round r of the XCD's range is its tiles [r nq, (r+1) nq); this block
+  // takes slot (q + r) mod nq of it.  The slot turns with the round because a
+  // row-tile group's tiles cycle through its entries, so a fixed slot would
+  // give one block the same entry in every round, and the cheap tiles of a
+  // partly filled entry would all land on the same few blocks.
+  const int span = max(0, t_end - t_begin), full_r = span / nq, rem_r = span - full_r * nq;
+  const int n_whole = full_r + ((q + full_r) % nq < rem_r ? 1 : 0);
   const int N = p.N;
   constexpr uint32_t kOOB = 0x80000000u;
 
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     // this block's whole tiles, then its split units
     int t, half = -1;  // -1: whole tile; else the part of its reduction
     if (it < n_whole) {
-      t = t_begin + q + it * nq;
+      t = t_begin + it * nq + (q + it) % nq;
     } else {
       const int u = h_begin + q + (it - n_whole) * nq;
       if (u >= h_end) break;
@@ -305,6 +311,15 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     const int nks = ke - kb;
     const int k_end = ke == nk ? K : ke * BK;
     const int n_out0 = n_idx * (GATED ? BR / 2 : BR);
+    // Waves 4-7 compute tile rows 128-255 and issue no loads: in a tile of at
+    // most 128 rows (the partly filled last row tile of a group) they only
+    // keep the tile's barriers (one before the prologue, one per stage, one
+    // before the epilogue), which halves its MFMA work.  (Not in the [K][N]
+    // forms, the backward's few-row input gradients, whose registers are full.)
+    if (!BT && wm == 1 && te.rows <= 128) {
+      for (int st = 0; st < nks + 2; ++st) asm volatile("s_barrier" ::: "memory");
+      continue;
+    }
 
     // ---- direct-to-LDS loads.  A quarter is 16 loads of 1 KiB (8 rows x 128
     // bytes, whole cache lines); loading wave w (0-3) fills rows 16w .. 16w+15
