@@ -375,12 +375,12 @@ moe_status_t moe_combine_expert_choice(const moe_config_t* cfg, const float* y_r
  * rows and the combine: the down projection stores gate * row straight into
  * each kept token's row of y (the same bf16 values the combine would form)
  * and the router zeroes y's rows first, so dropped tokens read zero.
- * A bf16 token-choice layer whose tokens gather 4 or more expert rows (k plus
- * n_shared), called without aux->y_rows, keeps those rows in its workspace as
- * bf16 (each rounded once from its float32 sum, bias included) instead of
- * float32, which halves the bytes the down projection writes and the combine
- * reads; the combine still accumulates in float32 in the same fixed order.
- * With aux->y_rows the rows are float32, as the stage entry points give them.
+ * Any other bf16 token-choice layer called without aux->y_rows keeps its
+ * expert rows in its workspace as bf16 (each rounded once from its float32
+ * sum, bias included) instead of float32, which halves the bytes the down
+ * projection writes and the combine reads; the combine still accumulates in
+ * float32 in the same fixed order.  With aux->y_rows the rows are float32, as
+ * the stage entry points give them.
  * Intermediates live in `ws` unless `aux` names a buffer for them.
  */
 moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w,

@@ -147,15 +147,26 @@ DiagWs carve_diag(Carve& cv, const Cfg& c) {
   return w;
 }
 // Tile schedule of the tiled GEMM, plus the tail-split partials of its
-// launches (two 256 x 256 float32 blocks per split tile).
-FfnWs carve_ffn(Carve& cv, int64_t rows_bound, int64_t groups, int64_t S, int64_t T, int64_t d) {
+// launches (256 x 256 float32 blocks, `blocks` per split tile: 2, or 3 where
+// a down projection with a bf16 output may split).
+FfnWs carve_ffn(Carve& cv, int64_t rows_bound, int64_t groups, int64_t S, int64_t T, int64_t d,
+                int blocks = 2) {
   FfnWs w;
   const int64_t ent = ffn_max_entries(rows_bound, (int)groups, (int)S, (int)T);
   w.entries = static_cast<TileEntry*>(cv.take((size_t)ent * sizeof(TileEntry)));
   w.n_entries = static_cast<int32_t*>(cv.take(4));
   w.split_cap = (int)ffn_split_cap(ent, d);
-  w.split = static_cast<float*>(cv.take((size_t)w.split_cap * 2 * 256 * 256 * 4));
+  w.split = static_cast<float*>(cv.take((size_t)w.split_cap * blocks * 256 * 256 * 4));
   return w;
+}
+
+// A bf16 token-choice layer call keeps its expert rows in bf16 (unless the
+// caller wants them, or a top-1 direct store leaves none); where its down
+// projection is tiled, that projection's split tiles need a third partial
+// block.  The grouped GEMM is tiled unless every group holds at most 32 rows
+// (capacity) and there are no shared experts over more than 32 tokens.
+bool layer_tiled_bf16_rows(const Cfg& c) {
+  return c.bf16 && !c.ec && !(c.C <= 32 && (c.S == 0 || c.T <= 32));
 }
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
@@ -197,7 +208,7 @@ LayerWs carve_layer(Carve& cv, const Cfg& c, const moe_aux_t* aux) {
   w.y_rows = static_cast<float*>(pick(aux ? aux->y_rows : nullptr, (size_t)rows * c.d * 4));
   w.rw = carve_route(cv, c);
   w.dw = carve_dispatch(cv, c);
-  w.fw = carve_ffn(cv, c.R, c.E, c.S, c.T, c.d);
+  w.fw = carve_ffn(cv, c.R, c.E, c.S, c.T, c.d, layer_tiled_bf16_rows(c) ? 3 : 2);
   w.gw = carve_diag(cv, c);
   w.rrw = RerouteWs{};
   if (c.rr) w.rrw = carve_reroute(cv, c);
@@ -807,13 +818,12 @@ static moe_status_t layer_forward(const moe_config_t* cfg, const moe_weights_t* 
     dn.out = y; dn.out_bf16 = 1;
     dn.direct_token = L.row_token; dn.direct_gate = L.gate;
   }
-  // A bf16 layer whose combine gathers 4 or more rows per token (k routed
-  // plus the shared experts) keeps its own expert rows in bf16, rounded once
-  // like every other bf16 activation: half the bytes the down projection
-  // writes and the combine reads.  Not when the caller wants the float32
-  // rows, and not with fewer rows per token, where the float32 down
-  // projection's tail split is worth more than the traffic.
-  const bool rows_bf16 = c.bf16 && !c.ec && !direct && !(aux && aux->y_rows) && c.k + c.S >= 4;
+  // A bf16 layer keeps its own expert rows in bf16, rounded once (bias
+  // included) like every other bf16 activation: half the bytes the down
+  // projection writes and the combine reads.  Not when the caller wants the
+  // float32 rows.  (A tiled down projection's split tiles then sum float32
+  // partials in a fixup, in the third scratch block carve_layer gave them.)
+  const bool rows_bf16 = c.bf16 && !c.ec && !direct && !(aux && aux->y_rows);
   if (rows_bf16) dn.out_bf16 = 1;
   if ((st = hip_status(launch_ffn(dn, stream))) != MOE_OK) return st;
 

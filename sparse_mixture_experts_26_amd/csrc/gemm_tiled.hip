@@ -211,10 +211,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
   // weight gradients: tiles differ in depth, so the XCD ranges balance work
   // (computed with the schedule); otherwise equal tile counts
   // (the GELU / ReLU forms would spill registers with a split epilogue)
-  // (a bf16 down projection does not split: its partials would need a
-  // converting fixup)
   constexpr bool SPLITS = ACT == -1 || ACT == 2;
-  const SplitPlan plan = SPLITS && p.split && !(ACT == -1 && p.out_bf16)
+  const SplitPlan plan = SPLITS && p.split
                              ? split_plan(tiles, gridDim.x, (p.K + BK - 1) / BK, p.split_cap, GATED)
                              : SplitPlan{tiles, 0, 1};
   const int per = (plan.full + 7) >> 3;
@@ -638,6 +636,15 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
                *reinterpret_cast<u32x2*>(out + r * ld + N + colc) = o;
              }
            });
+    } else if (ACT == -1 && !BT && p.out_bf16 && half >= 0) {
+      // a part of a split tile with a bf16 output: every part writes its
+      // float32 sums (no bias), tile-local rows of BR values, one block per
+      // part; split_bf16_fixup_kernel adds them and rounds
+      float* part = p.split + ((int64_t)(t - plan.full) * 3 + half) * (BM * BR);
+      emit(F32{}, [&](int mi, int nj, int v) __attribute__((always_inline)) { return acc[mi][nj][v]; },
+           [&](int row, int colc, const u32x4& ch) __attribute__((always_inline)) {
+             *reinterpret_cast<u32x4*>(part + row * BR + (colc - n_out0)) = ch;
+           });
     } else if (SPLITS && half >= 1) {
       // a later part of a split tile: float32 partials (no bias), tile-local
       // rows of BR values
@@ -646,7 +653,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
            [&](int row, int colc, const u32x4& ch) __attribute__((always_inline)) {
              *reinterpret_cast<u32x4*>(part + row * BR + (colc - n_out0)) = ch;
            });
-    } else if (ACT == -1 && p.out_bf16) {
+    } else if (ACT == -1 && !BT && p.out_bf16) {
       // bf16 rows of a down projection (a layer call's expert outputs, read
       // once by its combine), bias added before the one rounding
       uint16_t* out = static_cast<uint16_t*>(p.out);
@@ -778,6 +785,60 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(FfnParams p, int n_til
 #pragma unroll
   for (int u = 0; u < kPer; ++u)
     if (ok[u]) *dst[u] = third ? (b[u] + a[u]) + c3[u] : b[u] + a[u];
+}
+
+// The split tiles of a down projection with a bf16 output: out = ((part0 +
+// part1) (+ part2)) + bias, rounded once, in part order (same plan as the
+// GEMM with P of its blocks).  kFixParts blocks per split tile, 16 rows each;
+// every thread issues its chunks' loads before adding.
+__global__ __launch_bounds__(256) void split_bf16_fixup_kernel(FfnParams p, int n_tiles_n, int P) {
+  const int n_entries = *p.n_entries;
+  const SplitPlan plan = split_plan(n_entries * n_tiles_n, P, (p.K + BK - 1) / BK, p.split_cap, false);
+  const int j = blockIdx.x / kFixParts, r0 = (blockIdx.x % kFixParts) * (BM / kFixParts);
+  if (j * plan.parts >= plan.units) return;
+  int e_idx, n_idx;
+  tile_coords(plan.full + j, n_entries, n_tiles_n, e_idx, n_idx);
+  const TileEntry te = p.entries[e_idx];
+  const bool routed = te.group < p.G;
+  const int gw = routed ? te.group : te.group - p.G;
+  const float* bias = routed ? p.bias_main : p.bias_shared;
+  const int n_out0 = n_idx * BR;
+  uint16_t* out = static_cast<uint16_t*>(p.out);
+  const float* part = p.split + (int64_t)(3 * j) * (BM * BR);
+  const bool third = plan.parts == 3;
+  constexpr int kChunks = BR / 4;  // float4 chunks per tile row
+  constexpr int kPer = (BM / kFixParts) * kChunks / 256;
+  f32x4 a[kPer], b[kPer], c3[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = threadIdx.x + u * 256;
+    const int row = r0 + i / kChunks, c = (i % kChunks) * 4;
+    a[u] = *reinterpret_cast<const f32x4*>(part + row * BR + c);
+    b[u] = *reinterpret_cast<const f32x4*>(part + BM * BR + row * BR + c);
+    if (third) c3[u] = *reinterpret_cast<const f32x4*>(part + 2 * BM * BR + row * BR + c);
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = threadIdx.x + u * 256;
+    const int row = r0 + i / kChunks, c = (i % kChunks) * 4, col = n_out0 + c;
+    if (row >= te.rows || col >= p.N) continue;
+    f32x4 v = a[u] + b[u];
+    if (third) v += c3[u];
+    uint32_t w[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      float lo = v[2 * q], hi = v[2 * q + 1];
+      if (bias) {
+        lo += bias[(int64_t)gw * p.N + col + 2 * q];
+        hi += bias[(int64_t)gw * p.N + col + 2 * q + 1];
+      }
+      w[q] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    }
+    u32x2 o;
+    o[0] = w[0];
+    o[1] = w[1];
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(out + (int64_t)(te.c_row0 + row) * p.N + col));
+  }
 }
 
 // The split tiles of the gated up projection: out = silu(gate) * up in bf16
@@ -942,13 +1003,17 @@ hipError_t launch_ffn_tiled(const FfnParams& p, hipStream_t stream) {
       default: hipLaunchKernelGGL(ffn_tiled_kernel<-1>, g, block, 0, stream, p, n_tiles_n); break;
     }
     // the split tiles of a tail split (the plan is made on the device)
-    const bool splits = (p.act == -1 && !p.out_bf16) || p.act == 2;
+    const bool splits = p.act == -1 || p.act == 2;
     if (splits && p.split && p.split_cap > 0) {
       const int fix = (int)std::min<int64_t>(p.split_cap, grid / 2);
       const dim3 fg((unsigned)(fix * kFixParts)), fb(256);
-      if (fix > 0) switch (p.act) {
-        case 2: hipLaunchKernelGGL(split_act_fixup_kernel<2>, fg, fb, 0, stream, p, n_tiles_n, (int)grid); break;
-        default: hipLaunchKernelGGL(split_fixup_kernel, fg, fb, 0, stream, p, n_tiles_n, (int)grid); break;
+      if (fix > 0) {
+        if (p.act == 2)
+          hipLaunchKernelGGL(split_act_fixup_kernel<2>, fg, fb, 0, stream, p, n_tiles_n, (int)grid);
+        else if (p.out_bf16)
+          hipLaunchKernelGGL(split_bf16_fixup_kernel, fg, fb, 0, stream, p, n_tiles_n, (int)grid);
+        else
+          hipLaunchKernelGGL(split_fixup_kernel, fg, fb, 0, stream, p, n_tiles_n, (int)grid);
       }
     }
   }

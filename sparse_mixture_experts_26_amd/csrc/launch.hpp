@@ -150,9 +150,11 @@ struct FfnParams {
   void* out_shared;
   int32_t* xcd_bounds;       // [9] scratch: each XCD's tile range
   // tiled path, act -1 and 2: float32 partials of the tiles whose reduction
-  // is cut in two (tail split), 2 * split_cap blocks of 256 x 256 (act -1
-  // uses one per split tile, the gated up projection, whose epilogue needs
-  // the whole sum, two); null = no split
+  // is cut in parts (tail split), blocks of 256 x 256: 2 * split_cap (act -1
+  // with a float32 output uses one per later part, the gated up projection,
+  // whose epilogue needs the whole sum, one per part of its two), or
+  // 3 * split_cap for act -1 with a bf16 output (one per part, summed and
+  // rounded by a fixup); null = no split
   float* split;
   int split_cap;
   // tiled path (act -1 or kActBwd + a) and weight-streaming path (act -1):
