@@ -132,28 +132,36 @@ def test_router_wave_counts(E, noise):
     _check_own_router(cfg, inp, want, got)
 
 
-@pytest.mark.parametrize("E,noise,d", [(1, False, 256), (8, False, 264), (13, True, 256),
-                                       (16, True, 200), (17, False, 256), (33, True, 264),
-                                       (40, False, 264),
-                                       (64, False, 256), (100, True, 200), (128, True, 264),
-                                       (256, False, 256)])
-def test_router_logits_kernel(E, noise, d):
+@pytest.mark.parametrize("E,noise,d,T", [(1, False, 256, 1101), (8, False, 264, 1101),
+                                         (13, True, 256, 1101), (16, True, 200, 1101),
+                                         (17, False, 256, 1101), (33, True, 264, 1101),
+                                         (40, False, 264, 1101), (64, False, 256, 1101),
+                                         (100, True, 200, 1101), (128, True, 264, 1101),
+                                         (256, False, 256, 1101),
+                                         # a width of 64: two of the four waves' ranges are empty
+                                         (64, False, 64, 1101),
+                                         # exactly the batch size where the split starts
+                                         (32, False, 128, 1024), (32, False, 128, 1023)])
+def test_router_logits_kernel(E, noise, d, T):
     """Batches of 1024 tokens or more with 32 logit columns or more compute
     their logits in a kernel of their own (64-token blocks, one to four
     16-column groups, gate and noise columns of the same experts in one block)
     before the top-k step replays them; narrower routers keep the fused
     kernel.  T = 1101 ends in a partial 64-token block; expert counts that are
     not multiples of the column block and model widths that are not multiples
-    of 32 leave ragged column and reduction tails."""
+    of 32 leave ragged column and reduction tails; T = 1024 and 1023 sit on
+    either side of the threshold."""
     import sparse_mixture_experts_26_amd as M
     k = min(2, E)
-    cfg = _cfg(name=f"router_logits_E{E}_{'noisy' if noise else 'plain'}_d{d}", T=1101, d=d,
+    cfg = _cfg(name=f"router_logits_E{E}_{'noisy' if noise else 'plain'}_d{d}_T{T}", T=T, d=d,
                E=E, k=k, h=64, act="relu", capacity_factor=1.25, router_noise=noise,
                router_bias="normal", router_bias_std=0.5)
     waves, _ = M.moe_route_launch_shape(M.make_config(cfg.T, cfg.d, E, k, 64,
                                                       router_noise=noise), True)
-    if E * (2 if noise else 1) >= 32:
+    if E * (2 if noise else 1) >= 32 and T >= 1024:
         assert waves == 4  # the router kernel replays the logits kernel's output
+    else:
+        assert waves >= 8  # the fused kernel
     inp, want, layer, got = _run(cfg, replay=False)
     assert np.all(host(got["topk_idx"]) >= 0)
     _check_own_router(cfg, inp, want, got)
