@@ -825,6 +825,26 @@ static moe_status_t layer_forward(const moe_config_t* cfg, const moe_weights_t* 
   // partials in a fixup, in the third scratch block carve_layer gave them.)
   const bool rows_bf16 = c.bf16 && !c.ec && !direct && !(aux && aux->y_rows);
   if (rows_bf16) dn.out_bf16 = 1;
+  // Two shared experts on the tiled path run as one group whose reduction
+  // covers both in turn (2h deep): one output row per token, the sum of the
+  // two, instead of two rows for the combine to add; half the shared tiles,
+  // each twice as deep.  Their hidden rows stay where the up projection
+  // wrote them (expert s's row t at R + s*T + t); the launch builds its own
+  // schedule (one shared group).  Not when the caller wants the rows, and
+  // only for h a multiple of the 64-deep stage, so no stage straddles the
+  // two experts.
+  const bool shared_cat = c.bf16 && !c.ec && c.S == 2 && c.h % 64 == 0 && !ffn_uses_skinny(fp) &&
+                          !(aux && aux->y_rows) && !direct;
+  if (shared_cat) {
+    dn.S = 1;
+    dn.shared_cat = 2;
+    dn.a_shared = static_cast<const char*>(L.hidden) + (size_t)c.R * c.h * c.esz;
+    dn.tiles_built = 0;
+    // tiles of two depths: the XCD ranges are cut by depth and the tail is
+    // not split
+    dn.split = nullptr;
+    dn.split_cap = 0;
+  }
   if ((st = hip_status(launch_ffn(dn, stream))) != MOE_OK) return st;
 
   // 5. combine (+ statistics)
@@ -849,7 +869,7 @@ static moe_status_t layer_forward(const moe_config_t* cfg, const moe_weights_t* 
     cp.y_shared = c.S > 0 ? static_cast<const char*>(static_cast<const void*>(L.y_rows)) +
                                 (size_t)c.R * c.d * (rows_bf16 ? 2 : 4)
                           : nullptr;
-    cp.y = y; cp.T = (int)c.T; cp.d = (int)c.d; cp.k = (int)c.k; cp.S = (int)c.S;
+    cp.y = y; cp.T = (int)c.T; cp.d = (int)c.d; cp.k = (int)c.k; cp.S = shared_cat ? 1 : (int)c.S;
     cp.out_bf16 = c.bf16; cp.rows_bf16 = rows_bf16;
     if ((st = hip_status(launch_combine(cp, stream))) != MOE_OK) return st;
   }

@@ -216,8 +216,21 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
                              ? split_plan(tiles, gridDim.x, (p.K + BK - 1) / BK, p.split_cap, GATED)
                              : SplitPlan{tiles, 0, 1};
   const int per = (plan.full + 7) >> 3;
-  const int t_begin = WGRAD ? p.xcd_bounds[xcd] : xcd * per;
-  const int t_end = WGRAD ? p.xcd_bounds[xcd + 1] : min(plan.full, (xcd + 1) * per);
+  int t_begin = WGRAD ? p.xcd_bounds[xcd] : xcd * per;
+  int t_end = WGRAD ? p.xcd_bounds[xcd + 1] : min(plan.full, (xcd + 1) * per);
+  if (ACT == -1 && !BT && p.shared_cat == 2) {
+    // the routed tiles come first and the concatenated shared group's last,
+    // each of those twice as deep: the XCD ranges are cut by depth, not
+    // count (the launch does not split its tail)
+    const int ts = ((p.T + BM - 1) / BM) * n_tiles_n, tr = tiles - ts;
+    const int64_t ctot = tr + 2 * (int64_t)ts;
+    auto at = [&](int x) {
+      const int64_t c = ctot * x / 8;
+      return (int)(c <= tr ? c : tr + (c - tr + 1) / 2);
+    };
+    t_begin = at(xcd);
+    t_end = at(xcd + 1);
+  }
   const int per_h = (plan.units + 7) >> 3;
   const int h_begin = xcd * per_h, h_end = min(plan.units, (xcd + 1) * per_h);
   // Round r of the XCD's range is its tiles [r nq, (r+1) nq); this block
@@ -279,7 +292,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     const TileEntry te = p.entries[e_idx];
     const bool routed = te.group < p.G;
     const int gw = routed ? te.group : te.group - p.G;
-    int K = p.K;  // reduction depth of this tile
+    // the shared group of a down projection over 2 shared experts in turn
+    const bool cat = ACT == -1 && !BT && !routed && p.shared_cat == 2;
+    const int ldk = p.K;                // row stride of both operands
+    int K = cat ? 2 * p.K : p.K;        // reduction depth of this tile
     int64_t wstride = (int64_t)N * K;
     const uint16_t* W;
     const uint16_t* U;
@@ -352,15 +368,15 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
       for (int h = 0; h < 2; ++h) {
         const int row = h * 128 + rq;  // tile row
         const bool ok = row < te.rows;
-        int arow = p.a_from_c ? te.c_row0 + row : te.a_row0 + row;
+        int arow = (p.a_from_c && !cat) ? te.c_row0 + row : te.a_row0 + row;
         if (ok && routed && p.gather && !p.a_from_c) arow = p.gather[arow];
-        off[2 + h][j] = ok ? ((uint32_t)arow * (uint32_t)K + kc * 8) * 2u : kOOB;
+        off[2 + h][j] = ok ? ((uint32_t)arow * (uint32_t)(WGRAD ? K : ldk) + kc * 8) * 2u : kOOB;
         if constexpr (BT) {
           const int n = n_out0 + h * 128 + 8 * gc;
           off[h][j] = n < N ? ((uint32_t)kq * (uint32_t)N + n) * 2u : kOOB;
         } else {
           const int n = n_out0 + (GATED ? rq : row);
-          off[h][j] = n < N ? ((uint32_t)n * (uint32_t)K + kc * 8) * 2u : kOOB;
+          off[h][j] = n < N ? ((uint32_t)n * (uint32_t)(WGRAD ? K : ldk) + kc * 8) * 2u : kOOB;
         }
       }
     }
@@ -382,6 +398,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
         rs = u_rs;
         kset = k0 - p.kh;
       }
+      // the second shared expert of a concatenated group: its operand rows
+      // are T rows further on, its weights N rows
+      uint32_t kbase = (uint32_t)k0 * 2u;
+      if (cat && k0 >= ldk)
+        kbase = (uint32_t)(k0 - ldk) * 2u + (uint32_t)(qq >= 2 ? p.T : N) * (uint32_t)ldk * 2u;
       if (wid < 4) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -389,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
           if (BT && qq < 2)
             kadd = (k0 + l_kq[j] < k_end) ? (uint32_t)kset * (uint32_t)N * 2u : kOOB;
           else
-            kadd = (k0 + l_kc[j] * 8 < k_end) ? (uint32_t)k0 * 2u : kOOB;
+            kadd = (k0 + l_kc[j] * 8 < k_end) ? kbase : kOOB;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               rs, MOE_LDS(L + slot * kQuarter + ((wid + 4 * (j >> 1)) * 2 + (j & 1)) * 1024), 16,
               off[qq][j] + kadd, 0, 0, 0);

@@ -170,6 +170,12 @@ struct FfnParams {
   // of `out` ([T, N], the layer output) instead of row r; null = row r
   const int32_t* direct_token;
   const float* direct_gate;
+  // tiled path, act -1 (a layer call's down projection): nonzero = the
+  // launch's one shared group (S = 1) runs over this many (2) shared experts
+  // in turn, a reduction of shared_cat * K: expert s's operand row t is row
+  // t + s*T of a_shared (rows of K elements) and its weights start s*N*K
+  // elements into w_shared; the group's output row t is their sum
+  int shared_cat;
 };
 constexpr int kActBwd = 4;   // act codes 4, 5, 6: GELU, ReLU, SwiGLU backward
 constexpr int kActWgrad = 8;

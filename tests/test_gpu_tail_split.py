@@ -145,40 +145,51 @@ def test_gated_up_tail_split_matches_oracle(sizes, rows_bound, d, h):
     assert worst_row_error(got, want) <= 5e-2
 
 
-@pytest.mark.parametrize("E,k,T,d,h,act,bias", [
-    (48, 1, 2000, 512, 256, "swiglu", False),  # 9 x 2 tiles on a 112-block launch: 3 parts
-    (32, 2, 3000, 640, 320, "gelu", True),     # 26 x 3 tiles (2.5 column tiles) on 168: 2 parts
+@pytest.mark.parametrize("E,k,T,d,h,act,bias,S", [
+    (48, 1, 2000, 512, 256, "swiglu", False, 0),  # 9 x 2 tiles on a 112-block launch: 3 parts
+    (32, 2, 3000, 640, 320, "gelu", True, 0),     # 26 x 3 tiles (2.5 column tiles) on 168: 2 parts
+    # two shared experts run as one group of 2h-deep tiles (8 row tiles):
+    # that launch cuts its XCD ranges by depth and does not split
+    (48, 1, 2000, 512, 256, "swiglu", False, 2),
 ])
-def test_layer_call_bf16_rows_split(E, k, T, d, h, act, bias):
+def test_layer_call_bf16_rows_split(E, k, T, d, h, act, bias, S):
     """The single layer call of a bf16 layer keeps its expert rows in bf16; a
     down projection whose tail tiles split then writes every part's float32
     sums, and a fixup adds them in part order with the bias and rounds once.
     A strongly biased router concentrates the rows in a few experts, so the
     launch has far fewer tiles than its row bound allows and splits; every
-    token's output is checked against the oracle (routing replayed)."""
+    token's output is checked against the oracle (routing replayed).  With two
+    shared experts the call's down projection runs them as one group whose
+    reduction covers both (one output row per token), on XCD ranges cut by
+    depth and without a tail split."""
     from tests.gpu_util import oracle_forward, row_tol, upload, weights_of, worst_row_error, y_tol
     from sparse_mixture_experts_26_amd.layer import MoeLayer
     require_gpu()
-    cfg = LayerConfig(name=f"layer_split_E{E}_k{k}", cfg_id=77, T=T, d=d, E=E, k=k, h=h, act=act,
-                      capacity_factor=0.0, dtype="bf16", ffn_bias=bias, router_bias="normal",
-                      router_bias_std=3.0)
+    cfg = LayerConfig(name=f"layer_split_E{E}_k{k}_S{S}", cfg_id=77, T=T, d=d, E=E, k=k, h=h,
+                      act=act, capacity_factor=0.0, dtype="bf16", ffn_bias=bias,
+                      router_bias="normal", router_bias_std=3.0, n_shared=S)
     inp = make_inputs(cfg, seed=0)
     want = oracle_forward(inp)
     # the down launch's split plan (host-side mirror; the layer's workspace
     # caps the split tiles at half its row bound's tiles)
     offsets = want["offsets"]
     R = min(T * k, E * T)
-    max_entries = (R + BM - 1) // BM + E
+    t_tiles = (T + BM - 1) // BM
+    # the down launch holds the two shared experts as one group (S_down = 1);
+    # the split scratch is carved for the layer's S
+    S_down = 1 if S == 2 else S
+    max_entries = (R + BM - 1) // BM + E + S_down * t_tiles
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    entries = int(sum((s + BM - 1) // BM for s in np.diff(offsets)))
+    entries = int(sum((n + BM - 1) // BM for n in np.diff(offsets))) + S_down * t_tiles
     n_cols = (d + BR - 1) // BR
     P = min(cus, max_entries * n_cols)
     w, r = divmod(entries * n_cols, P)
-    cap = min(128, (max_entries * n_cols + 1) // 2)
+    cap = min(128, (((R + BM - 1) // BM + E + S * t_tiles) * n_cols + 1) // 2)
     parts = 3 if 3 * r <= P else 2
     banner(f"layer split E={E} k={k} T={T} d={d} h={h}: {entries} x {n_cols} tiles on {P} "
            f"blocks, r={r}, cap={cap}, parts={parts}")
-    assert r > 0 and 2 * r <= P and r <= cap, "case no longer exercises the split"
+    if S != 2:
+        assert r > 0 and 2 * r <= P and r <= cap, "case no longer exercises the split"
     dev = upload(inp)
     layer = MoeLayer(cfg, weights_of(dev))
     layer.out["y"].fill_(float("nan"))
