@@ -380,7 +380,10 @@ moe_status_t moe_combine_expert_choice(const moe_config_t* cfg, const float* y_r
  * sum, bias included) instead of float32, which halves the bytes the down
  * projection writes and the combine reads; the combine still accumulates in
  * float32 in the same fixed order.  With aux->y_rows the rows are float32, as
- * the stage entry points give them.
+ * the stage entry points give them.  Without it, two shared experts of such a
+ * layer on the tiled path (h a multiple of 64) are summed in the down
+ * projection's float32 accumulators (one shared row per token) rather than
+ * by the combine.
  * Intermediates live in `ws` unless `aux` names a buffer for them.
  */
 moe_status_t moe_layer_forward(const moe_config_t* cfg, const moe_weights_t* w,
