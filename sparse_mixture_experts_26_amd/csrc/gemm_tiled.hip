@@ -1024,7 +1024,9 @@ hipError_t launch_ffn_tiled(const FfnParams& p, hipStream_t stream) {
       default: hipLaunchKernelGGL(ffn_tiled_kernel<-1>, g, block, 0, stream, p, n_tiles_n); break;
     }
     // the split tiles of a tail split (the plan is made on the device)
-    const bool splits = p.act == -1 || p.act == 2;
+    // (a reduction too shallow for the plan ever to split launches no fixup)
+    const int nk = (p.K + BK - 1) / BK;
+    const bool splits = (p.act == -1 && nk >= 2) || (p.act == 2 && nk >= kGatedSplitStages);
     if (splits && p.split && p.split_cap > 0) {
       const int fix = (int)std::min<int64_t>(p.split_cap, grid / 2);
       const dim3 fg((unsigned)(fix * kFixParts)), fb(256);
