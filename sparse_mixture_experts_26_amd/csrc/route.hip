@@ -154,20 +154,24 @@ __device__ void router_tile_bf16(const RouteParams& p, float* part, int ldh, int
 // batch of T tokens reads it T/16 times from L2 (a 128-expert noisy router
 // over 4096 tokens: 100 MB; 64 experts over 16384 tokens: 268 MB).  Here a
 // block takes 64 tokens and one block of columns: EB experts' gate rows (and,
-// with noise, the same experts' noise rows), 16 NG weight rows in all.  Its 4
+// with noise, the same experts' noise rows), 16 NG weight rows in all.  Its KW
 // waves split the model width into contiguous ranges and each computes the
 // whole 64 x 16NG tile over its range (4 x NG tiles of
 // v_mfma_f32_16x16x32_bf16, float32 accumulate), so no operand is loaded
-// twice within a block; the 4 partial tiles are summed in LDS in wave order
+// twice within a block; the KW partial tiles are summed in LDS in wave order
 // (fixed, deterministic), then bias and noise are applied as in the fused
 // kernel and the logits (and the pre-softplus noise sums) written out.
 // Columns: gate expert e0 + c for c < EB; with noise, noise expert e0 + c - EB
 // for EB <= c < 2 EB (EB = 8 NG with noise, 16 NG without).
 constexpr int kLogitRows = 64;
-template <int NG, bool NOISE>
-__global__ __launch_bounds__(256) void router_logits_kernel(RouteParams p) {
+#ifndef MOE_LOGIT_WAVES
+#define MOE_LOGIT_WAVES 8
+#endif
+constexpr int kLogitWaves = MOE_LOGIT_WAVES;
+template <int NG, bool NOISE, int KW>
+__global__ __launch_bounds__(64 * KW) void router_logits_kernel(RouteParams p) {
   constexpr int NC = 16 * NG, EB = NOISE ? NC / 2 : NC, LD = NC + 1;
-  __shared__ float part[4][kLogitRows * LD];
+  __shared__ float part[KW][kLogitRows * LD];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * kLogitRows, e0 = blockIdx.y * EB;
@@ -191,7 +195,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(RouteParams p) {
     b_off[j] = e < min(p.E, e0 + EB) ? (uint32_t)e * (uint32_t)d * 2u : kOOB;
   }
   // this wave's contiguous model-width range, in steps of 32
-  const int steps = (d + 31) / 32, per = (steps + 3) / 4;
+  const int steps = (d + 31) / 32, per = (steps + KW - 1) / KW;
   const int kb = w * per * 32, ke = min(d, (w + 1) * per * 32);
   f32x4 acc[4][NG] = {};
   // batches of kBatch steps: all of a batch's loads are issued before its
@@ -236,9 +240,10 @@ __global__ __launch_bounds__(256) void router_logits_kernel(RouteParams p) {
       for (int i = 0; i < 4; ++i)
         part[w][(16 * m + 4 * (lane >> 4) + i) * LD + 16 * j + (lane & 15)] = acc[m][j][i];
   __syncthreads();
-  // thread -> column c = tid % EB, rows tid / EB + (256 / EB) i: the bias is
-  // loaded once and every eps load of the thread is issued before any is used
-  constexpr int RS = 256 / EB, NR = kLogitRows / RS;
+  // thread -> column c = tid % EB, rows tid / EB + (64 KW / EB) i: the bias
+  // is loaded once and every eps load of the thread is issued before any is
+  // used
+  constexpr int RS = 64 * KW / EB, NR = kLogitRows / RS;
   const int c = threadIdx.x % EB, r0 = threadIdx.x / EB, e = e0 + c;
   const bool col_ok = e < p.E;
   const float bias = (p.b_g && col_ok) ? p.b_g[e] : 0.f;
@@ -255,11 +260,15 @@ __global__ __launch_bounds__(256) void router_logits_kernel(RouteParams p) {
     const int r = r0 + RS * i, t = t0 + r;
     if (!col_ok || t >= p.T) continue;
     const int o = r * LD + c;
-    float v = ((part[0][o] + part[1][o]) + part[2][o]) + part[3][o];  // wave order
+    float v = part[0][o];
+#pragma unroll
+    for (int q = 1; q < KW; ++q) v += part[q][o];  // wave order
     v += bias;
     if constexpr (NOISE) {
       const int on = o + EB;
-      const float n = ((part[0][on] + part[1][on]) + part[2][on]) + part[3][on];
+      float n = part[0][on];
+#pragma unroll
+      for (int q = 1; q < KW; ++q) n += part[q][on];
       v += eps[i] * softplus_f32(n);
       if (p.noise_pre) p.noise_pre[(int64_t)t * p.E + e] = n;
     }
@@ -520,7 +529,8 @@ hipError_t launch_route(const RouteParams& p, hipStream_t stream) {
     const int ng = (noise ? 2 * p.E : p.E) > 32 ? 4 : 2;
     const int eb = noise ? 8 * ng : 16 * ng;
     const dim3 g((unsigned)((p.T + kLogitRows - 1) / kLogitRows), (unsigned)((p.E + eb - 1) / eb));
-#define MOE_LOGITS(NGV, NZ) hipLaunchKernelGGL((router_logits_kernel<NGV, NZ>), g, dim3(256), 0, stream, p)
+#define MOE_LOGITS(NGV, NZ) \
+  hipLaunchKernelGGL((router_logits_kernel<NGV, NZ, kLogitWaves>), g, dim3(64 * kLogitWaves), 0, stream, p)
     if (noise) {
       if (ng == 4) MOE_LOGITS(4, true); else MOE_LOGITS(2, true);
     } else {
