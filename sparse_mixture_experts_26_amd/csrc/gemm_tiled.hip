@@ -9,9 +9,13 @@
 // list of (group, first row, rows, first output row) entries of at most 256
 // rows, so no host synchronisation is needed.  The GEMM is persistent: one
 // block per CU walks the tiles; the hardware hands block P to XCD P % 8, and
-// XCD x owns an equal, contiguous range of the real tiles, in which groups of
-// 8 row tiles sweep the output columns together so the operand slabs of
-// concurrent tiles are shared through that XCD's L2.
+// XCD x owns an equal, contiguous range of the real tiles (cut by depth
+// instead when a down projection's two shared experts run as one 2h-deep
+// group), in which groups of 8 row tiles sweep the output columns together so
+// the operand slabs of concurrent tiles are shared through that XCD's L2.
+// Each round of an XCD's range goes to its blocks with the slot map turned by
+// the round, and in a tile of at most 128 rows the 4 waves of the empty half
+// only keep the barriers.
 //
 // Block tile: 256 rows x 256 weight rows, 8 waves (2 per SIMD, so one wave's
 // stalls are covered by the other's MFMAs) in a 2x4 grid, each wave 128x64 as
