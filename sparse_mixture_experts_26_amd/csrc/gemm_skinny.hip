@@ -570,8 +570,11 @@ hipError_t launch_ffn_skinny(const FfnParams& p, hipStream_t stream) {
   // Unit width and work split from a cost model in wave-steps of one
   // 16-column fragment: the busiest worker's units times their steps (the
   // K-split pays about 3 more steps per unit for its LDS reduction), times
-  // the width.  Whole-unit waves must beat the K-split by 15% to be chosen;
-  // between widths, ties go to the wider unit.
+  // the width.  The cheaper estimate wins, with no margin for either form
+  // (the Mixtral decode batch's gated up projection: 64-column whole units
+  // 282 us against 32-column split units 286 us, where a 15% margin for the
+  // split had kept the latter); ties go to the form and the width tried first
+  // (the wider unit, the K-split).
   const int64_t groups = p.G + p.S;
   const int64_t cap = (int64_t)device_cus() * kBlocksPerCU;
   const int64_t kch = (p.K + kStep - 1) / kStep;
@@ -588,7 +591,7 @@ hipError_t launch_ffn_skinny(const FfnParams& p, hipStream_t stream) {
     const int64_t blocks = std::min<int64_t>(units, cap);
     const double ksplit = (double)((units + blocks - 1) / blocks) * ((kch + 3) / 4 + 3) * cand;
     const int64_t wblocks = std::min<int64_t>((units + 3) / 4, cap);
-    const double whole = (double)((units + 4 * wblocks - 1) / (4 * wblocks)) * kch * cand * 1.15;
+    const double whole = (double)((units + 4 * wblocks - 1) / (4 * wblocks)) * kch * cand;
     // a gated 64-column unit split over the waves would need 128 KiB of LDS
     // (weight slots and partial products), leaving one block per CU
     if (ksplit < best && !(p.act == 2 && cand == 4)) { best = ksplit; nf = cand; wu = false; }
