@@ -37,7 +37,8 @@
  *     patterns); biases, eps, logits, gates, expert outputs and statistics are
  *     float32; every index and count is int32.
  *   - All device pointers must be 16-byte aligned; d and h must be multiples
- *     of 8; E <= 256; k <= 8 (MOE_ERR_UNSUPPORTED otherwise).
+ *     of 8; E <= 256 (<= 128 with router noise); k <= 8; n_shared <= 64
+ *     (MOE_ERR_UNSUPPORTED otherwise).
  *   - Entry points are stateless and may be called from several host threads;
  *     calls that share a workspace or outputs must be ordered by the caller.
  */

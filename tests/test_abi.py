@@ -106,7 +106,10 @@ def test_config_validation_statuses():
     assert _route(M.make_config(64, 60, 4, 2, 128)) == M.MOE_ERR_UNSUPPORTED       # d % 8
     assert _route(M.make_config(64, 64, 4, 2, 100)) == M.MOE_ERR_UNSUPPORTED       # h % 8
     assert _route(M.make_config(64, 64, 200, 2, 128, router_noise=True),
+                  w_noise=P[7], eps=P[8]) == M.MOE_ERR_UNSUPPORTED               # noisy E > 128
+    assert _route(M.make_config(64, 64, 129, 2, 128, router_noise=True),
                   w_noise=P[7], eps=P[8]) == M.MOE_ERR_UNSUPPORTED
+    assert _route(M.make_config(64, 64, 4, 2, 128, n_shared=65)) == M.MOE_ERR_UNSUPPORTED  # S > 64
     assert _route(ok, logits=None) == M.MOE_ERR_INVALID_ARGUMENT
     assert _route(ok, w_g=None) == M.MOE_ERR_INVALID_ARGUMENT
     assert _route(M.make_config(64, 64, 4, 2, 128, router_noise=True)) == M.MOE_ERR_INVALID_ARGUMENT
