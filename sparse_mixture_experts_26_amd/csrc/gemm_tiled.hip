@@ -14,8 +14,10 @@
 // group), in which groups of 8 row tiles sweep the output columns together so
 // the operand slabs of concurrent tiles are shared through that XCD's L2.
 // Each round of an XCD's range goes to its blocks with the slot map turned by
-// the round, and in a tile of at most 128 rows the 4 waves of the empty half
-// only keep the barriers.
+// the round, whole tiles of odd rounds walk their reduction from its end (so
+// a round begins on the slices of the shared operand rows that the previous
+// round ended on, still in the L2 and the MALL), and in a tile of at most 128
+// rows the 4 waves of the empty half only keep the barriers.
 //
 // Block tile: 256 rows x 256 weight rows, 8 waves (2 per SIMD, so one wave's
 // stalls are covered by the other's MFMAs) in a 2x4 grid, each wave 128x64 as
@@ -328,6 +330,10 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     const int ke = half < 0 ? nk : (half + 1) * nk / plan.parts;
     const int nks = ke - kb;
     const int k_end = ke == nk ? K : ke * BK;
+    // whole tiles of odd rounds walk their reduction from the end, so they
+    // start on the operand slices the previous round of the XCD ended on,
+    // which the L2 and the MALL still hold
+    const bool k_rev = half < 0 && (it & 1);
     const int n_out0 = n_idx * (GATED ? BR / 2 : BR);
     // Waves 4-7 compute tile rows 128-255 and issue no loads: in a tile of at
     // most 128 rows (the partly filled last row tile of a group) they only
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(FfnParams p, int
     // quarter qq (0..3) of stage kt into ring slot `slot`; stages past the
     // end read zeros
     auto issue = [&](int slot, int qq, int kt) __attribute__((always_inline)) {
-      const int k0 = (kb + kt) * BK;
+      const int k0 = (k_rev && kt < nks ? ke - 1 - kt : kb + kt) * BK;
       __amdgpu_buffer_rsrc_t rs = qq >= 2 ? a_rs : (GATED && qq == 1 ? u_rs : w_rs);
       // BT weight quarters: stage rows k0.. of the set holding them
       int kset = k0;
